@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's sharded AdamW step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over the rank's slice: the host layout call
+(shard_layout: flatten, floor-rule slice, segment table) and the fused GPU step
+(adamw_shard_step: rank-order fp32 reduction of the F bf16 contributions, AdamW on the fp32
+master / m / v, bf16 copy into the flat parameter layout).  Inputs are synthetic, seeded and
+resident in HBM before the timed region; the gradient buffers are drawn once and re-read by every
+step.  The timed region is K steps bracketed by device synchronisation; each kernel launch is also
+bracketed by HIP events on the stream it runs on, which gives the kernel's own average duration
+for the roofline figure.
+
+Prints one JSON line (the last line of stdout).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "params updated/sec per GPU (sharded AdamW step); achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+DEFAULT_WORKLOAD = "dense7b_n8_rank0"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc", "shard_step.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_param(fan_in):
+    """HBM bytes one real parameter must move in the fused step: F bf16 contributions read,
+    fp32 master / m / v each read and written, one bf16 parameter written."""
+    return 2 * fan_in + 3 * 4 * 2 + 2
+
+
+def source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """Per-launch HBM bytes from the committed rocprofv3 counter summary, if it was taken on the
+    kernel source as it is now (otherwise None)."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(workload, seconds=12.0, sample=1 << 21):
+    """The oracle as it is, single-threaded NumPy on the host, on the first `sample` elements of
+    the same workload's slice; repeated steps until about `seconds` of work."""
+    import numpy as np
+    import workloads as W
+    from oracle import layout as OL
+    from oracle import step as OS
+
+    w = W.WORKLOADS[workload]
+    lo, hi, osegs = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
+    n = min(sample, hi - lo)
+    flags = np.zeros(n, dtype=np.int64)
+    for s in osegs:
+        a, b = s["shard_begin"], min(n, s["shard_begin"] + s["length"])
+        if a < n:
+            flags[a:b] = s["flags"]
+    master, m, v = W.np_state(w, n, 0)
+    grads = W.np_grads(w, n, 1, 0)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        steps += 1
+        master, m, v, out = OS.shard_step(master, m, v, grads, flags, w.hp, steps)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    n_real = int(np.count_nonzero((flags & OL.PADDING) == 0))
+    return {"value": n_real * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} elements of the {workload} slice, fan-in {w.fan_in}, "
+                      f"{steps} oracle steps in {el:.1f} s (NumPy float32, one thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-reference", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: it times one rank's slice on a single MI355X and "
+              "has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fsdp_sharded_optimizer_layout_amd as F
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    F.lib()  # fail loudly if the library is missing
+    if args.blocks_per_cu:
+        F.set_blocks_per_cu(args.blocks_per_cu)
+
+    w = W.WORKLOADS[args.workload]
+    L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
+    n, lo, Fi = L.n, L.lo, w.fan_in
+    log(f"workload {w.name}: P={L.P} slice [{L.lo}, {L.hi}) n={n} n_real={L.n_real} "
+        f"F={Fi} segments={L.n_segments}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    master, m, v = W.torch_state(w, n, 0, dev)
+    grads = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(Fi)]
+    W.torch_grads_into(w, grads, 1, 0)
+    if w.nan_padding_grads:
+        for s in segs:
+            if s["flags"] & F.SEG_PADDING:
+                for g in grads:
+                    g[int(s["shard_begin"]): int(s["shard_begin"] + s["length"])] = 0x7FC0
+    phase = lo % 8
+    flat = torch.empty(n + phase, dtype=torch.int16, device=dev)
+    segs_dev = F.segments_to_device(segs, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step(t, ev=None):
+        F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
+        if ev is not None:
+            ev[0].record(stream)
+        F.adamw_shard_step(master, m, v, grads, step=t, segs=segs_dev, n_segments=L.n_segments,
+                           flat=flat, flat_index0=lo - phase, lo=lo, stream=stream, **w.hp)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for t in range(1, args.warmup + 1):
+        one_step(t)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + 1 + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in events]
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; kernel avg {avg_kernel_s*1e3:.3f} ms "
+        f"(min {min(kernel_ms):.3f}, max {max(kernel_ms):.3f})")
+
+    bpp = algorithmic_bytes_per_param(Fi)
+    alg_bytes = L.n_real * bpp
+    achieved = alg_bytes / avg_kernel_s / 1e9
+    traffic = counter_traffic(w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": traffic}
+
+    copy_ref = None
+    if not args.no_copy_reference:
+        del grads
+        torch.cuda.empty_cache()
+        nbytes = 4 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            F.stream_copy(src, dst, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        reps = 10
+        for _ in range(reps):
+            F.stream_copy(src, dst, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = a.elapsed_time(b) / reps
+        copy_ref = {"GBps": round(2 * nbytes / (copy_ms / 1e3) / 1e9, 1), "bytes_moved": 2 * nbytes,
+                    "kernel": "fsdpshard_stream_copy (16-byte loads and stores)"}
+        log(f"copy reference: {copy_ref['GBps']} GB/s")
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(w.name)
+        log(f"cpu oracle: {cpu['value']:.3e} params/s")
+
+    value = L.n_real / (ms_per_step / 1e3)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "flat_params": L.P,
+            "world_size": w.world_size,
+            "rank": w.rank,
+            "slice_elems": n,
+            "real_params": L.n_real,
+            "fan_in": Fi,
+            "segments": L.n_segments,
+            "storage": "bf16 grads and params, fp32 master/m/v",
+            "algorithmic_bytes_per_param": bpp,
+            "achieved_GBps_wall": round(alg_bytes / (ms_per_step / 1e3) / 1e9, 1),
+            "kernel_avg_ms": round(avg_kernel_s * 1e3, 4),
+            "blocks_per_cu": args.blocks_per_cu or "default",
+        },
+        "roofline": roofline,
+        "copy_reference": copy_ref,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+"""Python binding of libfsdpshard.so: one rank's share of a fully sharded training step on MI355X.
+
+Argument marshalling only.  Every computation runs in the library (host layout code and gfx950
+kernels); this module turns tensors into pointers and sizes, picks the current HIP stream, and
+raises on a non-zero status.  There is no fallback: if the library is missing, every call raises.
+
+Calls (same names as the C ABI in include/fsdpshard.h):
+  shard_layout      flat layout + floor-rule slice of one rank (host)
+  reduce_shard      fp32 rank-order sum of F bf16 contributions (GPU)
+  adamw_shard_step  fused reduce + AdamW + bf16 unflatten of one slice (GPU)
+  unflatten_bf16    bf16 copy of an fp32 master slice into the flat layout (GPU)
+bf16 tensors may be torch.bfloat16, torch.int16 or torch.uint16 (bit patterns); fp32 tensors
+are torch.float32.  All device tensors must be contiguous.
+"""
+
+import ctypes
+import os
+from collections import namedtuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsdpshard.so")
+MAX_FAN_IN = 64
+SEG_WEIGHT_DECAY = 1
+SEG_PADDING = 2
+
+c_i64, c_i32, c_u32, c_vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
+
+
+class _Segment(ctypes.Structure):
+    _fields_ = [("shard_begin", c_i64), ("length", c_i64), ("tensor_offset", c_i64),
+                ("tensor_id", c_i32), ("flags", c_u32)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("P", c_i64), ("lo", c_i64), ("hi", c_i64), ("n", c_i64), ("n_real", c_i64),
+                ("n_segments", c_i32), ("n_tensors", c_i32)]
+
+
+class _AdamW(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("grad_scale", ctypes.c_double), ("step", c_i64)]
+
+
+# numpy view of fsdpshard_segment (32 bytes)
+SEGMENT_DTYPE = np.dtype([("shard_begin", "<i8"), ("length", "<i8"), ("tensor_offset", "<i8"),
+                          ("tensor_id", "<i4"), ("flags", "<u4")])
+assert SEGMENT_DTYPE.itemsize == ctypes.sizeof(_Segment) == 32
+
+Layout = namedtuple("Layout", "P lo hi n n_real n_segments n_tensors")
+
+
+class FsdpShardError(RuntimeError):
+    def __init__(self, call, code):
+        self.code = code
+        super().__init__(f"{call} failed: {strerror(code)} (status {code})")
+
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m fsdp_sharded_optimizer_layout_amd.build`")
+    h = ctypes.CDLL(LIB_PATH)
+    h.shard_layout.argtypes = [ctypes.POINTER(c_i64), c_i32, c_i64, ctypes.POINTER(ctypes.c_uint8),
+                               c_i32, c_i32, ctypes.POINTER(_Layout), ctypes.POINTER(_Segment), c_i32]
+    h.reduce_shard.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float, c_vp, c_vp]
+    h.adamw_shard_step.argtypes = [c_vp, c_vp, c_vp, ctypes.POINTER(c_vp), c_i32, c_i64, c_vp,
+                                   c_i32, ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64, c_vp]
+    h.unflatten_bf16.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp, c_i64, c_i64, c_vp]
+    h.fsdpshard_strerror.argtypes = [ctypes.c_int]
+    h.fsdpshard_strerror.restype = ctypes.c_char_p
+    h.fsdpshard_abi_version.argtypes = []
+    h.fsdpshard_set_blocks_per_cu.argtypes = [ctypes.c_int]
+    h.fsdpshard_stream_copy.argtypes = [c_vp, c_vp, c_i64, c_vp]
+    for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
+                 "fsdpshard_abi_version", "fsdpshard_set_blocks_per_cu", "fsdpshard_stream_copy"):
+        getattr(h, name).restype = ctypes.c_int
+    _lib_handle = h
+    return h
+
+
+def strerror(code):
+    return lib().fsdpshard_strerror(int(code)).decode()
+
+
+def abi_version():
+    return lib().fsdpshard_abi_version()
+
+
+def set_blocks_per_cu(blocks_per_cu):
+    """Resident 256-thread work-groups per compute unit for the GPU calls (0 = default)."""
+    return lib().fsdpshard_set_blocks_per_cu(int(blocks_per_cu))
+
+
+def _check(call, code):
+    if code != 0:
+        raise FsdpShardError(call, code)
+
+
+# ------------------------------------------------------------------------------ host layout
+
+def shard_layout(numels, world_size, rank, pad_multiple=1, wd_mask=None):
+    """Flat layout and rank ``rank``'s slice.  Returns (Layout, segments) where segments is a
+    numpy array of SEGMENT_DTYPE describing [0, n) of the slice in flat order."""
+    sizes = np.ascontiguousarray(np.asarray(numels, dtype=np.int64).reshape(-1))
+    T = int(sizes.size)
+    mask = None
+    if wd_mask is not None:
+        mask = np.ascontiguousarray(np.asarray(wd_mask, dtype=np.uint8).reshape(-1))
+        if mask.size != T:
+            raise ValueError("wd_mask needs one entry per tensor")
+    h = lib()
+    out = _Layout()
+    sizes_p = sizes.ctypes.data_as(ctypes.POINTER(c_i64)) if T else None
+    mask_p = mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)) if mask is not None else None
+    _check("shard_layout", h.shard_layout(sizes_p, T, int(pad_multiple), mask_p, int(world_size),
+                                          int(rank), ctypes.byref(out), None, 0))
+    segs = np.zeros(out.n_segments, dtype=SEGMENT_DTYPE)
+    if out.n_segments:
+        _check("shard_layout", h.shard_layout(
+            sizes_p, T, int(pad_multiple), mask_p, int(world_size), int(rank), ctypes.byref(out),
+            segs.ctypes.data_as(ctypes.POINTER(_Segment)), out.n_segments))
+    return Layout(out.P, out.lo, out.hi, out.n, out.n_real, out.n_segments, out.n_tensors), segs
+
+
+def segments_to_device(segs, device="cuda"):
+    """Upload a SEGMENT_DTYPE array as a device byte tensor (pass it as ``segs`` below)."""
+    import torch
+    raw = np.ascontiguousarray(segs).view(np.uint8)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+# ------------------------------------------------------------------------------ GPU calls
+
+_BF16_DTYPES = None
+
+
+def _bf16_dtypes():
+    global _BF16_DTYPES
+    if _BF16_DTYPES is None:
+        import torch
+        _BF16_DTYPES = {torch.bfloat16, torch.int16, getattr(torch, "uint16", torch.int16)}
+    return _BF16_DTYPES
+
+
+def _ptr(t, what, dtypes=None, numel=None):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{what} has dtype {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{what} holds {t.numel()} elements, {numel} needed")
+    return t.data_ptr()
+
+
+def _stream(stream, like=None):
+    if stream is None:
+        import torch
+        dev = like.device if like is not None and hasattr(like, "device") else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _contrib_array(contribs, n):
+    if not 1 <= len(contribs) <= MAX_FAN_IN:
+        raise ValueError(f"fan-in must be 1..{MAX_FAN_IN}")
+    arr = (c_vp * len(contribs))()
+    for r, c in enumerate(contribs):
+        arr[r] = _ptr(c, f"contribution {r}", _bf16_dtypes(), n)
+    return arr
+
+
+def reduce_shard(contribs, out, scale=1.0, n=None, stream=None):
+    """out[i] = scale * sum over ranks r (in order) of contribs[r][i], in float32."""
+    import torch
+    n = out.numel() if n is None else int(n)
+    arr = _contrib_array(contribs, n)
+    _check("reduce_shard", lib().reduce_shard(
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n, float(scale),
+        _ptr(out, "out", {torch.float32}, n), _stream(stream, out)))
+
+
+def adamw_shard_step(master, m, v, contribs, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                     weight_decay=0.0, grad_scale=1.0, segs=None, n_segments=0, flat=None,
+                     flat_index0=0, lo=0, n=None, stream=None):
+    """Fused reduce + AdamW + bf16 unflatten of one slice (see adamw_shard_step in the header).
+
+    ``segs``: device byte tensor from segments_to_device (or None), with ``n_segments`` entries.
+    ``flat``: device bf16 window of the flat parameter vector starting at flat index
+    ``flat_index0``; the slice's elements land at flat indices [lo, lo + n).
+    """
+    import torch
+    n = master.numel() if n is None else int(n)
+    f32 = {torch.float32}
+    arr = _contrib_array(contribs, n)
+    hp = _AdamW(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                float(grad_scale), int(step))
+    if flat is not None and not isinstance(flat, int):
+        _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
+    _check("adamw_shard_step", lib().adamw_shard_step(
+        _ptr(master, "master", f32, n), _ptr(m, "m", f32, n), _ptr(v, "v", f32, n),
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n,
+        _ptr(segs, "segs"), int(n_segments), ctypes.byref(hp),
+        _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
+
+
+def unflatten_bf16(master, flat, flat_index0=0, lo=0, segs=None, n_segments=0, n=None,
+                   stream=None):
+    """flat[lo + i - flat_index0] = bf16(master[i]) for real elements, +0 for padding."""
+    import torch
+    n = master.numel() if n is None else int(n)
+    if not isinstance(flat, int):
+        _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
+    _check("unflatten_bf16", lib().unflatten_bf16(
+        _ptr(master, "master", {torch.float32}, n), n, _ptr(segs, "segs"), int(n_segments),
+        _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
+
+
+def stream_copy(src, dst, nbytes=None, stream=None):
+    """Measurement aid: plain 16-byte-vector device copy (bandwidth reference)."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check("fsdpshard_stream_copy", lib().fsdpshard_stream_copy(
+        _ptr(src, "src"), _ptr(dst, "dst"), nbytes, _stream(stream, src)))

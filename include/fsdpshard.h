@@ -1,0 +1,191 @@
+/*
+ * fsdpshard.h -- C ABI of libfsdpshard.so: one rank's share of a fully sharded (ZeRO-3 / FSDP
+ * FULL_SHARD) training step on one AMD Instinct MI355X (gfx950).
+ *
+ * The pages this follows (titles as published):
+ *   [FSDP]  "FSDP: Fully Sharded Data Parallel Training at Scale"
+ *   [DDL]   "Distributed Deep Learning & Model Sharding"
+ *
+ * Conventions for every call below
+ *   - Counts and indices are int64_t.  bf16 values travel as uint16_t bit patterns.
+ *   - "device" pointers are HIP device allocations on the current HIP device; "host" pointers are
+ *     ordinary process memory.  The caller owns every buffer; the library never allocates device
+ *     memory and keeps no state besides a per-device cached compute-unit count.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the device's null stream).  GPU calls are
+ *     asynchronous and stream-ordered: they validate their arguments on the host, enqueue one
+ *     kernel and return.  A fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Every call returns 0 (FSDPSHARD_OK) or a positive fsdpshard_status.  Nothing is enqueued
+ *     when a call returns an error; nothing is thrown and nothing aborts.
+ *   - n == 0 is a successful no-op.
+ */
+#ifndef FSDPSHARD_H
+#define FSDPSHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSDPSHARD_ABI_VERSION 1
+#define FSDPSHARD_MAX_FAN_IN 64
+
+typedef enum fsdpshard_status {
+    FSDPSHARD_OK = 0,
+    FSDPSHARD_ERR_INVALID_ARG = 1,  /* null pointer, negative size, rank >= world, overlap, ... */
+    FSDPSHARD_ERR_OVERFLOW = 2,     /* a flat offset, P, or k*P does not fit the int64 range */
+    FSDPSHARD_ERR_CAPACITY = 3,     /* segment array too small; the layout reports the count */
+    FSDPSHARD_ERR_ALIGNMENT = 4,    /* an fp32 or gradient pointer is not 16-byte aligned, ... */
+    FSDPSHARD_ERR_UNSUPPORTED = 5,  /* fan_in above FSDPSHARD_MAX_FAN_IN */
+    FSDPSHARD_ERR_HIP = 6           /* the HIP runtime refused a query or the kernel launch */
+} fsdpshard_status;
+
+/* Segment flags. */
+#define FSDPSHARD_SEG_WEIGHT_DECAY 1u  /* decoupled weight decay applies to these elements */
+#define FSDPSHARD_SEG_PADDING 2u       /* padding: never updated, served as +0 */
+
+/*
+ * One run of a rank's slice that belongs to a single tensor and is either all real elements or
+ * all padding.  32 bytes, 8-byte aligned; the same struct is used on the host and, uploaded by
+ * the caller, on the device.
+ */
+typedef struct fsdpshard_segment {
+    int64_t shard_begin;    /* first element of the run, counted from the slice start lo   */
+    int64_t length;         /* elements in the run, >= 1                                    */
+    int64_t tensor_offset;  /* position of shard_begin inside its tensor's padded extent    */
+    int32_t tensor_id;      /* index of the tensor in the flatten order                     */
+    uint32_t flags;         /* FSDPSHARD_SEG_* bits                                         */
+} fsdpshard_segment;
+
+typedef struct fsdpshard_layout {
+    int64_t P;           /* flat length, padding included                                  */
+    int64_t lo, hi;      /* the rank's slice [lo, hi) of the flat vector                   */
+    int64_t n;           /* hi - lo                                                        */
+    int64_t n_real;      /* elements of the slice that are not padding                     */
+    int32_t n_segments;  /* segments needed to describe the slice (always reported)        */
+    int32_t n_tensors;   /* tensors that intersect the slice                               */
+} fsdpshard_layout;
+
+/* AdamW hyperparameters of one step (float64 on the host; see adamw_shard_step). */
+typedef struct fsdpshard_adamw {
+    double lr;
+    double beta1, beta2;    /* each in [0, 1)                                     */
+    double eps;
+    double weight_decay;    /* decoupled, scaled by lr                            */
+    double grad_scale;      /* multiplies the reduced gradient; 1.0 = plain sum   */
+    int64_t step;           /* 1-based step counter t, incremented by the caller  */
+} fsdpshard_adamw;
+
+/*
+ * shard_layout -- flatten tensors and cut rank `rank`'s slice.            (host only, no GPU)
+ *
+ * [FSDP], passage on sharding a linear layer: a unit's parameters are viewed as one 1-D tensor
+ * of length P; with N ranks, rank k owns the contiguous elements floor(kP/N) .. floor((k+1)P/N)-1,
+ * and its gradient, m and v shards cover the same positions.  Several tensors are laid out one
+ * after another in the order given, each padded up to a multiple of `pad_multiple` elements
+ * (1 = no padding).
+ *
+ *   numels        host, n_tensors sizes (each >= 0); may be NULL when n_tensors == 0
+ *   pad_multiple  >= 1
+ *   wd_mask       host, n_tensors bytes (nonzero = weight decay on), or NULL = on everywhere
+ *   world_size    N >= 1;  rank: 0 <= rank < N
+ *   out           host, receives P, lo, hi, n, n_real, n_segments, n_tensors (required)
+ *   segs          host, room for seg_capacity segments, or NULL to only count
+ *   seg_capacity  >= 0
+ * Segments tile [0, n) in flat order.  k*P is formed in 128-bit arithmetic.  If segs is non-NULL
+ * and n_segments > seg_capacity, `out` is still filled, the first seg_capacity segments are
+ * written and FSDPSHARD_ERR_CAPACITY is returned (call again with a larger array).
+ * Errors: INVALID_ARG (nulls, negative sizes, bad rank or world size, pad_multiple < 1),
+ *         OVERFLOW (P or a padded size beyond INT64_MAX).
+ */
+int shard_layout(const int64_t* numels, int32_t n_tensors, int64_t pad_multiple,
+                 const uint8_t* wd_mask, int32_t world_size, int32_t rank,
+                 fsdpshard_layout* out, fsdpshard_segment* segs, int32_t seg_capacity);
+
+/*
+ * reduce_shard -- out[i] = scale * (((+0 + G_0[i]) + G_1[i]) + ... + G_{F-1}[i]),  0 <= i < n.
+ *
+ * [FSDP], communication pattern of one unit: the reduce-scatter after backward sums the ranks'
+ * gradients and leaves rank k only the part matching its slice; mixed-precision passage: the
+ * reduction runs in float32.  Here the F contributions of the slice are already on this GPU
+ * (no collective); each is widened exactly from bf16 and added in rank order 0..F-1 in float32.
+ *
+ *   contribs  host array of `fan_in` device pointers, each to n bf16 values, 16-byte aligned
+ *   fan_in    1 .. FSDPSHARD_MAX_FAN_IN
+ *   scale     multiplies the sum once (float32)
+ *   out       device, n floats, 16-byte aligned, must not overlap any contribution
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP.
+ */
+int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n, float scale,
+                 float* out, void* stream);
+
+/*
+ * adamw_shard_step -- the fused local step of one slice: reduce the F bf16 contributions,
+ * AdamW-update the fp32 master, m and v shards in place, and write the bf16 copy of the updated
+ * master into the flat parameter layout.
+ *
+ * [FSDP], communication pattern: the optimizer step runs on each rank with only its own
+ * parameter, gradient and optimizer-state slices; the next all-gather serves the bf16 params.
+ * [FSDP], memory breakdown, and [DDL], "The constraint is rarely FLOPs": bf16 params and grads,
+ * fp32 master weights, fp32 first moment (moving average of g) and second moment (moving average
+ * of g^2).  The pages do not print the update; it is bias-corrected Adam with decoupled weight
+ * decay scaled by lr.  Per real element, each step an IEEE float32 operation on its own:
+ *   g = scale * sum_r G_r             (as reduce_shard)
+ *   m = b1*m + c1*g;  v = b2*v + c2*(g*g)
+ *   den = sqrt(v / bc2) + eps;  th = th*dec (decay flag);  th = th - lr*((m / bc1) / den)
+ *   flat[lo + i] = bf16 round-to-nearest-even of th  (NaN stays a quiet NaN)
+ * with c1 = 1-beta1, c2 = 1-beta2, bc1 = 1-beta1^t, bc2 = 1-beta2^t, dec = 1-lr*weight_decay
+ * formed in float64 and rounded to float32 once.  Padding elements keep master, m and v bit for
+ * bit and are served as +0; their gradient values are ignored.
+ *
+ *   master, m, v  device, n floats each, 16-byte aligned, updated in place
+ *   contribs      host array of fan_in device pointers, each to n bf16 values, 16-byte aligned
+ *   segs          device copy of the slice's segments (as shard_layout emits them), 8-byte
+ *                 aligned, or NULL with n_segments == 0 (all elements real, decay everywhere).
+ *                 Segments must tile [0, n) in order; elements they do not cover take the flags
+ *                 of the nearest preceding segment (never an out-of-bounds read).
+ *   hp            host
+ *   flat_bf16     device window of the flat bf16 parameter vector whose element 0 is flat index
+ *                 flat_index0 (2-byte aligned; any phase); the call writes exactly the elements
+ *                 of flat indices [lo, lo + n) and nothing else.  NULL skips the bf16 output.
+ *   lo            flat index of the slice start, flat_index0 <= lo
+ * No written buffer may overlap another buffer of the call.
+ * Errors: INVALID_ARG (nulls, n < 0, step < 1, betas outside [0,1), non-finite values,
+ *         overlaps, n_segments < 0), ALIGNMENT, UNSUPPORTED, HIP.
+ */
+int adamw_shard_step(float* master, float* m, float* v,
+                     const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                     const fsdpshard_segment* segs, int32_t n_segments,
+                     const fsdpshard_adamw* hp,
+                     uint16_t* flat_bf16, int64_t flat_index0, int64_t lo, void* stream);
+
+/*
+ * unflatten_bf16 -- flat[lo + i] = bf16_rne(master[i]) for real elements, +0 for padding.
+ *
+ * [FSDP], communication pattern: after the all-gather every rank holds the full bf16 parameter
+ * tensor, each rank's slice sitting at [lo, hi) of the flat layout; this writes one slice's part.
+ * Arguments as in adamw_shard_step (master 16-byte aligned; flat_bf16 any 2-byte phase; segs
+ * may be NULL with n_segments == 0).
+ * Errors: INVALID_ARG, ALIGNMENT, HIP.
+ */
+int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs,
+                   int32_t n_segments, uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
+                   void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fsdpshard_strerror(int code);
+
+/* FSDPSHARD_ABI_VERSION of the loaded library. */
+int fsdpshard_abi_version(void);
+
+/*
+ * Occupancy knob of the GPU calls: resident work-groups of 256 threads launched per compute unit
+ * (1 .. 16); 0 restores the built-in default.  Process-wide; returns the previous value.
+ */
+int fsdpshard_set_blocks_per_cu(int blocks_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSDPSHARD_H */

@@ -1,0 +1,225 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* The library loads and exports every function that include/*.h declares.
+* shard_layout (host code in the library) matches the oracle's layout bit for bit, including
+  empty shards, padding, the 2,000-tensor workload and the capacity two-call pattern.
+* Argument validation returns its status before any HIP call (only calls that stop in
+  validation are made here; nothing reaches a kernel launch).
+"""
+
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import fsdp_sharded_optimizer_layout_amd as F
+import workloads as W
+from oracle import layout as OL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, OVERFLOW, CAPACITY, ALIGN, UNSUP, HIPERR = range(7)
+
+
+def _declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[\w ]+?\**\s*\b(\w+)\s*\(", text, flags=re.M)
+    return [n for n in names if n not in ("defined",)]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = F.lib()
+    declared = _declared_functions()
+    assert {"shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert F.abi_version() == 1
+    assert F.strerror(CAPACITY) == "segment array too small"
+
+
+def _oracle_segments(sizes, pad, wd, N, k):
+    lo, hi, segs = OL.segments(sizes, pad, wd, N, k)
+    return lo, hi, [(s["shard_begin"], s["length"], s["tensor_offset"], s["tensor_id"], s["flags"])
+                    for s in segs]
+
+
+def _lib_segments(sizes, pad, wd, N, k):
+    L, segs = F.shard_layout(sizes, N, k, pad, wd)
+    return L, [tuple(int(x) for x in s) for s in segs]
+
+
+def test_layout_matches_oracle_random():
+    rng = random.Random(3)
+    for trial in range(500):
+        T = rng.randint(0, 12)
+        sizes = [rng.choice([0, 1, 2, 3, 7, 8, 15, 16, 17, 100]) for _ in range(T)]
+        pad = rng.choice([1, 2, 8, 16])
+        wd = [rng.random() < 0.5 for _ in range(T)] if rng.random() < 0.5 else None
+        N = rng.randint(1, 20)
+        for k in range(N):
+            lo, hi, want = _oracle_segments(sizes, pad, wd, N, k)
+            L, got = _lib_segments(sizes, pad, wd, N, k)
+            assert (L.lo, L.hi, L.n) == (lo, hi, hi - lo)
+            assert got == want
+            assert L.n_real == sum(s[1] for s in want if not s[4] & OL.PADDING)
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_layout_of_workloads(name):
+    w = W.WORKLOADS[name]
+    lo, hi, want = _oracle_segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
+    L, got = _lib_segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
+    assert (L.P, L.lo, L.hi) == (w.total, lo, hi)
+    assert got == want
+
+
+def test_workload_realisations():
+    # flat lengths and slices of the five shard configurations
+    expect = {
+        "p1000003_n8_rank3": (1_000_003, 375_001, 500_001),
+        "llama_layer_n8_rank0": (218_112_000, 0, 27_264_000),
+        "dense7b_n8_rank0": (7_241_728_000, 0, 905_216_000),
+        "dense70b_n64_rank0": (68_976_640_000, 0, 1_077_760_000),
+        "many_small_n16_rank3": (529_512_096, 99_283_518, 132_378_024),
+    }
+    for name, (P, lo, hi) in expect.items():
+        w = W.WORKLOADS[name]
+        L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
+        assert (L.P, L.lo, L.hi) == (P, lo, hi)
+    L, segs = F.shard_layout(W.WORKLOADS["many_small_n16_rank3"].sizes, 16, 3, 16,
+                             W.WORKLOADS["many_small_n16_rank3"].wd_mask)
+    assert L.n - L.n_real == 1008 and L.n_real == 33_093_498
+
+
+def test_empty_shards_when_P_below_N():
+    bounds = [F.shard_layout([3], 8, k)[0] for k in range(8)]
+    assert [b.lo for b in bounds] + [3] == [0, 0, 0, 1, 1, 1, 2, 2, 3]
+    assert [b.n for b in bounds] == [0, 0, 1, 0, 0, 1, 0, 1]
+    L, segs = F.shard_layout([], 4, 2)
+    assert L.P == 0 and L.n == 0 and segs.size == 0
+
+
+def test_capacity_two_call_pattern():
+    lib = F.lib()
+    sizes = (ctypes.c_int64 * 5)(5, 6, 7, 8, 9)
+    out = F._Layout()
+    segs = (F._Segment * 2)()
+    rc = lib.shard_layout(sizes, 5, 4, None, 1, 0, ctypes.byref(out), segs, 2)
+    assert rc == CAPACITY and out.n_segments == 9     # tensor 3 (8 elements) has no padding
+    assert (segs[0].shard_begin, segs[0].length, segs[1].flags) == (0, 5, 3)
+    segs = (F._Segment * 9)()
+    assert lib.shard_layout(sizes, 5, 4, None, 1, 0, ctypes.byref(out), segs, 9) == OK
+
+
+def test_layout_argument_errors():
+    lib = F.lib()
+    sizes = (ctypes.c_int64 * 2)(5, 6)
+    out = F._Layout()
+    assert lib.shard_layout(sizes, 2, 1, None, 0, 0, ctypes.byref(out), None, 0) == INVALID
+    assert lib.shard_layout(sizes, 2, 1, None, 4, 4, ctypes.byref(out), None, 0) == INVALID
+    assert lib.shard_layout(sizes, 2, 1, None, 4, -1, ctypes.byref(out), None, 0) == INVALID
+    assert lib.shard_layout(sizes, 2, 0, None, 4, 0, ctypes.byref(out), None, 0) == INVALID
+    assert lib.shard_layout(None, 2, 1, None, 4, 0, ctypes.byref(out), None, 0) == INVALID
+    assert lib.shard_layout(sizes, 2, 1, None, 4, 0, None, None, 0) == INVALID
+    neg = (ctypes.c_int64 * 1)(-1)
+    assert lib.shard_layout(neg, 1, 1, None, 4, 0, ctypes.byref(out), None, 0) == INVALID
+    big = (ctypes.c_int64 * 2)(2 ** 62, 2 ** 62)
+    assert lib.shard_layout(big, 2, 1, None, 4, 0, ctypes.byref(out), None, 0) == OVERFLOW
+    odd = (ctypes.c_int64 * 1)(2 ** 63 - 5)
+    assert lib.shard_layout(odd, 1, 16, None, 4, 0, ctypes.byref(out), None, 0) == OVERFLOW
+
+
+def test_layout_128bit_product():
+    # k * P overflows int64 for P near 2^62 and k = 63; the library forms it in 128 bits.
+    P = 2 ** 62 + 12345
+    for k in (1, 31, 63):
+        L, _ = F.shard_layout([P], 64, k)
+        assert (L.lo, L.hi) == OL.shard_bounds(P, 64, k)
+
+
+class _Fake:
+    """Aligned fake device addresses: only used for calls that stop in argument validation."""
+    base = 1 << 40
+
+    @classmethod
+    def at(cls, i, off=0):
+        return cls.base + i * (1 << 32) + off
+
+
+def _step(lib, master, m, v, contribs, fan_in, n, segs, nseg, hp, flat, f0, lo):
+    arr = (ctypes.c_void_p * max(1, len(contribs)))(*contribs) if contribs is not None else None
+    return lib.adamw_shard_step(master, m, v, arr, fan_in, n, segs, nseg,
+                                ctypes.byref(hp) if hp is not None else None, flat, f0, lo, None)
+
+
+def test_step_validation_errors():
+    lib = F.lib()
+    hp = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    a, b, c = _Fake.at(0), _Fake.at(1), _Fake.at(2)
+    g = [_Fake.at(3), _Fake.at(4)]
+    out = _Fake.at(5)
+    # n == 0 with valid arguments: success without touching the GPU
+    assert _step(lib, a, b, c, g, 2, 0, None, 0, hp, out, 0, 0) == OK
+    assert _step(lib, None, b, c, g, 2, 0, None, 0, hp, out, 0, 0) == INVALID
+    assert _step(lib, a, b, c, g, 2, -1, None, 0, hp, out, 0, 0) == INVALID
+    assert _step(lib, a, b, c, g, 0, 0, None, 0, hp, out, 0, 0) == INVALID
+    assert _step(lib, a, b, c, g * 40, 65, 0, None, 0, hp, out, 0, 0) == UNSUP
+    assert _step(lib, a, b, c, [g[0], None], 2, 0, None, 0, hp, out, 0, 0) == INVALID
+    assert _step(lib, a, b, c, [g[0], g[1] + 2], 2, 0, None, 0, hp, out, 0, 0) == ALIGN
+    assert _step(lib, a + 4, b, c, g, 2, 0, None, 0, hp, out, 0, 0) == ALIGN
+    assert _step(lib, a, b, c, g, 2, 0, None, 0, hp, out + 1, 0, 0) == ALIGN
+    assert _step(lib, a, b, c, g, 2, 0, _Fake.at(6, 4), 1, hp, out, 0, 0) == ALIGN
+    assert _step(lib, a, b, c, g, 2, 0, None, 3, hp, out, 0, 0) == INVALID   # count without table
+    assert _step(lib, a, b, c, g, 2, 0, None, 0, hp, out, 5, 4) == INVALID   # window after lo
+    assert _step(lib, a, b, c, g, 2, 0, None, 0, None, out, 0, 0) == INVALID
+    for bad in (dict(step=0), dict(beta1=1.0), dict(beta2=-0.1), dict(lr=float("nan")),
+                dict(eps=float("inf"))):
+        h = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+        for k, val in bad.items():
+            setattr(h, k, val)
+        assert _step(lib, a, b, c, g, 2, 0, None, 0, h, out, 0, 0) == INVALID
+    # overlapping written buffers are refused (checked when n > 0, before any launch)
+    assert _step(lib, a, a + 16, c, g, 2, 100, None, 0, hp, out, 0, 0) == INVALID
+    assert _step(lib, a, b, c, [a, g[1]], 2, 100, None, 0, hp, out, 0, 0) == INVALID
+    assert _step(lib, a, b, c, g, 2, 100, None, 0, hp, g[0] + 64, 0, 0) == INVALID
+
+
+def test_reduce_and_unflatten_validation_errors():
+    lib = F.lib()
+    g = (ctypes.c_void_p * 2)(_Fake.at(3), _Fake.at(4))
+    out = _Fake.at(5)
+    assert lib.reduce_shard(g, 2, 0, 1.0, out, None) == OK
+    assert lib.reduce_shard(g, 2, 0, 1.0, None, None) == INVALID
+    assert lib.reduce_shard(g, 2, 0, 1.0, out + 8, None) == ALIGN
+    assert lib.reduce_shard(g, 0, 0, 1.0, out, None) == INVALID
+    assert lib.reduce_shard(g, 2, 100, 1.0, _Fake.at(3, 16), None) == INVALID   # overlap
+    m = _Fake.at(6)
+    assert lib.unflatten_bf16(m, 0, None, 0, out, 0, 0, None) == OK
+    assert lib.unflatten_bf16(m + 8, 0, None, 0, out, 0, 0, None) == ALIGN
+    assert lib.unflatten_bf16(m, 0, None, 0, out + 1, 0, 0, None) == ALIGN
+    assert lib.unflatten_bf16(m, 0, None, 0, None, 0, 0, None) == INVALID
+    assert lib.unflatten_bf16(m, 10, None, 0, m + 8, 0, 0, None) == INVALID     # overlap
+    assert lib.fsdpshard_stream_copy(m, out, 0, None) == OK
+    assert lib.fsdpshard_stream_copy(m, out, 8, None) == INVALID
+
+
+def test_blocks_per_cu_knob():
+    prev = F.set_blocks_per_cu(0)
+    assert prev >= 1
+    assert F.set_blocks_per_cu(prev) >= 1
+    assert F.lib().fsdpshard_set_blocks_per_cu(99) == -1
+
+
+def test_segment_dtype_matches_struct():
+    assert F.SEGMENT_DTYPE.itemsize == ctypes.sizeof(F._Segment) == 32
+    assert ctypes.sizeof(F._AdamW) == 56 and ctypes.sizeof(F._Layout) == 48
+    L, segs = F.shard_layout([5, 3], 2, 0, 4, [1, 0])
+    raw = np.ascontiguousarray(segs).view(np.uint8)
+    assert raw.size == 32 * L.n_segments

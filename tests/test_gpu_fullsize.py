@@ -1,0 +1,117 @@
+"""Full-size parity: each shard configuration at its real shape, in the launch configuration the
+benchmark times, compared with the oracle on sampled windows of the slice.
+
+The step is elementwise once the layout is fixed, so the oracle can recompute any subset of
+elements from the same inputs.  Windows: the first and last 64 Ki elements, +-4 Ki around every
+segment edge inside the slice, and 16 random 64 Ki windows.  Inputs are drawn on the device with
+seeded generators (no value comes from the library); the oracle receives copies of exactly the
+windowed inputs.  The bf16 destination uses the phase the slice has in a 16-byte aligned flat
+vector (lo mod 8), and a guarded prefix / suffix of the flat window must survive.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_layout_amd as F
+import workloads as W
+from oracle import layout as OL
+from oracle import step as OS
+from gpu_helpers import SENT16, assert_bf16, assert_f32, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+WIN = 65536
+EDGE = 4096
+
+
+def _windows(n, edges, rng):
+    spans = [(0, WIN), (n - WIN, n)] + [(e - EDGE, e + EDGE) for e in edges]
+    for s in rng.integers(0, max(1, n - WIN), 16):
+        spans.append((int(s), int(s) + WIN))
+    mask_idx = []
+    for a, b in spans:
+        a, b = max(0, a), min(n, b)
+        if a < b:
+            mask_idx.append(np.arange(a, b, dtype=np.int64))
+    return np.unique(np.concatenate(mask_idx))
+
+
+def _flags_at(osegs, idx):
+    starts = np.array([s["shard_begin"] for s in osegs], dtype=np.int64)
+    fl = np.array([s["flags"] for s in osegs], dtype=np.int64)
+    return fl[np.searchsorted(starts, idx, side="right") - 1]
+
+
+def run_fullsize(name, seed=0, steps=None):
+    w = W.WORKLOADS[name]
+    L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
+    lo_o, hi_o, osegs = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
+    assert (L.lo, L.hi) == (lo_o, hi_o)
+    n, lo = L.n, L.lo
+    say(f"fullsize {name}: n={n} lo={lo} F={w.fan_in} segs={L.n_segments}")
+    edges = [s["shard_begin"] for s in osegs[1:]]
+    rng = np.random.default_rng(seed)
+    idx = _windows(n, edges, rng)
+    idx_t = torch.from_numpy(idx).cuda()
+    flags = _flags_at(osegs, idx)
+    pad_mask_dev = None
+    if w.nan_padding_grads:
+        pad_mask_dev = torch.zeros(n, dtype=torch.bool, device="cuda")
+        for s in osegs:
+            if s["flags"] & OL.PADDING:
+                pad_mask_dev[s["shard_begin"]: s["shard_begin"] + s["length"]] = True
+
+    master, m, v = W.torch_state(w, n, seed, "cuda")
+    grads = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(w.fan_in)]
+    phase = lo % 8
+    GUARD = 64
+    flat_full = torch.full((GUARD + phase + n + GUARD,), int(SENT16),
+                           dtype=torch.int16, device="cuda")
+    flat = flat_full[GUARD:]
+    segs_dev = F.segments_to_device(segs)
+
+    om = master[idx_t].cpu().numpy()
+    omm = m[idx_t].cpu().numpy()
+    ov = v[idx_t].cpu().numpy()
+    total = (steps or w.steps) + w.warm_steps
+    for t in range(1, total + 1):
+        W.torch_grads_into(w, grads, t, seed)
+        if pad_mask_dev is not None:
+            for g in grads:
+                g.masked_fill_(pad_mask_dev, 0x7FC0)
+        F.adamw_shard_step(master, m, v, grads, step=t, segs=segs_dev, n_segments=L.n_segments,
+                           flat=flat, flat_index0=lo - phase, lo=lo, **w.hp)
+        contribs = [g[idx_t].cpu().numpy().view(np.uint16) for g in grads]
+        torch.cuda.synchronize()
+        om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, w.hp, t)
+        assert_f32(master[idx_t].cpu().numpy(), om, f"{name} master step {t}")
+        assert_f32(m[idx_t].cpu().numpy(), omm, f"{name} m step {t}")
+        assert_f32(v[idx_t].cpu().numpy(), ov, f"{name} v step {t}")
+        got = flat[phase:][idx_t].cpu().numpy().view(np.uint16)
+        assert_bf16(got, oout, f"{name} bf16 step {t}")
+        say(f"  step {t} ok")
+    host_flat = flat_full.cpu().numpy().view(np.uint16)
+    assert np.all(host_flat[:GUARD + phase] == SENT16), "flat prefix written"
+    assert np.all(host_flat[GUARD + phase + n:] == SENT16), "flat suffix written"
+    del master, m, v, grads, flat_full
+    torch.cuda.empty_cache()
+
+
+def test_p1000003_rank3():
+    run_fullsize("p1000003_n8_rank3")
+
+
+def test_llama_layer_with_warm_moments():
+    run_fullsize("llama_layer_n8_rank0", steps=3)
+
+
+def test_many_small_tensors():
+    run_fullsize("many_small_n16_rank3")
+
+
+def test_dense7b_slice():
+    run_fullsize("dense7b_n8_rank0", steps=2)
+
+
+def test_dense70b_slice():
+    run_fullsize("dense70b_n64_rank0", steps=2)

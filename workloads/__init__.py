@@ -126,6 +126,22 @@ def np_grads(w: Workload, n, step, seed):
     return out
 
 
+def np_bf16_normal(key, n, std):
+    """n bf16 bit patterns ~ N(0, std) (uint16), from a seed sequence ``key``."""
+    rng = np.random.default_rng(key)
+    return _truncate_to_bf16_bits(rng.standard_normal(n, dtype=np.float32) * np.float32(std))
+
+
+def np_f32_normal(key, n, std):
+    rng = np.random.default_rng(key)
+    return (rng.standard_normal(n, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def np_f32_uniform(key, n, lo, hi):
+    rng = np.random.default_rng(key)
+    return rng.uniform(lo, hi, n).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------- torch (device) draws
 
 def torch_state(w: Workload, n, seed, device):
