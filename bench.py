@@ -61,6 +61,53 @@ def counter_traffic(workload):
     return entry.get("bytes_per_launch")
 
 
+def summarize_counters(workload, fetch_dir, write_dir, kernel_prefix="void (anonymous namespace)::fused_step_kernel",
+                       calib_kernel="stream_copy_kernel", calib_bytes=4 << 30):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, in KiB per
+    dispatch) into per-launch HBM bytes of the step kernel, each counter scaled by what it reads
+    for the plain copy kernel, whose true traffic is calib_bytes read and calib_bytes written.
+    Writes the result into profiles/traffic.json under the workload's name."""
+    import csv
+    import statistics
+
+    def per_dispatch(d, counter):
+        path = os.path.join(d, "run_counter_collection.csv")
+        step, calib = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                kib = float(r["Counter_Value"])
+                if r["Kernel_Name"].startswith(kernel_prefix):
+                    step.append(kib)
+                elif calib_kernel in r["Kernel_Name"]:
+                    calib.append(kib)
+        return statistics.median(step), statistics.median(calib), len(step)
+
+    f_step, f_cal, nf = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_step, w_cal, nw = per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = calib_bytes / (f_cal * 1024.0)
+    w_scale = calib_bytes / (w_cal * 1024.0)
+    fetch = f_step * 1024.0 * f_scale
+    write = w_step * 1024.0 * w_scale
+    try:
+        with open(PROFILE_TRAFFIC) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {}
+    rec[workload] = {
+        "bytes_per_launch": round(fetch + write),
+        "fetch_bytes": round(fetch), "write_bytes": round(write),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "dispatches": [nf, nw],
+        "kernel_source_sha256_16": source_digest(),
+    }
+    with open(PROFILE_TRAFFIC, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(rec[workload]))
+
+
 def cpu_baseline(workload, seconds=12.0, sample=1 << 21):
     """The oracle as it is, single-threaded NumPy on the host, on the first `sample` elements of
     the same workload's slice; repeated steps until about `seconds` of work."""
@@ -99,10 +146,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--groups-per-wave", type=int, default=0,
+                    help="512-element groups per wavefront (1, 2, 4; 0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-reference", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.workload, *args.summarize_counters)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: it times one rank's slice on a single MI355X and "
@@ -117,8 +170,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     F.lib()  # fail loudly if the library is missing
-    if args.blocks_per_cu:
-        F.set_blocks_per_cu(args.blocks_per_cu)
+    if args.groups_per_wave:
+        F.set_groups_per_wave(args.groups_per_wave)
 
     w = W.WORKLOADS[args.workload]
     L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
@@ -178,6 +231,27 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic}
 
+    # Same streams, same grid, trivial arithmetic: the ceiling of this access pattern.
+    n8 = n - n % 8
+    mix_ref = None
+    if not args.no_copy_reference and n8 > 0:
+        out16 = flat[phase:phase + n8] if phase == 0 else torch.empty(n8, dtype=torch.int16,
+                                                                        device=dev)
+        for _ in range(2):
+            F.stream_mix(grads, master, m, v, out16, n=n8, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a.record(stream)
+        for _ in range(reps):
+            F.stream_mix(grads, master, m, v, out16, n=n8, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        mix_ms = a.elapsed_time(b) / reps
+        mix_ref = {"GBps": round(n8 * bpp / (mix_ms / 1e3) / 1e9, 1), "ms": round(mix_ms, 4),
+                   "kernel": "fsdpshard_stream_mix (the step's loads and stores, no arithmetic)"}
+        log(f"stream-mix reference: {mix_ref['GBps']} GB/s")
+        del out16
+
     copy_ref = None
     if not args.no_copy_reference:
         del grads
@@ -234,9 +308,10 @@ def main():
             "algorithmic_bytes_per_param": bpp,
             "achieved_GBps_wall": round(alg_bytes / (ms_per_step / 1e3) / 1e9, 1),
             "kernel_avg_ms": round(avg_kernel_s * 1e3, 4),
-            "blocks_per_cu": args.blocks_per_cu or "default",
+            "groups_per_wave": args.groups_per_wave or "default",
         },
         "roofline": roofline,
+        "mix_reference": mix_ref,
         "copy_reference": copy_ref,
         "cpu_baseline": cpu,
     }

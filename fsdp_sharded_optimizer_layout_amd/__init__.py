@@ -79,10 +79,13 @@ def lib():
     h.fsdpshard_strerror.argtypes = [ctypes.c_int]
     h.fsdpshard_strerror.restype = ctypes.c_char_p
     h.fsdpshard_abi_version.argtypes = []
-    h.fsdpshard_set_blocks_per_cu.argtypes = [ctypes.c_int]
+    h.fsdpshard_set_groups_per_wave.argtypes = [ctypes.c_int]
     h.fsdpshard_stream_copy.argtypes = [c_vp, c_vp, c_i64, c_vp]
+    h.fsdpshard_stream_mix.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                       c_vp]
     for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
-                 "fsdpshard_abi_version", "fsdpshard_set_blocks_per_cu", "fsdpshard_stream_copy"):
+                 "fsdpshard_abi_version", "fsdpshard_set_groups_per_wave", "fsdpshard_stream_copy",
+                 "fsdpshard_stream_mix"):
         getattr(h, name).restype = ctypes.c_int
     _lib_handle = h
     return h
@@ -96,9 +99,13 @@ def abi_version():
     return lib().fsdpshard_abi_version()
 
 
-def set_blocks_per_cu(blocks_per_cu):
-    """Resident 256-thread work-groups per compute unit for the GPU calls (0 = default)."""
-    return lib().fsdpshard_set_blocks_per_cu(int(blocks_per_cu))
+def set_groups_per_wave(groups):
+    """512-element groups per wavefront in adamw_shard_step (1, 2 or 4; 0 = built-in choice).
+    Returns the previous setting."""
+    prev = lib().fsdpshard_set_groups_per_wave(int(groups))
+    if prev < 0:
+        raise ValueError("groups per wave must be 0, 1, 2 or 4")
+    return prev
 
 
 def _check(call, code):
@@ -238,3 +245,12 @@ def stream_copy(src, dst, nbytes=None, stream=None):
     nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
     _check("fsdpshard_stream_copy", lib().fsdpshard_stream_copy(
         _ptr(src, "src"), _ptr(dst, "dst"), nbytes, _stream(stream, src)))
+
+
+def stream_mix(contribs, s0, s1, s2, out, n=None, stream=None):
+    """Measurement aid: the fused step's traffic with trivial arithmetic (n a multiple of 8)."""
+    n = s0.numel() if n is None else int(n)
+    arr = _contrib_array(contribs, n)
+    _check("fsdpshard_stream_mix", lib().fsdpshard_stream_mix(
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(s0, "s0"), _ptr(s1, "s1"),
+        _ptr(s2, "s2"), _ptr(out, "out"), n, _stream(stream, s0)))

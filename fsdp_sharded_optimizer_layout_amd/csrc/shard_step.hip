@@ -15,14 +15,16 @@
 //   * Every lane owns a vector of 8 consecutive elements: one 16-byte load per gradient stream,
 //     two 16-byte loads / stores per fp32 stream, one 16-byte bf16 store.  A wave covers 512
 //     elements (1 KiB per bf16 stream, 2 KiB per fp32 stream, all fully coalesced).
-//   * Each work-group owns one contiguous chunk of the slice; its 4 waves take interleaved 512-
-//     element groups of it.  The grid is a few work-groups per compute unit (256 CUs), sized so
-//     every wave has the same number of groups.
+//   * One tile per wave: each wave owns U consecutive 512-element groups (U = 1 by default; 2
+//     and 4 selectable) and issues every HBM load of its tile before the first arithmetic
+//     instruction; the grid has one work-group of 4 waves per 4U groups (hundreds of thousands
+//     for a 7B-model slice), so the hardware dispatcher feeds all 256 CUs in address order.  Gradient loads and all
+//     full-vector stores carry the non-temporal hint (single-use streams); the state loads do not.
 //   * Contributions are reduced in registers in rank order 0..F-1 from +0 (fixed order, so the
 //     result is deterministic and matches a sequential float32 sum bit for bit).
 //   * Segment flags (padding, weight decay) come from a per-wave cursor over the segment table:
-//     one binary search when a wave starts, a compare per group after that, and a per-element
-//     scan only in the rare groups that contain a tensor edge.
+//     one binary search when a wave starts (issued after the tile's loads, so it overlaps them),
+//     a compare per group after that, and a per-element scan only in groups that hold an edge.
 //   * The bf16 destination may start at any 2-byte phase inside a 16-byte vector (a slice starts
 //     wherever floor(kP/N) falls).  The state streams stay aligned; the bf16 result is re-phased
 //     across lanes (each lane borrows its right neighbour's first elements through a lane
@@ -46,8 +48,6 @@ constexpr int kVec = 8;            // elements per lane
 constexpr int kWave = 64;          // lanes per wavefront
 constexpr int kBlock = 256;        // threads per work-group
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kDefaultBlocksPerCu = 4;
-constexpr int kMaxDevices = 64;
 
 // ------------------------------------------------------------------------------------------------
 // Kernel parameter blocks (passed by value in the kernel-argument segment).
@@ -60,7 +60,6 @@ struct StepParams {
     const fsdpshard_segment* segs;
     uint16_t* out;           // destination of slice element 0 (flat index lo), or null
     int64_t n;               // elements in the slice
-    int64_t block_vecs;      // 8-element vectors per work-group (multiple of 64 * waves)
     int32_t n_segs;
     int32_t fan_in;
     int32_t out_shift;       // first slice element whose destination is 16-byte aligned (0..7)
@@ -71,7 +70,6 @@ struct ReduceParams {
     const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
     float* out;
     int64_t n;
-    int64_t block_vecs;
     int32_t fan_in;
     float scale;
 };
@@ -81,7 +79,6 @@ struct UnflattenParams {
     const fsdpshard_segment* segs;
     uint16_t* out;
     int64_t n;
-    int64_t block_vecs;
     int32_t n_segs;
     int32_t out_shift;
 };
@@ -122,6 +119,22 @@ __device__ __forceinline__ float4 ld_f4(const float* p) {
 }
 __device__ __forceinline__ void st_f4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
 
+// Non-temporal forms for single-use streams (global_load / global_store with the nt bit).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_u4_nt(const uint16_t* p) {
+    const u32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ void st_f4_nt(float* p, float a, float b, float c, float d) {
+    const f32x4_t v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void st_u4_nt(uint16_t* p, uint4 x) {
+    const u32x4_t v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Partial vector (slice tail): element-wise loads of the first `cnt` elements, zeros after.
 __device__ __forceinline__ uint4 ld_u4_partial(const uint16_t* p, int cnt) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -142,8 +155,8 @@ __device__ __forceinline__ void load8(const float* p, bool full, int cnt, float 
 
 __device__ __forceinline__ void store8(float* p, bool full, int cnt, const float (&x)[kVec]) {
     if (full) {
-        st_f4(p, make_float4(x[0], x[1], x[2], x[3]));
-        st_f4(p + 4, make_float4(x[4], x[5], x[6], x[7]));
+        st_f4_nt(p, x[0], x[1], x[2], x[3]);
+        st_f4_nt(p + 4, x[4], x[5], x[6], x[7]);
     } else {
 #pragma unroll
         for (int e = 0; e < kVec; ++e)
@@ -251,7 +264,7 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* out, int64_t e0, int sh
 
     uint32_t narrow = 0;  // bit e: write element e with a 2-byte store
     if (shift == 0) {
-        if (cnt == kVec) *reinterpret_cast<uint4*>(out + e0) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (cnt == kVec) st_u4_nt(out + e0, make_uint4(w[0], w[1], w[2], w[3]));
         else narrow = (1u << cnt) - 1u;
     } else {
         const uint32_t lo_mask = (1u << shift) - 1u;
@@ -267,7 +280,7 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* out, int64_t e0, int sh
                 case 6: r = rephase<6>(w, x); break;
                 default: r = rephase<7>(w, x); break;
             }
-            *reinterpret_cast<uint4*>(out + e0 + shift) = r;
+            st_u4_nt(out + e0 + shift, r);
         } else {
             narrow |= ~lo_mask & real_mask;
         }
@@ -323,9 +336,41 @@ __device__ __forceinline__ void sum_contribs(const StepParams& p, int64_t e0, bo
     }
 }
 
-// One 512-element group of the fused step.  TAIL = false is the interior case (all 64 vectors of
-// the group are complete slice elements) and compiles to straight-line loads; TAIL = true handles
-// the last, partial group of a work-group's chunk with per-lane bounds.
+// AdamW on 8 elements in registers; padding elements keep their state.
+__device__ __forceinline__ void adam8(const StepParams& p, const uint32_t (&fl)[kVec],
+                                      const float (&g)[kVec], float (&th)[kVec],
+                                      float (&mm)[kVec], float (&vv)[kVec]) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+        const float gs = g[e] * p.scale;
+        const float m1 = p.b1 * mm[e] + p.c1 * gs;
+        const float v1 = p.b2 * vv[e] + p.c2 * (gs * gs);
+        const float mh = m1 / p.bc1;
+        const float vh = v1 / p.bc2;
+        const float den = sqrtf(vh) + p.eps;
+        const float decayed = (fl[e] & FSDPSHARD_SEG_WEIGHT_DECAY) ? th[e] * p.dec : th[e];
+        const float t1 = decayed - p.lr * (mh / den);
+        const bool real = (fl[e] & FSDPSHARD_SEG_PADDING) == 0u;
+        th[e] = real ? t1 : th[e];
+        mm[e] = real ? m1 : mm[e];
+        vv[e] = real ? v1 : vv[e];
+    }
+}
+
+// bf16 bits of 8 updated weights, +0 for padding, packed two per dword.
+__device__ __forceinline__ void pack_out(const uint32_t (&fl)[kVec], const float (&th)[kVec],
+                                         uint32_t (&w)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t lo16 = (fl[2 * k] & FSDPSHARD_SEG_PADDING) ? 0u : to_bf16_bits(th[2 * k]);
+        const uint32_t hi16 =
+            (fl[2 * k + 1] & FSDPSHARD_SEG_PADDING) ? 0u : to_bf16_bits(th[2 * k + 1]);
+        w[k] = lo16 | (hi16 << 16);
+    }
+}
+
+// One 512-element group with per-lane bounds: the slice's last, partial group, and every group
+// of the run-time fan-in kernel.  TAIL = false drops the bounds for complete groups.
 template <int F, bool OUT, bool TAIL>
 __device__ __forceinline__ void step_group(const StepParams& p, const SegCursor& cur, int64_t vec,
                                            int64_t group_end_vec, int lane) {
@@ -353,39 +398,16 @@ __device__ __forceinline__ void step_group(const StepParams& p, const SegCursor&
     int64_t g1 = group_end_vec * kVec;
     if (g1 > n) g1 = n;
     element_flags(cur, g1, e0, fl);
-
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-        const float gs = g[e] * p.scale;
-        const float m1 = p.b1 * mm[e] + p.c1 * gs;
-        const float v1 = p.b2 * vv[e] + p.c2 * (gs * gs);
-        const float mh = m1 / p.bc1;
-        const float vh = v1 / p.bc2;
-        const float den = sqrtf(vh) + p.eps;
-        const float decayed = (fl[e] & FSDPSHARD_SEG_WEIGHT_DECAY) ? th[e] * p.dec : th[e];
-        const float t1 = decayed - p.lr * (mh / den);
-        const bool real = (fl[e] & FSDPSHARD_SEG_PADDING) == 0u;
-        th[e] = real ? t1 : th[e];
-        mm[e] = real ? m1 : mm[e];
-        vv[e] = real ? v1 : vv[e];
-    }
+    adam8(p, fl, g, th, mm, vv);
 
     if (valid) {
         store8(p.master + e0, full, cnt, th);
         store8(p.m + e0, full, cnt, mm);
         store8(p.v + e0, full, cnt, vv);
     }
-
     if constexpr (OUT) {
         uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool r0 = (fl[2 * k] & FSDPSHARD_SEG_PADDING) == 0u;
-            const bool r1 = (fl[2 * k + 1] & FSDPSHARD_SEG_PADDING) == 0u;
-            const uint32_t lo16 = r0 ? to_bf16_bits(th[2 * k]) : 0u;
-            const uint32_t hi16 = r1 ? to_bf16_bits(th[2 * k + 1]) : 0u;
-            w[k] = lo16 | (hi16 << 16);
-        }
+        pack_out(fl, th, w);
         const int s = p.out_shift;
         const bool next_ok = (lane < kWave - 1) && (vec + 1 < group_end_vec) &&
                              ((vec + 1) * kVec + s <= n);
@@ -394,161 +416,217 @@ __device__ __forceinline__ void step_group(const StepParams& p, const SegCursor&
     }
 }
 
-template <int F, bool OUT>
+// A wave's whole tile of U complete groups (compile-time fan-in F >= 1): all 14U loads of the
+// tile are issued first (gradients non-temporal), then the segment cursor is placed, then each
+// group is reduced, updated and stored.
+template <int F, bool OUT, int U>
+__device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, int lane) {
+    uint4 raw[U][F];
+    float th[U][kVec], mm[U][kVec], vv[U][kVec];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t e0 = (base0 + u * kWave + lane) * kVec;
+#pragma unroll
+        for (int r = 0; r < F; ++r) raw[u][r] = ld_u4_nt(p.contrib[r] + e0);
+        load8(p.master + e0, true, kVec, th[u]);
+        load8(p.m + e0, true, kVec, mm[u]);
+        load8(p.v + e0, true, kVec, vv[u]);
+    }
+    SegCursor cur;
+    cur.init(p.segs, p.n_segs, base0 * kVec);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t gb = base0 + u * kWave;
+        const int64_t e0 = (gb + lane) * kVec;
+        cur.seek(gb * kVec);
+        uint32_t fl[kVec];
+        element_flags(cur, (gb + kWave) * kVec, e0, fl);
+        float g[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < F; ++r) accumulate(g, raw[u][r]);
+        adam8(p, fl, g, th[u], mm[u], vv[u]);
+        store8(p.master + e0, true, kVec, th[u]);
+        store8(p.m + e0, true, kVec, mm[u]);
+        store8(p.v + e0, true, kVec, vv[u]);
+        if constexpr (OUT) {
+            uint32_t w[4];
+            pack_out(fl, th[u], w);
+            const int s = p.out_shift;
+            const bool next_ok = (lane < kWave - 1) && ((gb + lane + 1) * kVec + s <= p.n);
+            const bool prev_ok = (lane > 0) && (e0 + s <= p.n);
+            store_bf16_vec(p.out, e0, s, w, true, kVec, next_ok, prev_ok);
+        }
+    }
+}
+
+// Wave w of the grid owns vectors [w * 64U, (w + 1) * 64U) of the slice.
+__device__ __forceinline__ int64_t tile_base(int wave, int groups) {
+    return (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * (kWave * groups);
+}
+
+template <int F, bool OUT, int U>
 __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
-    const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * p.block_vecs;
-    int64_t blk1 = blk0 + p.block_vecs;
-    if (blk1 > nvec) blk1 = nvec;
-
+    const int64_t base0 = tile_base(wave, U);
+    if (base0 >= nvec) return;
+    if constexpr (F > 0) {
+        if (base0 + kWave * U <= p.n / kVec) {
+            step_tile<F, OUT, U>(p, base0, lane);
+            return;
+        }
+    }
     SegCursor cur;
-    cur.init(p.segs, p.n_segs, (blk0 + static_cast<int64_t>(wave) * kWave) * kVec);
-    for (int64_t base = blk0 + static_cast<int64_t>(wave) * kWave; base < blk1;
-         base += kWavesPerBlock * kWave) {
-        int64_t gend = base + kWave;
-        if (gend > blk1) gend = blk1;
-        cur.seek(base * kVec);
-        if (gend == base + kWave && gend * kVec <= p.n)
-            step_group<F, OUT, false>(p, cur, base + lane, gend, lane);
+    cur.init(p.segs, p.n_segs, base0 * kVec);
+    for (int u = 0; u < U; ++u) {
+        const int64_t gb = base0 + u * kWave;
+        if (gb >= nvec) break;
+        int64_t gend = gb + kWave;
+        if (gend > nvec) gend = nvec;
+        cur.seek(gb * kVec);
+        if (gend == gb + kWave && gend * kVec <= p.n)
+            step_group<F, OUT, false>(p, cur, gb + lane, gend, lane);
         else
-            step_group<F, OUT, true>(p, cur, base + lane, gend, lane);
+            step_group<F, OUT, true>(p, cur, gb + lane, gend, lane);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// Standalone reduce and unflatten.
+// Standalone reduce and unflatten: one 512-element group per wave.
 
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
-    const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * p.block_vecs;
-    int64_t blk1 = blk0 + p.block_vecs;
-    if (blk1 > nvec) blk1 = nvec;
-    for (int64_t base = blk0 + static_cast<int64_t>(wave) * kWave; base < blk1;
-         base += kWavesPerBlock * kWave) {
-        const int64_t vec = base + lane;
-        if (vec >= blk1) continue;
-        const int64_t e0 = vec * kVec;
-        const int cnt = static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec);
-        const bool full = cnt == kVec;
-        float g[kVec];
+    const int64_t vec = tile_base(wave, 1) + lane;
+    if (vec >= nvec) return;
+    const int64_t e0 = vec * kVec;
+    const int cnt = static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec);
+    const bool full = cnt == kVec;
+    float g[kVec];
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
-        for (int r0 = 0; r0 < p.fan_in; r0 += 4) {
-            uint4 raw[4];
+    for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+    for (int r0 = 0; r0 < p.fan_in; r0 += 4) {
+        uint4 raw[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (r0 + q < p.fan_in) {
-                    const uint16_t* src = p.contrib[r0 + q] + e0;
-                    raw[q] = full ? ld_u4(src) : ld_u4_partial(src, cnt);
-                }
+        for (int q = 0; q < 4; ++q) {
+            if (r0 + q < p.fan_in) {
+                const uint16_t* src = p.contrib[r0 + q] + e0;
+                raw[q] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (r0 + q < p.fan_in) accumulate(g, raw[q]);
         }
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) g[e] = g[e] * p.scale;
-        store8(p.out + e0, full, cnt, g);
+        for (int q = 0; q < 4; ++q)
+            if (r0 + q < p.fan_in) accumulate(g, raw[q]);
     }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) g[e] = g[e] * p.scale;
+    store8(p.out + e0, full, cnt, g);
 }
 
 __global__ __launch_bounds__(kBlock) void unflatten_kernel(UnflattenParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
-    const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * p.block_vecs;
-    int64_t blk1 = blk0 + p.block_vecs;
-    if (blk1 > nvec) blk1 = nvec;
-
-    SegCursor cur;
-    cur.init(p.segs, p.n_segs, (blk0 + static_cast<int64_t>(wave) * kWave) * kVec);
-    for (int64_t base = blk0 + static_cast<int64_t>(wave) * kWave; base < blk1;
-         base += kWavesPerBlock * kWave) {
-        int64_t gend = base + kWave;
-        if (gend > blk1) gend = blk1;
-        cur.seek(base * kVec);
-        const int64_t vec = base + lane;
-        const int64_t e0 = vec * kVec;
-        const bool valid = vec < gend;
-        const int cnt = valid ? static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec) : 0;
-        float th[kVec];
-        if (valid) load8(p.master + e0, cnt == kVec, cnt, th);
-        else {
+    const int64_t gb = tile_base(wave, 1);
+    if (gb >= nvec) return;
+    int64_t gend = gb + kWave;
+    if (gend > nvec) gend = nvec;
+    const int64_t vec = gb + lane;
+    const int64_t e0 = vec * kVec;
+    const bool valid = vec < gend;
+    const int cnt = valid ? static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec) : 0;
+    float th[kVec];
+    if (valid) {
+        load8(p.master + e0, cnt == kVec, cnt, th);
+    } else {
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) th[e] = 0.0f;
-        }
-        uint32_t fl[kVec];
-        int64_t g1 = gend * kVec;
-        if (g1 > p.n) g1 = p.n;
-        element_flags(cur, g1, e0, fl);
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo16 = (fl[2 * k] & FSDPSHARD_SEG_PADDING) ? 0u : to_bf16_bits(th[2 * k]);
-            const uint32_t hi16 =
-                (fl[2 * k + 1] & FSDPSHARD_SEG_PADDING) ? 0u : to_bf16_bits(th[2 * k + 1]);
-            w[k] = lo16 | (hi16 << 16);
-        }
-        const int s = p.out_shift;
-        const bool next_ok = (lane < kWave - 1) && (vec + 1 < gend) && ((vec + 1) * kVec + s <= p.n);
-        const bool prev_ok = (lane > 0) && (e0 + s <= p.n);
-        store_bf16_vec(p.out, e0, s, w, valid, cnt, next_ok, prev_ok);
+        for (int e = 0; e < kVec; ++e) th[e] = 0.0f;
     }
+    SegCursor cur;
+    cur.init(p.segs, p.n_segs, gb * kVec);
+    uint32_t fl[kVec];
+    int64_t g1 = gend * kVec;
+    if (g1 > p.n) g1 = p.n;
+    element_flags(cur, g1, e0, fl);
+    uint32_t w[4];
+    pack_out(fl, th, w);
+    const int s = p.out_shift;
+    const bool next_ok = (lane < kWave - 1) && (vec + 1 < gend) && ((vec + 1) * kVec + s <= p.n);
+    const bool prev_ok = (lane > 0) && (e0 + s <= p.n);
+    store_bf16_vec(p.out, e0, s, w, valid, cnt, next_ok, prev_ok);
 }
 
 __global__ __launch_bounds__(kBlock) void stream_copy_kernel(const uint4* __restrict__ src,
                                                              uint4* __restrict__ dst,
                                                              int64_t nvec) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec; i += stride)
-        dst[i] = src[i];
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= nvec) return;
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + i));
+}
+
+// Measurement aid: the fused step's exact streams (F non-temporal bf16 loads, three fp32
+// read-modify-write streams, one bf16 store per 8-element vector, one 512-element group per wave)
+// with trivial integer arithmetic in place of the reduction and the optimizer.
+struct MixParams {
+    const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
+    float* s[3];
+    uint16_t* out;
+    int64_t nvec;
+    int32_t fan_in;
+};
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int64_t vec = tile_base(wave, 1) + lane;
+    if (vec >= p.nvec) return;
+    const int64_t e0 = vec * kVec;
+    const int fan_in = F > 0 ? F : p.fan_in;
+    uint4 raw[F > 0 ? F : 1];
+    float st[3][kVec];
+    uint32_t x = 0;
+    if constexpr (F > 0) {
+#pragma unroll
+        for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) load8(p.s[k] + e0, true, kVec, st[k]);
+    if constexpr (F > 0) {
+#pragma unroll
+        for (int r = 0; r < F; ++r) x ^= raw[r].x ^ raw[r].y ^ raw[r].z ^ raw[r].w;
+    } else {
+        for (int r = 0; r < fan_in; ++r) {
+            const uint4 q = ld_u4_nt(p.contrib[r] + e0);
+            x ^= q.x ^ q.y ^ q.z ^ q.w;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        st[k][0] = __uint_as_float(__float_as_uint(st[k][0]) ^ x);
+        store8(p.s[k] + e0, true, kVec, st[k]);
+    }
+    st_u4_nt(p.out + e0, make_uint4(__float_as_uint(st[0][1]), __float_as_uint(st[1][1]),
+                                    __float_as_uint(st[2][1]), x));
 }
 
 // ------------------------------------------------------------------------------------------------
 // Host-side launch helpers.
 
-std::atomic<int> g_cu_count[kMaxDevices];
-std::atomic<int> g_blocks_per_cu{kDefaultBlocksPerCu};
+std::atomic<int> g_groups_per_wave{0};   // 0: built-in choice per fan-in
 
-int cu_count(int* out) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return FSDPSHARD_ERR_HIP;
-    if (dev >= 0 && dev < kMaxDevices) {
-        const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
-        if (cached > 0) {
-            *out = cached;
-            return FSDPSHARD_OK;
-        }
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        return FSDPSHARD_ERR_HIP;
-    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
-    *out = cus;
-    return FSDPSHARD_OK;
-}
-
-// Grid for n elements: a few resident work-groups per CU, each owning an equal contiguous
-// chunk whose size is a multiple of one group per wave.
-int plan_grid(int64_t n, int64_t* block_vecs, unsigned* blocks) {
-    int cus = 0;
-    const int rc = cu_count(&cus);
-    if (rc != FSDPSHARD_OK) return rc;
+// One work-group of 4 waves per 4 * groups * 64 vectors of 8 elements.
+int tile_grid(int64_t n, int groups, unsigned* blocks) {
     const int64_t nvec = (n + kVec - 1) / kVec;
-    const int64_t unit = static_cast<int64_t>(kWave) * kWavesPerBlock;  // vectors per block round
-    const int64_t max_blocks = static_cast<int64_t>(cus) * g_blocks_per_cu.load();
-    int64_t want = (nvec + unit - 1) / unit;
-    if (want > max_blocks) want = max_blocks;
-    if (want < 1) want = 1;
-    int64_t per = (nvec + want - 1) / want;
-    per = (per + unit - 1) / unit * unit;
-    *block_vecs = per;
-    *blocks = static_cast<unsigned>((nvec + per - 1) / per);
+    const int64_t per_block = static_cast<int64_t>(kWavesPerBlock) * kWave * groups;
+    const int64_t b = (nvec + per_block - 1) / per_block;
+    if (b > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
+    *blocks = static_cast<unsigned>(b);
     return FSDPSHARD_OK;
 }
 
@@ -566,19 +644,36 @@ int launch(const void* kernel, unsigned blocks, void* params, void* stream) {
     return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
 }
 
-template <int F>
-const void* step_kernel(bool out) {
-    return out ? reinterpret_cast<const void*>(&fused_step_kernel<F, true>)
-               : reinterpret_cast<const void*>(&fused_step_kernel<F, false>);
+template <int F, int U>
+const void* step_kernel_u(bool out) {
+    return out ? reinterpret_cast<const void*>(&fused_step_kernel<F, true, U>)
+               : reinterpret_cast<const void*>(&fused_step_kernel<F, false, U>);
 }
 
-const void* pick_step_kernel(int fan_in, bool out) {
+template <int F>
+const void* step_kernel(bool out, int groups) {
+    switch (groups) {
+        case 1: return step_kernel_u<F, 1>(out);
+        case 4: return step_kernel_u<F, 4>(out);
+        default: return step_kernel_u<F, 2>(out);
+    }
+}
+
+// Groups per wave: the process-wide setting if one was made, else the built-in choice.
+int groups_for(int fan_in) {
+    const int g = g_groups_per_wave.load(std::memory_order_relaxed);
+    if (g > 0) return g;
+    (void)fan_in;
+    return 1;  // measured fastest on MI355X for every fan-in (one 512-element group per wave)
+}
+
+const void* pick_step_kernel(int fan_in, bool out, int groups) {
     switch (fan_in) {
-        case 1: return step_kernel<1>(out);
-        case 2: return step_kernel<2>(out);
-        case 4: return step_kernel<4>(out);
-        case 8: return step_kernel<8>(out);
-        default: return step_kernel<0>(out);
+        case 1: return step_kernel<1>(out, groups);
+        case 2: return step_kernel<2>(out, groups);
+        case 4: return step_kernel<4>(out, groups);
+        case 8: return step_kernel<8>(out, groups);
+        default: return step_kernel<0>(out, groups);
     }
 }
 
@@ -667,10 +762,11 @@ extern "C" int adamw_shard_step(float* master, float* m, float* v,
     p.dec = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
     p.scale = static_cast<float>(hp->grad_scale);
 
+    const int groups = groups_for(fan_in);
     unsigned blocks = 0;
-    rc = plan_grid(n, &p.block_vecs, &blocks);
+    rc = tile_grid(n, groups, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(pick_step_kernel(fan_in, out != nullptr), blocks, &p, stream);
+    return launch(pick_step_kernel(fan_in, out != nullptr, groups), blocks, &p, stream);
 }
 
 extern "C" int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
@@ -690,7 +786,7 @@ extern "C" int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int
     p.fan_in = fan_in;
     p.scale = scale;
     unsigned blocks = 0;
-    rc = plan_grid(n, &p.block_vecs, &blocks);
+    rc = tile_grid(n, 1, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
     return launch(reinterpret_cast<const void*>(&reduce_kernel), blocks, &p, stream);
 }
@@ -717,7 +813,7 @@ extern "C" int unflatten_bf16(const float* master, int64_t n, const fsdpshard_se
     p.n_segs = segs == nullptr ? 0 : n_segments;
     p.out_shift = out_shift_of(out);
     unsigned blocks = 0;
-    int rc = plan_grid(n, &p.block_vecs, &blocks);
+    int rc = tile_grid(n, 1, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
     return launch(reinterpret_cast<const void*>(&unflatten_kernel), blocks, &p, stream);
 }
@@ -728,13 +824,9 @@ extern "C" int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, 
     if (!aligned16(src) || !aligned16(dst)) return FSDPSHARD_ERR_ALIGNMENT;
     if (bytes > 0 && overlaps(src, bytes, dst, bytes)) return FSDPSHARD_ERR_INVALID_ARG;
     if (bytes == 0) return FSDPSHARD_OK;
-    int cus = 0;
-    const int rc = cu_count(&cus);
-    if (rc != FSDPSHARD_OK) return rc;
     const int64_t nvec = bytes / 16;
-    int64_t blocks = static_cast<int64_t>(cus) * 8;
-    const int64_t need = (nvec + kBlock - 1) / kBlock;
-    if (blocks > need) blocks = need;
+    const int64_t blocks = (nvec + kBlock - 1) / kBlock;
+    if (blocks > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
     void* args[3];
     const uint4* s = static_cast<const uint4*>(src);
     uint4* d = static_cast<uint4*>(dst);
@@ -748,8 +840,42 @@ extern "C" int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, 
     return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
 }
 
-extern "C" int fsdpshard_set_blocks_per_cu(int blocks_per_cu) {
-    if (blocks_per_cu < 0 || blocks_per_cu > 16) return -1;
-    const int v = blocks_per_cu == 0 ? kDefaultBlocksPerCu : blocks_per_cu;
-    return g_blocks_per_cu.exchange(v);
+extern "C" int fsdpshard_set_groups_per_wave(int groups) {
+    if (groups != 0 && groups != 1 && groups != 2 && groups != 4) return -1;
+    return g_groups_per_wave.exchange(groups);
+}
+
+extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0,
+                                    float* s1, float* s2, uint16_t* out, int64_t n, void* stream) {
+    if (s0 == nullptr || s1 == nullptr || s2 == nullptr || out == nullptr || n < 0 || n % kVec)
+        return FSDPSHARD_ERR_INVALID_ARG;
+    int rc = check_contribs(contribs, fan_in, n);
+    if (rc != FSDPSHARD_OK) return rc;
+    if (!aligned16(s0) || !aligned16(s1) || !aligned16(s2) || !aligned16(out))
+        return FSDPSHARD_ERR_ALIGNMENT;
+    if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
+    if (n == 0) return FSDPSHARD_OK;
+    const void* wr[4] = {s0, s1, s2, out};
+    const int64_t wb[4] = {n * 4, n * 4, n * 4, n * 2};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(wr[i], wb[i], wr[j], wb[j])) return FSDPSHARD_ERR_INVALID_ARG;
+        for (int r = 0; r < fan_in; ++r)
+            if (overlaps(wr[i], wb[i], contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+    }
+    MixParams p;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
+    p.s[0] = s0;
+    p.s[1] = s1;
+    p.s[2] = s2;
+    p.out = out;
+    p.nvec = n / kVec;
+    p.fan_in = fan_in;
+    unsigned blocks = 0;
+    rc = tile_grid(n, 1, &blocks);
+    if (rc != FSDPSHARD_OK) return rc;
+    const void* k = fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1>)
+                    : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8>)
+                                  : reinterpret_cast<const void*>(&stream_mix_kernel<0>);
+    return launch(k, blocks, &p, stream);
 }

@@ -10,7 +10,7 @@
  *   - Counts and indices are int64_t.  bf16 values travel as uint16_t bit patterns.
  *   - "device" pointers are HIP device allocations on the current HIP device; "host" pointers are
  *     ordinary process memory.  The caller owns every buffer; the library never allocates device
- *     memory and keeps no state besides a per-device cached compute-unit count.
+ *     memory and keeps no state besides the process-wide tuning setting below.
  *   - `stream` is a hipStream_t passed as void* (NULL = the device's null stream).  GPU calls are
  *     asynchronous and stream-ordered: they validate their arguments on the host, enqueue one
  *     kernel and return.  A fault inside a kernel surfaces at the caller's next synchronisation.
@@ -179,10 +179,11 @@ const char* fsdpshard_strerror(int code);
 int fsdpshard_abi_version(void);
 
 /*
- * Occupancy knob of the GPU calls: resident work-groups of 256 threads launched per compute unit
- * (1 .. 16); 0 restores the built-in default.  Process-wide; returns the previous value.
+ * Tuning knob of adamw_shard_step: how many consecutive 512-element groups each wavefront owns
+ * (1, 2 or 4; 0 restores the built-in choice).  Process-wide; results do not depend on it.
+ * Returns the previous setting, or -1 for an unsupported value.
  */
-int fsdpshard_set_blocks_per_cu(int blocks_per_cu);
+int fsdpshard_set_groups_per_wave(int groups);
 
 #ifdef __cplusplus
 }

@@ -210,11 +210,12 @@ def test_reduce_and_unflatten_validation_errors():
     assert lib.fsdpshard_stream_copy(m, out, 8, None) == INVALID
 
 
-def test_blocks_per_cu_knob():
-    prev = F.set_blocks_per_cu(0)
-    assert prev >= 1
-    assert F.set_blocks_per_cu(prev) >= 1
-    assert F.lib().fsdpshard_set_blocks_per_cu(99) == -1
+def test_groups_per_wave_knob():
+    prev = F.set_groups_per_wave(4)
+    assert F.set_groups_per_wave(prev) == 4
+    assert F.lib().fsdpshard_set_groups_per_wave(3) == -1
+    with pytest.raises(ValueError):
+        F.set_groups_per_wave(8)
 
 
 def test_segment_dtype_matches_struct():

@@ -35,7 +35,7 @@ def _layout_case(sizes, pad, wd, N, k):
 
 
 def run_case(n=None, F_in=8, steps=2, d=0, layout=None, seed=0, warm_state=True, nan_pad=False,
-             hp=HP, blocks_per_cu=0, grad_std=1e-2, check_bitexact=False, lo=1000):
+             hp=HP, groups=0, grad_std=1e-2, check_bitexact=False, lo=1000):
     """Run `steps` fused steps on one slice through the library and through the oracle."""
     if layout is not None:
         L, segs, flags = _layout_case(*layout)
@@ -45,7 +45,7 @@ def run_case(n=None, F_in=8, steps=2, d=0, layout=None, seed=0, warm_state=True,
     else:
         flags = np.full(n, OL.WEIGHT_DECAY, dtype=np.int64)
         segs_dev, nseg = None, 0
-    say(f"case n={n} F={F_in} steps={steps} d={d} segs={nseg} seed={seed} bpc={blocks_per_cu}")
+    say(f"case n={n} F={F_in} steps={steps} d={d} segs={nseg} seed={seed} groups={groups}")
     master0 = W.np_f32_normal([seed, 1], n, 0.02)
     if warm_state:
         m0 = W.np_f32_normal([seed, 2], n, 1e-3)
@@ -57,7 +57,7 @@ def run_case(n=None, F_in=8, steps=2, d=0, layout=None, seed=0, warm_state=True,
     gm, gmm, gv = Guarded(master0), Guarded(m0), Guarded(v0)
     flat = Guarded(np.zeros(n, np.uint16), pre=d)
     om, omm, ov = master0.copy(), m0.copy(), v0.copy()
-    prev = F.set_blocks_per_cu(blocks_per_cu)
+    prev = F.set_groups_per_wave(groups)
     try:
         for t in range(1, steps + 1):
             contribs = [W.np_bf16_normal([seed, 100 + t, r], n, grad_std) for r in range(F_in)]
@@ -80,7 +80,7 @@ def run_case(n=None, F_in=8, steps=2, d=0, layout=None, seed=0, warm_state=True,
         for g, what in ((gm, "master"), (gmm, "m"), (gv, "v"), (flat, "flat window")):
             g.assert_guards(what)
     finally:
-        F.set_blocks_per_cu(prev)
+        F.set_groups_per_wave(prev)
 
 
 SIZES = [1, 5, 8, 9, 63, 64, 511, 512, 513, 2047, 2048, 2049, 4103, 8191, 65539, 300001]
@@ -99,10 +99,13 @@ def test_every_output_phase(d, F_in):
     run_case(n=6151, F_in=F_in, d=d, steps=2, seed=40 + d)
 
 
-@pytest.mark.parametrize("bpc", [1, 2, 16])
-def test_many_groups_per_wave(bpc):
-    # few work-groups -> every wave walks many groups; exercises chunk edges and cursors
-    run_case(n=3_000_017, F_in=4, d=5, steps=1, seed=7, blocks_per_cu=bpc)
+@pytest.mark.parametrize("groups", [1, 2, 4])
+@pytest.mark.parametrize("F_in", [1, 3, 8])
+def test_groups_per_wave(groups, F_in):
+    # each setting changes which groups share a wave, its cursor and the tile / tail split
+    run_case(n=300_017, F_in=F_in, d=5, steps=1, seed=7, groups=groups)
+    run_case(layout=([5000, 3, 12000, 1, 1, 1, 7777, 100000], 16, [1, 0, 1, 1, 0, 1, 0, 1], 3, 1),
+             F_in=F_in, steps=1, seed=8, groups=groups, nan_pad=True)
 
 
 def test_bitexact_representative():
@@ -281,3 +284,29 @@ def test_errors_raise():
         F.adamw_shard_step(x[1:], x[1:], x[1:], [c], step=1, n=4, **HP)    # misaligned state
     with pytest.raises(F.FsdpShardError):
         F.adamw_shard_step(x, x, x, [c], step=1, n=4, **HP)                # aliasing state
+
+
+def test_calibration_kernels():
+    """The measurement aids do what their header says (they are not part of the step)."""
+    n = 8 * 3001
+    src = torch.arange(n * 4, dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    F.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    rng = np.random.default_rng(51)
+    grads = [rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16) for _ in range(8)]
+    st = [rng.standard_normal(n).astype(np.float32) for _ in range(3)]
+    dev_s = [torch.from_numpy(x.copy()).cuda() for x in st]
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    F.stream_mix([to_dev16(g) for g in grads], dev_s[0], dev_s[1], dev_s[2], out)
+    torch.cuda.synchronize()
+    words = np.stack([g.view(np.uint32) for g in grads]).reshape(8, -1, 4)
+    x = np.bitwise_xor.reduce(np.bitwise_xor.reduce(words, axis=2), axis=0)   # per 8-element vector
+    for k in range(3):
+        want = st[k].view(np.uint32).reshape(-1, 8).copy()
+        want[:, 0] ^= x
+        assert np.array_equal(dev_s[k].cpu().numpy().view(np.uint32).reshape(-1, 8), want)
+    o = out.cpu().numpy().view(np.uint32).reshape(-1, 4)
+    assert np.array_equal(o[:, 3], x)
+    assert np.array_equal(o[:, 0], st[0].view(np.uint32).reshape(-1, 8)[:, 1])
