@@ -22,6 +22,10 @@ What it computes, and where each piece comes from (page titles as published):
                  copy of the updated master written into the flat layout that the next all-gather
                  serves (communication-pattern passage).
 * accounting  -- the 16-bytes-per-parameter state accounting (2 + 2 + 4 + 8 for mixed precision).
+* clip        -- the global gradient norm of a sharded gradient and the clip coefficient (same
+                 page, gradient-clipping passage).
+* step also holds the fp32 gradient-shard accumulation across micro-batches and the step that
+  consumes such an fp32 shard (mixed-precision passage).
 
 Precision: the pages fix the precision of every stored quantity on this path (fp32 master, m, v
 and reduction; bf16 params and gradients), so the oracle computes in float32 with one IEEE
@@ -29,4 +33,4 @@ rounding per operation and no fused multiply-add, in a fixed operation order.  A
 the same recurrence (``step.adamw_update_f64``) exists only as a diagnostic.
 """
 
-from . import accounting, bf16, layout, step  # noqa: F401
+from . import accounting, bf16, clip, layout, step  # noqa: F401

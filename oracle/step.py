@@ -115,6 +115,28 @@ def shard_step(master, m, v, contribs, flags, hp, step):
     return master, m, v, unflatten_bf16(master, real)
 
 
+def accumulate_fp32(acc, contribs, scale=1.0):
+    """fp32 gradient-shard accumulation across micro-batches: acc + scale * (rank-order sum).
+
+    "FSDP: Fully Sharded Data Parallel Training at Scale", mixed-precision passage (gradients
+    accumulate in float32 so small values are not lost) and the note that gradient accumulation
+    over micro-batches suppresses synchronisation until the last one.  One float32 rounding for
+    the reduction (as reduce_contributions), one for the scale, one for the addition.
+    """
+    return (np.asarray(acc, np.float32) + reduce_contributions(contribs, scale)).astype(F32)
+
+
+def shard_step_f32grad(master, m, v, grad, flags, hp, step):
+    """One step from an fp32 gradient shard (accumulated over micro-batches): g = grad * scale,
+    then the same AdamW and bf16 output as shard_step."""
+    consts = hyper_constants(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                             hp["weight_decay"], step, hp.get("grad_scale", 1.0))
+    wd_on, real = flags_to_masks(flags)
+    g = np.asarray(grad, np.float32) * consts["scale"]
+    master, m, v = adamw_update(master, m, v, g, consts, wd_on, real)
+    return master, m, v, unflatten_bf16(master, real)
+
+
 def adamw_update_f64(master, m, v, g, hp, step, wd_on):
     """Diagnostic float64 shadow of the same recurrence (not a pass/fail reference)."""
     master = np.asarray(master, dtype=np.float64)
