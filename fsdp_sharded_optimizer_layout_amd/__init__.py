@@ -41,7 +41,8 @@ class _Layout(ctypes.Structure):
 class _AdamW(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
-                ("grad_scale", ctypes.c_double), ("step", c_i64)]
+                ("grad_scale", ctypes.c_double), ("step", c_i64),
+                ("max_grad_norm", ctypes.c_double), ("grad_sumsq", c_vp)]
 
 
 # numpy view of fsdpshard_segment (32 bytes)
@@ -76,6 +77,14 @@ def lib():
     h.adamw_shard_step.argtypes = [c_vp, c_vp, c_vp, ctypes.POINTER(c_vp), c_i32, c_i64, c_vp,
                                    c_i32, ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64, c_vp]
     h.unflatten_bf16.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp, c_i64, c_i64, c_vp]
+    h.adamw_shard_step_f32grad.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32,
+                                           ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64, c_vp]
+    h.reduce_shard_accumulate.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float,
+                                          c_vp, c_vp]
+    h.grad_sumsq_workspace_bytes.argtypes = [c_i64]
+    h.grad_sumsq_workspace_bytes.restype = c_i64
+    h.grad_sumsq_shard.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_i64, c_vp, c_i32,
+                                   ctypes.c_float, c_vp, c_i64, c_vp, c_vp]
     h.fsdpshard_strerror.argtypes = [ctypes.c_int]
     h.fsdpshard_strerror.restype = ctypes.c_char_p
     h.fsdpshard_abi_version.argtypes = []
@@ -84,6 +93,7 @@ def lib():
     h.fsdpshard_stream_mix.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_vp, c_vp, c_i64,
                                        c_vp]
     for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
+                 "adamw_shard_step_f32grad", "reduce_shard_accumulate", "grad_sumsq_shard",
                  "fsdpshard_abi_version", "fsdpshard_set_groups_per_wave", "fsdpshard_stream_copy",
                  "fsdpshard_stream_mix"):
         getattr(h, name).restype = ctypes.c_int
@@ -204,21 +214,33 @@ def reduce_shard(contribs, out, scale=1.0, n=None, stream=None):
         _ptr(out, "out", {torch.float32}, n), _stream(stream, out)))
 
 
+def _hp(step, lr, beta1, beta2, eps, weight_decay, grad_scale, max_grad_norm, grad_sumsq):
+    import torch
+    sumsq = None
+    if max_grad_norm:
+        if grad_sumsq is None:
+            raise ValueError("clipping needs grad_sumsq (a device float64 tensor)")
+        sumsq = _ptr(grad_sumsq, "grad_sumsq", {torch.float64}, 1)
+    return _AdamW(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                  float(grad_scale), int(step), float(max_grad_norm or 0.0), sumsq)
+
+
 def adamw_shard_step(master, m, v, contribs, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                      weight_decay=0.0, grad_scale=1.0, segs=None, n_segments=0, flat=None,
-                     flat_index0=0, lo=0, n=None, stream=None):
+                     flat_index0=0, lo=0, n=None, max_grad_norm=0.0, grad_sumsq=None,
+                     stream=None):
     """Fused reduce + AdamW + bf16 unflatten of one slice (see adamw_shard_step in the header).
 
     ``segs``: device byte tensor from segments_to_device (or None), with ``n_segments`` entries.
     ``flat``: device bf16 window of the flat parameter vector starting at flat index
     ``flat_index0``; the slice's elements land at flat indices [lo, lo + n).
+    ``max_grad_norm`` > 0 clips by the global norm whose square is in ``grad_sumsq`` (device).
     """
     import torch
     n = master.numel() if n is None else int(n)
     f32 = {torch.float32}
     arr = _contrib_array(contribs, n)
-    hp = _AdamW(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
-                float(grad_scale), int(step))
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay, grad_scale, max_grad_norm, grad_sumsq)
     if flat is not None and not isinstance(flat, int):
         _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
     _check("adamw_shard_step", lib().adamw_shard_step(
@@ -226,6 +248,64 @@ def adamw_shard_step(master, m, v, contribs, step, lr, beta1=0.9, beta2=0.999, e
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n,
         _ptr(segs, "segs"), int(n_segments), ctypes.byref(hp),
         _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
+
+
+def adamw_shard_step_f32grad(master, m, v, grad, step, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                             weight_decay=0.0, grad_scale=1.0, segs=None, n_segments=0,
+                             flat=None, flat_index0=0, lo=0, n=None, max_grad_norm=0.0,
+                             grad_sumsq=None, stream=None):
+    """As adamw_shard_step, fed by one fp32 gradient shard ``grad``."""
+    import torch
+    n = master.numel() if n is None else int(n)
+    f32 = {torch.float32}
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay, grad_scale, max_grad_norm, grad_sumsq)
+    if flat is not None and not isinstance(flat, int):
+        _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
+    _check("adamw_shard_step_f32grad", lib().adamw_shard_step_f32grad(
+        _ptr(master, "master", f32, n), _ptr(m, "m", f32, n), _ptr(v, "v", f32, n),
+        _ptr(grad, "grad", f32, n), n, _ptr(segs, "segs"), int(n_segments), ctypes.byref(hp),
+        _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
+
+
+def reduce_shard_accumulate(contribs, acc, scale=1.0, n=None, stream=None):
+    """acc[i] += scale * sum over ranks r (in order) of contribs[r][i], in float32."""
+    import torch
+    n = acc.numel() if n is None else int(n)
+    arr = _contrib_array(contribs, n)
+    _check("reduce_shard_accumulate", lib().reduce_shard_accumulate(
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n, float(scale),
+        _ptr(acc, "acc", {torch.float32}, n), _stream(stream, acc)))
+
+
+def grad_sumsq_workspace_bytes(n):
+    return int(lib().grad_sumsq_workspace_bytes(int(n)))
+
+
+def grad_sumsq_shard(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=None,
+                     n_segments=0, workspace=None, stream=None):
+    """Sum of squares of the slice's reduced gradient (float64, fixed order) into ``sumsq`` (a
+    device float64 tensor).  Give either the bf16 ``contribs`` or one fp32 ``grad`` shard.
+    ``workspace``: device tensor of at least grad_sumsq_workspace_bytes(n) bytes (allocated here
+    through PyTorch when omitted)."""
+    import torch
+    if (contribs is None) == (grad is None):
+        raise ValueError("give exactly one of contribs and grad")
+    if n is None:
+        n = grad.numel() if grad is not None else contribs[0].numel()
+    n = int(n)
+    need = grad_sumsq_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=sumsq.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if contribs is not None:
+        arr = _contrib_array(contribs, n)
+        arr_p, fan_in, gp = ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), None
+    else:
+        arr_p, fan_in, gp = None, 0, _ptr(grad, "grad", {torch.float32}, n)
+    _check("grad_sumsq_shard", lib().grad_sumsq_shard(
+        arr_p, fan_in, gp, n, _ptr(segs, "segs"), int(n_segments), float(scale),
+        _ptr(workspace, "workspace"), wbytes, _ptr(sumsq, "sumsq", {torch.float64}, 1),
+        _stream(stream, sumsq)))
 
 
 def unflatten_bf16(master, flat, flat_index0=0, lo=0, segs=None, n_segments=0, n=None,

@@ -58,7 +58,11 @@ struct StepParams {
     float* v;
     const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
     const fsdpshard_segment* segs;
+    const float* grad32;     // fp32 gradient shard (fan-in -1 kernels), else null
     uint16_t* out;           // destination of slice element 0 (flat index lo), or null
+    const double* sumsq;     // global sum of squares of the gradient when clipping, else null
+    double max_norm;         // clip threshold (> 0 when clipping)
+    double grad_scale;       // grad_scale in float64 (the clipped scale is formed from it)
     int64_t n;               // elements in the slice
     int32_t n_segs;
     int32_t fan_in;
@@ -68,9 +72,23 @@ struct StepParams {
 
 struct ReduceParams {
     const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
-    float* out;
+    float* out;              // receives scale * sum (plus its old value when accumulating)
     int64_t n;
     int32_t fan_in;
+    float scale;
+};
+
+struct SumsqParams {
+    const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
+    const float* grad32;     // fp32 gradient shard when fan_in == 0
+    const fsdpshard_segment* segs;
+    double* partials;        // one float64 per work-group
+    double* result;
+    int64_t n;
+    int64_t groups_per_wave;
+    int32_t n_segs;
+    int32_t fan_in;
+    int32_t n_partials;
     float scale;
 };
 
@@ -125,6 +143,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_u4_nt(const uint16_t* p) {
     const u32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     return make_uint4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ void ld8_f32_nt(const float* p, float (&x)[8]) {
+    const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 __device__ __forceinline__ void st_f4_nt(float* p, float a, float b, float c, float d) {
     const f32x4_t v = {a, b, c, d};
@@ -297,22 +321,33 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* out, int64_t e0, int sh
 // ------------------------------------------------------------------------------------------------
 // The fused step.
 
-// Contributions of one vector, summed in rank order from +0.  Every HBM load of the vector is
-// issued before the first add: the compile-time fan-ins load all F vectors at once, the generic
-// path loads four at a time.
+// Gradient sources.  F >= 1: F bf16 contributions, a compile-time count; F == 0: run-time fan-in
+// (p.fan_in); F == -1: one fp32 gradient shard (accumulated over micro-batches).
+//
+// Reduced gradient of one vector, before the scale: the contributions summed in rank order from
+// +0.  Every HBM load is issued before the first add (the run-time fan-in loads four at a time).
 template <int F>
-__device__ __forceinline__ void load_contribs(const StepParams& p, int64_t e0, bool full, int cnt,
-                                              uint4 (&raw)[F > 0 ? F : 1]) {
+__device__ __forceinline__ void load_grad(const StepParams& p, int64_t e0, bool full, int cnt,
+                                          uint4 (&raw)[F > 0 ? F : 1], float (&gf)[kVec]) {
     if constexpr (F > 0) {
 #pragma unroll
         for (int r = 0; r < F; ++r)
-            raw[r] = full ? ld_u4(p.contrib[r] + e0) : ld_u4_partial(p.contrib[r] + e0, cnt);
+            raw[r] = full ? ld_u4_nt(p.contrib[r] + e0) : ld_u4_partial(p.contrib[r] + e0, cnt);
+    } else if constexpr (F == -1) {
+        if (full) ld8_f32_nt(p.grad32 + e0, gf);
+        else load8(p.grad32 + e0, false, cnt, gf);
     }
 }
 
 template <int F>
-__device__ __forceinline__ void sum_contribs(const StepParams& p, int64_t e0, bool full, int cnt,
-                                             const uint4 (&raw)[F > 0 ? F : 1], float (&g)[kVec]) {
+__device__ __forceinline__ void sum_grad(const StepParams& p, int64_t e0, bool full, int cnt,
+                                         const uint4 (&raw)[F > 0 ? F : 1],
+                                         const float (&gf)[kVec], float (&g)[kVec]) {
+    if constexpr (F == -1) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = gf[e];
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
     if constexpr (F > 0) {
@@ -326,7 +361,7 @@ __device__ __forceinline__ void sum_contribs(const StepParams& p, int64_t e0, bo
             for (int q = 0; q < 4; ++q) {
                 if (r0 + q < fan_in) {
                     const uint16_t* src = p.contrib[r0 + q] + e0;
-                    q4[q] = full ? ld_u4(src) : ld_u4_partial(src, cnt);
+                    q4[q] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
                 }
             }
 #pragma unroll
@@ -337,12 +372,12 @@ __device__ __forceinline__ void sum_contribs(const StepParams& p, int64_t e0, bo
 }
 
 // AdamW on 8 elements in registers; padding elements keep their state.
-__device__ __forceinline__ void adam8(const StepParams& p, const uint32_t (&fl)[kVec],
+__device__ __forceinline__ void adam8(const StepParams& p, float scale, const uint32_t (&fl)[kVec],
                                       const float (&g)[kVec], float (&th)[kVec],
                                       float (&mm)[kVec], float (&vv)[kVec]) {
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-        const float gs = g[e] * p.scale;
+        const float gs = g[e] * scale;
         const float m1 = p.b1 * mm[e] + p.c1 * gs;
         const float v1 = p.b2 * vv[e] + p.c2 * (gs * gs);
         const float mh = m1 / p.bc1;
@@ -355,6 +390,16 @@ __device__ __forceinline__ void adam8(const StepParams& p, const uint32_t (&fl)[
         mm[e] = real ? m1 : mm[e];
         vv[e] = real ? v1 : vv[e];
     }
+}
+
+// Scale applied to the reduced gradient: grad_scale, or with clipping
+// float32(grad_scale * min(1, max_norm / (sqrt(global sum of squares) + 1e-6))) in float64.
+__device__ __forceinline__ float step_scale(const StepParams& p) {
+    if (p.sumsq == nullptr) return p.scale;
+    const double s = *p.sumsq;
+    double coef = p.max_norm / (sqrt(s) + 1e-6);
+    coef = coef < 1.0 ? coef : 1.0;
+    return static_cast<float>(p.grad_scale * coef);
 }
 
 // bf16 bits of 8 updated weights, +0 for padding, packed two per dword.
@@ -372,8 +417,8 @@ __device__ __forceinline__ void pack_out(const uint32_t (&fl)[kVec], const float
 // One 512-element group with per-lane bounds: the slice's last, partial group, and every group
 // of the run-time fan-in kernel.  TAIL = false drops the bounds for complete groups.
 template <int F, bool OUT, bool TAIL>
-__device__ __forceinline__ void step_group(const StepParams& p, const SegCursor& cur, int64_t vec,
-                                           int64_t group_end_vec, int lane) {
+__device__ __forceinline__ void step_group(const StepParams& p, float scale, const SegCursor& cur,
+                                           int64_t vec, int64_t group_end_vec, int lane) {
     const int64_t n = p.n;
     const int64_t e0 = vec * kVec;
     const bool valid = !TAIL || vec < group_end_vec;
@@ -381,14 +426,14 @@ __device__ __forceinline__ void step_group(const StepParams& p, const SegCursor&
         !TAIL ? kVec : (valid ? static_cast<int>((n - e0) < kVec ? (n - e0) : kVec) : 0);
     const bool full = !TAIL || cnt == kVec;
 
-    float g[kVec], th[kVec], mm[kVec], vv[kVec];
+    float g[kVec], gf[kVec], th[kVec], mm[kVec], vv[kVec];
     uint4 raw[F > 0 ? F : 1];
     if (valid) {
-        load_contribs<F>(p, e0, full, cnt, raw);
+        load_grad<F>(p, e0, full, cnt, raw, gf);
         load8(p.master + e0, full, cnt, th);
         load8(p.m + e0, full, cnt, mm);
         load8(p.v + e0, full, cnt, vv);
-        sum_contribs<F>(p, e0, full, cnt, raw, g);
+        sum_grad<F>(p, e0, full, cnt, raw, gf, g);
     } else {
 #pragma unroll
         for (int e = 0; e < kVec; ++e) g[e] = th[e] = mm[e] = vv[e] = 0.0f;
@@ -398,7 +443,7 @@ __device__ __forceinline__ void step_group(const StepParams& p, const SegCursor&
     int64_t g1 = group_end_vec * kVec;
     if (g1 > n) g1 = n;
     element_flags(cur, g1, e0, fl);
-    adam8(p, fl, g, th, mm, vv);
+    adam8(p, scale, fl, g, th, mm, vv);
 
     if (valid) {
         store8(p.master + e0, full, cnt, th);
@@ -416,22 +461,36 @@ __device__ __forceinline__ void step_group(const StepParams& p, const SegCursor&
     }
 }
 
-// A wave's whole tile of U complete groups (compile-time fan-in F >= 1): all 14U loads of the
-// tile are issued first (gradients non-temporal), then the segment cursor is placed, then each
-// group is reduced, updated and stored.
+// A wave's whole tile of U complete groups (compile-time gradient source F >= 1 or F == -1):
+// every HBM load of the tile is issued first (gradients non-temporal), then the segment cursor is
+// placed, then each group is reduced, updated and stored.
 template <int F, bool OUT, int U>
 __device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, int lane) {
-    uint4 raw[U][F];
-    float th[U][kVec], mm[U][kVec], vv[U][kVec];
+    uint4 raw[U][F > 0 ? F : 1];
+    float gf[U][kVec], th[U][kVec], mm[U][kVec], vv[U][kVec];
+    // Issue order of the tile's loads, pinned with scheduling barriers because it moves the
+    // kernel's bandwidth by about 2% on MI355X (measured): with one gradient stream every state
+    // load goes first; with several, master and m go first, then the gradients, then v.
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t e0 = (base0 + u * kWave + lane) * kVec;
-#pragma unroll
-        for (int r = 0; r < F; ++r) raw[u][r] = ld_u4_nt(p.contrib[r] + e0);
-        load8(p.master + e0, true, kVec, th[u]);
-        load8(p.m + e0, true, kVec, mm[u]);
-        load8(p.v + e0, true, kVec, vv[u]);
+        if constexpr (F == 1 || F == -1) {
+            load8(p.master + e0, true, kVec, th[u]);
+            load8(p.m + e0, true, kVec, mm[u]);
+            load8(p.v + e0, true, kVec, vv[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_grad<F>(p, e0, true, kVec, raw[u], gf[u]);
+        } else {
+            load8(p.master + e0, true, kVec, th[u]);
+            load8(p.m + e0, true, kVec, mm[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_grad<F>(p, e0, true, kVec, raw[u], gf[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            load8(p.v + e0, true, kVec, vv[u]);
+        }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const float scale = step_scale(p);     // after the loads: its own reads overlap them
     SegCursor cur;
     cur.init(p.segs, p.n_segs, base0 * kVec);
 #pragma unroll
@@ -442,11 +501,8 @@ __device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, in
         uint32_t fl[kVec];
         element_flags(cur, (gb + kWave) * kVec, e0, fl);
         float g[kVec];
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
-#pragma unroll
-        for (int r = 0; r < F; ++r) accumulate(g, raw[u][r]);
-        adam8(p, fl, g, th[u], mm[u], vv[u]);
+        sum_grad<F>(p, e0, true, kVec, raw[u], gf[u], g);
+        adam8(p, scale, fl, g, th[u], mm[u], vv[u]);
         store8(p.master + e0, true, kVec, th[u]);
         store8(p.m + e0, true, kVec, mm[u]);
         store8(p.v + e0, true, kVec, vv[u]);
@@ -473,12 +529,13 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     const int64_t nvec = (p.n + kVec - 1) / kVec;
     const int64_t base0 = tile_base(wave, U);
     if (base0 >= nvec) return;
-    if constexpr (F > 0) {
+    if constexpr (F != 0) {
         if (base0 + kWave * U <= p.n / kVec) {
             step_tile<F, OUT, U>(p, base0, lane);
             return;
         }
     }
+    const float scale = step_scale(p);
     SegCursor cur;
     cur.init(p.segs, p.n_segs, base0 * kVec);
     for (int u = 0; u < U; ++u) {
@@ -488,15 +545,119 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
         if (gend > nvec) gend = nvec;
         cur.seek(gb * kVec);
         if (gend == gb + kWave && gend * kVec <= p.n)
-            step_group<F, OUT, false>(p, cur, gb + lane, gend, lane);
+            step_group<F, OUT, false>(p, scale, cur, gb + lane, gend, lane);
         else
-            step_group<F, OUT, true>(p, cur, gb + lane, gend, lane);
+            step_group<F, OUT, true>(p, scale, cur, gb + lane, gend, lane);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Sum of squares of the reduced gradient (the rank's share of the global norm).
+//
+// Each wave walks G consecutive groups; every lane adds g^2 of its elements in float64 (exact
+// squares of float32 values) in a fixed order, padding excluded; the wave and the work-group then
+// add their lanes in a fixed tree, and one float64 partial per work-group goes to the workspace.
+// A second kernel adds the partials in a fixed order.  The result depends only on n and the data.
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_down(x, off, kWave);
+    return x;   // valid in lane 0
+}
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
+    __shared__ double wave_part[kWavesPerBlock];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int64_t nvec = (p.n + kVec - 1) / kVec;
+    const int64_t base0 =
+        (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * (kWave * p.groups_per_wave);
+    double acc = 0.0;
+    if (base0 < nvec) {
+        SegCursor cur;
+        cur.init(p.segs, p.n_segs, base0 * kVec);
+        for (int64_t gi = 0; gi < p.groups_per_wave; ++gi) {
+            const int64_t gb = base0 + gi * kWave;
+            if (gb >= nvec) break;
+            int64_t gend = gb + kWave;
+            if (gend > nvec) gend = nvec;
+            cur.seek(gb * kVec);
+            const int64_t vec = gb + lane;
+            const int64_t e0 = vec * kVec;
+            const bool valid = vec < gend;
+            const int cnt = valid ? static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec) : 0;
+            const bool full = cnt == kVec;
+            float g[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+            if (valid) {
+                if constexpr (F == -1) {
+                    if (full) ld8_f32_nt(p.grad32 + e0, g);
+                    else load8(p.grad32 + e0, false, cnt, g);
+                } else if constexpr (F > 0) {
+                    uint4 raw[F];
+#pragma unroll
+                    for (int r = 0; r < F; ++r)
+                        raw[r] = full ? ld_u4_nt(p.contrib[r] + e0)
+                                      : ld_u4_partial(p.contrib[r] + e0, cnt);
+#pragma unroll
+                    for (int r = 0; r < F; ++r) accumulate(g, raw[r]);
+                } else {
+                    for (int r = 0; r < p.fan_in; ++r) {
+                        const uint4 q = full ? ld_u4_nt(p.contrib[r] + e0)
+                                             : ld_u4_partial(p.contrib[r] + e0, cnt);
+                        accumulate(g, q);
+                    }
+                }
+            }
+            uint32_t fl[kVec];
+            int64_t g1 = gend * kVec;
+            if (g1 > p.n) g1 = p.n;
+            element_flags(cur, g1, e0, fl);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const float gs = g[e] * p.scale;
+                const double d = static_cast<double>(gs);
+                const bool use = valid && e < cnt && (fl[e] & FSDPSHARD_SEG_PADDING) == 0u;
+                acc += use ? d * d : 0.0;
+            }
+        }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) wave_part[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double b = wave_part[0];
+#pragma unroll
+        for (int w = 1; w < kWavesPerBlock; ++w) b += wave_part[w];
+        p.partials[blockIdx.x] = b;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void sumsq_finish_kernel(SumsqParams p) {
+    __shared__ double wave_part[kWavesPerBlock];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < p.n_partials; i += kBlock) acc += p.partials[i];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    acc = wave_sum(acc);
+    if (lane == 0) wave_part[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double b = wave_part[0];
+#pragma unroll
+        for (int w = 1; w < kWavesPerBlock; ++w) b += wave_part[w];
+        *p.result = b;
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // Standalone reduce and unflatten: one 512-element group per wave.
 
+// ACC = false: out = scale * sum.  ACC = true: out = out + scale * sum (fp32 accumulation of
+// micro-batches; one rounding for the sum, one for the scale, one for the addition).
+template <bool ACC>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
@@ -506,6 +667,8 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
     const int64_t e0 = vec * kVec;
     const int cnt = static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec);
     const bool full = cnt == kVec;
+    float acc[kVec];
+    if constexpr (ACC) load8(p.out + e0, full, cnt, acc);
     float g[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
@@ -523,7 +686,10 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
             if (r0 + q < p.fan_in) accumulate(g, raw[q]);
     }
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) g[e] = g[e] * p.scale;
+    for (int e = 0; e < kVec; ++e) {
+        g[e] = g[e] * p.scale;
+        if constexpr (ACC) g[e] = acc[e] + g[e];
+    }
     store8(p.out + e0, full, cnt, g);
 }
 
@@ -667,8 +833,10 @@ int groups_for(int fan_in) {
     return 1;  // measured fastest on MI355X for every fan-in (one 512-element group per wave)
 }
 
+// fan_in -1 selects the fp32-gradient kernels.
 const void* pick_step_kernel(int fan_in, bool out, int groups) {
     switch (fan_in) {
+        case -1: return step_kernel<-1>(out, groups);
         case 1: return step_kernel<1>(out, groups);
         case 2: return step_kernel<2>(out, groups);
         case 4: return step_kernel<4>(out, groups);
@@ -696,27 +864,33 @@ int check_contribs(const uint16_t* const* contribs, int32_t fan_in, int64_t n) {
 
 bool is_finite(double x) { return std::isfinite(x); }
 
-}  // namespace
-
-// ------------------------------------------------------------------------------------------------
-// C ABI.
-
-extern "C" int adamw_shard_step(float* master, float* m, float* v,
-                                const uint16_t* const* contribs, int32_t fan_in, int64_t n,
-                                const fsdpshard_segment* segs, int32_t n_segments,
-                                const fsdpshard_adamw* hp, uint16_t* flat_bf16,
-                                int64_t flat_index0, int64_t lo, void* stream) {
+// Shared by the two step entry points: exactly one of (contribs, fan_in >= 1) and
+// (grad32, fan_in == -1) is the gradient source.
+int launch_step(float* master, float* m, float* v, const uint16_t* const* contribs, int32_t fan_in,
+                const float* grad32, int64_t n, const fsdpshard_segment* segs, int32_t n_segments,
+                const fsdpshard_adamw* hp, uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
+                void* stream) {
     if (master == nullptr || m == nullptr || v == nullptr || hp == nullptr || n < 0 ||
         n_segments < 0 || (n_segments > 0 && segs == nullptr) || lo < 0)
         return FSDPSHARD_ERR_INVALID_ARG;
-    int rc = check_contribs(contribs, fan_in, n);
-    if (rc != FSDPSHARD_OK) return rc;
+    int rc = FSDPSHARD_OK;
+    if (fan_in == -1) {
+        if (grad32 == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
+        if (!aligned16(grad32)) return FSDPSHARD_ERR_ALIGNMENT;
+    } else {
+        rc = check_contribs(contribs, fan_in, n);
+        if (rc != FSDPSHARD_OK) return rc;
+    }
     if (hp->step < 1 || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
         !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !is_finite(hp->lr) || !is_finite(hp->eps) ||
-        !is_finite(hp->weight_decay) || !is_finite(hp->grad_scale))
+        !is_finite(hp->weight_decay) || !is_finite(hp->grad_scale) ||
+        !is_finite(hp->max_grad_norm) || hp->max_grad_norm < 0.0 ||
+        (hp->max_grad_norm > 0.0 && hp->grad_sumsq == nullptr))
         return FSDPSHARD_ERR_INVALID_ARG;
     if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return FSDPSHARD_ERR_ALIGNMENT;
     if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
+        return FSDPSHARD_ERR_ALIGNMENT;
+    if (hp->max_grad_norm > 0.0 && (reinterpret_cast<uintptr_t>(hp->grad_sumsq) & 7u) != 0)
         return FSDPSHARD_ERR_ALIGNMENT;
     uint16_t* out = nullptr;
     if (flat_bf16 != nullptr) {
@@ -734,8 +908,14 @@ extern "C" int adamw_shard_step(float* master, float* m, float* v,
         for (int j = i + 1; j < 4; ++j)
             if (wr[j] != nullptr && overlaps(wr[i], wb[i], wr[j], wb[j]))
                 return FSDPSHARD_ERR_INVALID_ARG;
-        for (int r = 0; r < fan_in; ++r)
-            if (overlaps(wr[i], wb[i], contribs[r], hb)) return FSDPSHARD_ERR_INVALID_ARG;
+        if (fan_in == -1) {
+            if (overlaps(wr[i], wb[i], grad32, fb)) return FSDPSHARD_ERR_INVALID_ARG;
+        } else {
+            for (int r = 0; r < fan_in; ++r)
+                if (overlaps(wr[i], wb[i], contribs[r], hb)) return FSDPSHARD_ERR_INVALID_ARG;
+        }
+        if (hp->max_grad_norm > 0.0 && overlaps(wr[i], wb[i], hp->grad_sumsq, 8))
+            return FSDPSHARD_ERR_INVALID_ARG;
     }
     if (n == 0) return FSDPSHARD_OK;
 
@@ -743,9 +923,14 @@ extern "C" int adamw_shard_step(float* master, float* m, float* v,
     p.master = master;
     p.m = m;
     p.v = v;
-    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
+        p.contrib[r] = (fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
     p.segs = segs;
+    p.grad32 = fan_in == -1 ? grad32 : nullptr;
     p.out = out;
+    p.sumsq = hp->max_grad_norm > 0.0 ? hp->grad_sumsq : nullptr;
+    p.max_norm = hp->max_grad_norm;
+    p.grad_scale = hp->grad_scale;
     p.n = n;
     p.n_segs = segs == nullptr ? 0 : n_segments;
     p.fan_in = fan_in;
@@ -769,8 +954,8 @@ extern "C" int adamw_shard_step(float* master, float* m, float* v,
     return launch(pick_step_kernel(fan_in, out != nullptr, groups), blocks, &p, stream);
 }
 
-extern "C" int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
-                            float scale, float* out, void* stream) {
+int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, float scale,
+                  float* out, bool accumulate, void* stream) {
     if (out == nullptr || n < 0) return FSDPSHARD_ERR_INVALID_ARG;
     int rc = check_contribs(contribs, fan_in, n);
     if (rc != FSDPSHARD_OK) return rc;
@@ -788,7 +973,109 @@ extern "C" int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int
     unsigned blocks = 0;
     rc = tile_grid(n, 1, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(reinterpret_cast<const void*>(&reduce_kernel), blocks, &p, stream);
+    return launch(accumulate ? reinterpret_cast<const void*>(&reduce_kernel<true>)
+                             : reinterpret_cast<const void*>(&reduce_kernel<false>),
+                  blocks, &p, stream);
+}
+
+// Sum-of-squares grid: each wave walks kSumsqGroups groups; one float64 partial per work-group.
+constexpr int64_t kSumsqGroups = 16;
+
+int64_t sumsq_partials(int64_t n) {
+    const int64_t nvec = (n + kVec - 1) / kVec;
+    const int64_t per_block = static_cast<int64_t>(kWavesPerBlock) * kWave * kSumsqGroups;
+    return (nvec + per_block - 1) / per_block;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// C ABI.
+
+extern "C" int adamw_shard_step(float* master, float* m, float* v,
+                                const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                                const fsdpshard_segment* segs, int32_t n_segments,
+                                const fsdpshard_adamw* hp, uint16_t* flat_bf16,
+                                int64_t flat_index0, int64_t lo, void* stream) {
+    if (fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
+    return launch_step(master, m, v, contribs, fan_in, nullptr, n, segs, n_segments, hp, flat_bf16,
+                       flat_index0, lo, stream);
+}
+
+extern "C" int adamw_shard_step_f32grad(float* master, float* m, float* v, const float* grad,
+                                        int64_t n, const fsdpshard_segment* segs,
+                                        int32_t n_segments, const fsdpshard_adamw* hp,
+                                        uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
+                                        void* stream) {
+    return launch_step(master, m, v, nullptr, -1, grad, n, segs, n_segments, hp, flat_bf16,
+                       flat_index0, lo, stream);
+}
+
+extern "C" int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                            float scale, float* out, void* stream) {
+    return launch_reduce(contribs, fan_in, n, scale, out, false, stream);
+}
+
+extern "C" int reduce_shard_accumulate(const uint16_t* const* contribs, int32_t fan_in,
+                                       int64_t n, float scale, float* acc, void* stream) {
+    return launch_reduce(contribs, fan_in, n, scale, acc, true, stream);
+}
+
+extern "C" int64_t grad_sumsq_workspace_bytes(int64_t n) {
+    if (n < 0) return -1;
+    return sumsq_partials(n) * static_cast<int64_t>(sizeof(double));
+}
+
+extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
+                                const float* grad, int64_t n, const fsdpshard_segment* segs,
+                                int32_t n_segments, float scale, void* workspace,
+                                int64_t workspace_bytes, double* sumsq, void* stream) {
+    if (n < 0 || sumsq == nullptr || n_segments < 0 || (n_segments > 0 && segs == nullptr))
+        return FSDPSHARD_ERR_INVALID_ARG;
+    if (fan_in == 0) {
+        if (grad == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
+        if (!aligned16(grad)) return FSDPSHARD_ERR_ALIGNMENT;
+    } else {
+        const int rc = check_contribs(contribs, fan_in, n);
+        if (rc != FSDPSHARD_OK) return rc;
+    }
+    if ((reinterpret_cast<uintptr_t>(sumsq) & 7u) != 0) return FSDPSHARD_ERR_ALIGNMENT;
+    if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
+        return FSDPSHARD_ERR_ALIGNMENT;
+    if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
+    const int64_t parts = sumsq_partials(n);
+    if (parts > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
+    const int64_t need = parts * static_cast<int64_t>(sizeof(double));
+    if (parts > 0 && (workspace == nullptr || workspace_bytes < need))
+        return FSDPSHARD_ERR_CAPACITY;
+    if (parts > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+        return FSDPSHARD_ERR_ALIGNMENT;
+    if (parts > 0 && overlaps(workspace, need, sumsq, 8)) return FSDPSHARD_ERR_INVALID_ARG;
+    SumsqParams p;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
+        p.contrib[r] = (fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
+    p.grad32 = fan_in == 0 ? grad : nullptr;
+    p.segs = segs;
+    p.partials = static_cast<double*>(workspace);
+    p.result = sumsq;
+    p.n = n;
+    p.groups_per_wave = kSumsqGroups;
+    p.n_segs = segs == nullptr ? 0 : n_segments;
+    p.fan_in = fan_in;
+    p.n_partials = static_cast<int32_t>(parts);
+    p.scale = scale;
+    int rc = FSDPSHARD_OK;
+    if (parts > 0) {
+        const void* k = fan_in == 0   ? reinterpret_cast<const void*>(&sumsq_kernel<-1>)
+                        : fan_in == 1 ? reinterpret_cast<const void*>(&sumsq_kernel<1>)
+                        : fan_in == 4 ? reinterpret_cast<const void*>(&sumsq_kernel<4>)
+                        : fan_in == 8 ? reinterpret_cast<const void*>(&sumsq_kernel<8>)
+                                      : reinterpret_cast<const void*>(&sumsq_kernel<0>);
+        rc = launch(k, static_cast<unsigned>(parts), &p, stream);
+        if (rc != FSDPSHARD_OK) return rc;
+    }
+    // One work-group adds the partials (or writes +0 for an empty slice).
+    return launch(reinterpret_cast<const void*>(&sumsq_finish_kernel), 1, &p, stream);
 }
 
 extern "C" int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs,

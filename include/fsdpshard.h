@@ -69,11 +69,14 @@ typedef struct fsdpshard_layout {
 /* AdamW hyperparameters of one step (float64 on the host; see adamw_shard_step). */
 typedef struct fsdpshard_adamw {
     double lr;
-    double beta1, beta2;    /* each in [0, 1)                                     */
+    double beta1, beta2;        /* each in [0, 1)                                          */
     double eps;
-    double weight_decay;    /* decoupled, scaled by lr                            */
-    double grad_scale;      /* multiplies the reduced gradient; 1.0 = plain sum   */
-    int64_t step;           /* 1-based step counter t, incremented by the caller  */
+    double weight_decay;        /* decoupled, scaled by lr                                 */
+    double grad_scale;          /* multiplies the reduced gradient; 1.0 = plain sum        */
+    int64_t step;               /* 1-based step counter t, incremented by the caller       */
+    double max_grad_norm;       /* > 0: clip by the global gradient norm; 0: no clipping   */
+    const double* grad_sumsq;   /* device: global sum of g^2 (see grad_sumsq_shard); read
+                                   by the kernel when max_grad_norm > 0, else ignored      */
 } fsdpshard_adamw;
 
 /*
@@ -137,6 +140,10 @@ int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n, flo
  * with c1 = 1-beta1, c2 = 1-beta2, bc1 = 1-beta1^t, bc2 = 1-beta2^t, dec = 1-lr*weight_decay
  * formed in float64 and rounded to float32 once.  Padding elements keep master, m and v bit for
  * bit and are served as +0; their gradient values are ignored.
+ * Clipping ([FSDP], gradient-clipping passage: the norm must be the global one, not the rank's):
+ * when hp->max_grad_norm > 0 the scale above is float32(grad_scale * min(1, max_grad_norm /
+ * (sqrt(*hp->grad_sumsq) + 1e-6))), formed in float64 on the device from the global sum of
+ * squares, so no host synchronisation is needed between the norm and the step.
  *
  *   master, m, v  device, n floats each, 16-byte aligned, updated in place
  *   contribs      host array of fan_in device pointers, each to n bf16 values, 16-byte aligned
@@ -151,13 +158,69 @@ int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n, flo
  *   lo            flat index of the slice start, flat_index0 <= lo
  * No written buffer may overlap another buffer of the call.
  * Errors: INVALID_ARG (nulls, n < 0, step < 1, betas outside [0,1), non-finite values,
- *         overlaps, n_segments < 0), ALIGNMENT, UNSUPPORTED, HIP.
+ *         negative max_grad_norm, clipping without grad_sumsq, overlaps, n_segments < 0),
+ *         ALIGNMENT, UNSUPPORTED, HIP.
  */
 int adamw_shard_step(float* master, float* m, float* v,
                      const uint16_t* const* contribs, int32_t fan_in, int64_t n,
                      const fsdpshard_segment* segs, int32_t n_segments,
                      const fsdpshard_adamw* hp,
                      uint16_t* flat_bf16, int64_t flat_index0, int64_t lo, void* stream);
+
+/*
+ * adamw_shard_step_f32grad -- adamw_shard_step fed by one fp32 gradient shard instead of F bf16
+ * contributions: g = grad[i] * scale (scale as in adamw_shard_step, clipping included).
+ *
+ * [FSDP], mixed-precision passage: gradients accumulated in float32 (reduce_dtype) keep small
+ * values; gradient accumulation over micro-batches suppresses the synchronisation until the last
+ * one.  reduce_shard / reduce_shard_accumulate build `grad` over the micro-batches.
+ *   grad   device, n floats, 16-byte aligned, read only, must not overlap a written buffer
+ *   other arguments as in adamw_shard_step.
+ * Errors: as adamw_shard_step.
+ */
+int adamw_shard_step_f32grad(float* master, float* m, float* v, const float* grad, int64_t n,
+                             const fsdpshard_segment* segs, int32_t n_segments,
+                             const fsdpshard_adamw* hp, uint16_t* flat_bf16, int64_t flat_index0,
+                             int64_t lo, void* stream);
+
+/*
+ * reduce_shard_accumulate -- acc[i] = acc[i] + scale * (((+0 + G_0[i]) + ...) + G_{F-1}[i]).
+ *
+ * [FSDP], mixed-precision passage (float32 gradient accumulation) and its note on accumulating
+ * over micro-batches before synchronising: one micro-batch's reduced contributions added to an
+ * fp32 gradient shard, each of the three steps one float32 rounding.
+ *   acc    device, n floats, 16-byte aligned, updated in place; other arguments as reduce_shard.
+ * Errors: as reduce_shard.
+ */
+int reduce_shard_accumulate(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                            float scale, float* acc, void* stream);
+
+/*
+ * grad_sumsq_workspace_bytes -- device workspace grad_sumsq_shard needs for an n-element slice
+ * (8 bytes per 32,768 elements, rounded up); -1 for n < 0.
+ */
+int64_t grad_sumsq_workspace_bytes(int64_t n);
+
+/*
+ * grad_sumsq_shard -- this rank's share of the squared global gradient norm: the sum over the
+ * slice's real elements of g_i^2, g_i the float32 reduced gradient times `scale` (as in
+ * reduce_shard), each square exact in float64, the sum in float64 in a fixed order (so the
+ * result depends only on n and the data).
+ *
+ * [FSDP], gradient-clipping passage: a norm computed from one rank's slice underestimates the
+ * global norm; the ranks' sums of squares are added (a scalar all-reduce across ranks) and the
+ * total feeds adamw_shard_step's clipping through hp->grad_sumsq.
+ *   contribs, fan_in  the bf16 contributions as in reduce_shard (fan_in 1 .. 64), or
+ *   grad              with fan_in == 0: one fp32 gradient shard (16-byte aligned)
+ *   segs, n_segments  as in adamw_shard_step (padding does not count)
+ *   workspace         device, >= grad_sumsq_workspace_bytes(n) bytes, 8-byte aligned, scratch
+ *   sumsq             device, one double, receives the sum (+0 for n == 0)
+ * Two kernels are enqueued on `stream`; the workspace may be reused once they have run.
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, CAPACITY (workspace too small), OVERFLOW, HIP.
+ */
+int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in, const float* grad,
+                     int64_t n, const fsdpshard_segment* segs, int32_t n_segments, float scale,
+                     void* workspace, int64_t workspace_bytes, double* sumsq, void* stream);
 
 /*
  * unflatten_bf16 -- flat[lo + i] = bf16_rne(master[i]) for real elements, +0 for padding.

@@ -220,7 +220,57 @@ def test_groups_per_wave_knob():
 
 def test_segment_dtype_matches_struct():
     assert F.SEGMENT_DTYPE.itemsize == ctypes.sizeof(F._Segment) == 32
-    assert ctypes.sizeof(F._AdamW) == 56 and ctypes.sizeof(F._Layout) == 48
+    assert ctypes.sizeof(F._AdamW) == 72 and ctypes.sizeof(F._Layout) == 48
     L, segs = F.shard_layout([5, 3], 2, 0, 4, [1, 0])
     raw = np.ascontiguousarray(segs).view(np.uint8)
     assert raw.size == 32 * L.n_segments
+
+
+def test_fp32_grad_step_and_accumulate_validation():
+    lib = F.lib()
+    hp = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    a, b, c, g, out = (_Fake.at(i) for i in range(5))
+    f = lib.adamw_shard_step_f32grad
+    assert f(a, b, c, g, 0, None, 0, ctypes.byref(hp), out, 0, 0, None) == OK
+    assert f(a, b, c, None, 0, None, 0, ctypes.byref(hp), out, 0, 0, None) == INVALID
+    assert f(a, b, c, g + 4, 0, None, 0, ctypes.byref(hp), out, 0, 0, None) == ALIGN
+    assert f(a, b, c, a + 64, 100, None, 0, ctypes.byref(hp), out, 0, 0, None) == INVALID  # overlap
+    # the bf16 entry point never takes the fp32 path
+    arr = (ctypes.c_void_p * 1)(g)
+    assert lib.adamw_shard_step(a, b, c, arr, -1, 0, None, 0, ctypes.byref(hp), out, 0, 0, None) == INVALID
+    # clipping needs a sum-of-squares pointer, non-negative finite threshold, 8-byte alignment
+    clip = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1, 1.0, None)
+    assert f(a, b, c, g, 0, None, 0, ctypes.byref(clip), out, 0, 0, None) == INVALID
+    clip.grad_sumsq = _Fake.at(6, 4)
+    assert f(a, b, c, g, 0, None, 0, ctypes.byref(clip), out, 0, 0, None) == ALIGN
+    clip.grad_sumsq = _Fake.at(6)
+    assert f(a, b, c, g, 0, None, 0, ctypes.byref(clip), out, 0, 0, None) == OK
+    clip.max_grad_norm = -1.0
+    assert f(a, b, c, g, 0, None, 0, ctypes.byref(clip), out, 0, 0, None) == INVALID
+    acc = lib.reduce_shard_accumulate
+    arr2 = (ctypes.c_void_p * 2)(_Fake.at(3), _Fake.at(4))
+    assert acc(arr2, 2, 0, 1.0, out, None) == OK
+    assert acc(arr2, 2, 0, 1.0, out + 4, None) == ALIGN
+    assert acc(arr2, 2, 100, 1.0, _Fake.at(3, 16), None) == INVALID
+
+
+def test_sumsq_validation_and_workspace():
+    lib = F.lib()
+    assert F.grad_sumsq_workspace_bytes(0) == 0
+    assert F.grad_sumsq_workspace_bytes(1) == 8
+    assert F.grad_sumsq_workspace_bytes(32768) == 8          # one partial per 32,768 elements
+    assert F.grad_sumsq_workspace_bytes(32769) == 16
+    assert F.grad_sumsq_workspace_bytes(905_216_000) == 8 * 27_625
+    assert lib.grad_sumsq_workspace_bytes(-1) == -1
+    arr = (ctypes.c_void_p * 2)(_Fake.at(3), _Fake.at(4))
+    ws, res, g = _Fake.at(7), _Fake.at(8), _Fake.at(9)
+    f = lib.grad_sumsq_shard
+    assert f(arr, 2, None, 100, None, 0, 1.0, ws, 0, res, None) == CAPACITY
+    assert f(arr, 2, None, 100, None, 0, 1.0, None, 8, res, None) == CAPACITY
+    assert f(arr, 2, None, 100, None, 0, 1.0, ws, 8, None, None) == INVALID
+    assert f(arr, 2, None, 100, None, 0, 1.0, ws, 8, res + 4, None) == ALIGN
+    assert f(arr, 2, None, 100, None, 0, 1.0, ws + 4, 8, res, None) == ALIGN
+    assert f(None, 0, None, 100, None, 0, 1.0, ws, 8, res, None) == INVALID
+    assert f(None, 0, g + 8, 100, None, 0, 1.0, ws, 8, res, None) == ALIGN
+    assert f(arr, 2, None, -1, None, 0, 1.0, ws, 8, res, None) == INVALID
+    assert f(arr, 2, None, 100, None, 0, 1.0, ws, 8, ws, None) == INVALID          # overlap
