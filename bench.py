@@ -42,6 +42,11 @@ def algorithmic_bytes_per_param(fan_in):
     return 2 * fan_in + 3 * 4 * 2 + 2
 
 
+def algorithmic_bytes_per_param_f32grad():
+    """The fused step fed by an fp32 gradient shard: 4 B gradient read, 24 B state, 2 B bf16."""
+    return 4 + 3 * 4 * 2 + 2
+
+
 def source_digest():
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -148,6 +153,11 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--groups-per-wave", type=int, default=0,
                     help="512-element groups per wavefront (1, 2, 4; 0 = library default)")
+    ap.add_argument("--path", choices=["fused", "clipped", "accumulate"], default="fused",
+                    help="fused: the fused step (default); clipped: sum of squares + clipped "
+                         "step; accumulate: fp32 micro-batch accumulation + clipped fp32 step")
+    ap.add_argument("--micro-batches", type=int, default=4)
+    ap.add_argument("--max-grad-norm", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-reference", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -194,39 +204,79 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
+    bpp = algorithmic_bytes_per_param(Fi)
+    common = dict(segs=segs_dev, n_segments=L.n_segments, flat=flat, flat_index0=lo - phase,
+                  lo=lo, stream=stream, **w.hp)
+
+    # Stages of one step: (name, launch(t), algorithmic bytes per launch).  The fused path is the
+    # default; the clipped and accumulate paths measure the clipping and micro-batch rows.
+    stages = []
+    if args.path == "fused":
+        stages.append(("adamw_shard_step", lambda t: F.adamw_shard_step(
+            master, m, v, grads, step=t, **common), L.n_real * bpp))
+    else:
+        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        ws = torch.empty(max(8, F.grad_sumsq_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+        if args.path == "clipped":
+            stages.append(("grad_sumsq_shard", lambda t: F.grad_sumsq_shard(
+                sumsq, contribs=grads, n=n, segs=segs_dev, n_segments=L.n_segments,
+                workspace=ws, stream=stream), n * 2 * Fi))
+            stages.append(("adamw_shard_step (clipped)", lambda t: F.adamw_shard_step(
+                master, m, v, grads, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
+                **common), L.n_real * bpp))
+        else:
+            acc = torch.empty(n, dtype=torch.float32, device=dev)
+            stages.append(("reduce_shard", lambda t: F.reduce_shard(grads, acc, stream=stream),
+                           n * (2 * Fi + 4)))
+            for mb in range(1, args.micro_batches):
+                stages.append((f"reduce_shard_accumulate[{mb}]", lambda t: F.reduce_shard_accumulate(
+                    grads, acc, stream=stream), n * (2 * Fi + 8)))
+            stages.append(("grad_sumsq_shard (fp32)", lambda t: F.grad_sumsq_shard(
+                sumsq, grad=acc, n=n, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
+                stream=stream), n * 4))
+            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: F.adamw_shard_step_f32grad(
+                master, m, v, acc, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
+                **common), L.n_real * algorithmic_bytes_per_param_f32grad()))
 
     def one_step(t, ev=None):
         F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
-        if ev is not None:
-            ev[0].record(stream)
-        F.adamw_shard_step(master, m, v, grads, step=t, segs=segs_dev, n_segments=L.n_segments,
-                           flat=flat, flat_index0=lo - phase, lo=lo, stream=stream, **w.hp)
-        if ev is not None:
-            ev[1].record(stream)
+        for i, (_, launch, _) in enumerate(stages):
+            if ev is not None:
+                ev[i][0].record(stream)
+            launch(t)
+            if ev is not None:
+                ev[i][1].record(stream)
 
     for t in range(1, args.warmup + 1):
         one_step(t)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in stages] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         one_step(args.warmup + 1 + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [a.elapsed_time(b) for a, b in events]
-    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
     ms_per_step = wall / args.steps * 1e3
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; kernel avg {avg_kernel_s*1e3:.3f} ms "
-        f"(min {min(kernel_ms):.3f}, max {max(kernel_ms):.3f})")
+    stage_info = []
+    for j, (name, _, nbytes) in enumerate(stages):
+        ms = [events[i][j][0].elapsed_time(events[i][j][1]) for i in range(args.steps)]
+        avg = sum(ms) / len(ms)
+        stage_info.append({"call": name, "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4),
+                           "algorithmic_bytes": nbytes,
+                           "GBps": round(nbytes / (avg / 1e3) / 1e9, 1)})
+    main_stage = max(stage_info, key=lambda x: x["avg_ms"])
+    avg_kernel_s = main_stage["avg_ms"] / 1e3
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; kernel avg {avg_kernel_s*1e3:.3f} ms")
+    for x in stage_info:
+        log(f"  {x['call']}: {x['avg_ms']:.3f} ms, {x['GBps']} GB/s")
 
-    bpp = algorithmic_bytes_per_param(Fi)
-    alg_bytes = L.n_real * bpp
+    alg_bytes = main_stage["algorithmic_bytes"]
     achieved = alg_bytes / avg_kernel_s / 1e9
-    traffic = counter_traffic(w.name)
+    traffic = counter_traffic(w.name) if args.path == "fused" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": traffic}
@@ -234,7 +284,7 @@ def main():
     # Same streams, same grid, trivial arithmetic: the ceiling of this access pattern.
     n8 = n - n % 8
     mix_ref = None
-    if not args.no_copy_reference and n8 > 0:
+    if not args.no_copy_reference and n8 > 0 and args.path == "fused":
         out16 = flat[phase:phase + n8] if phase == 0 else torch.empty(n8, dtype=torch.int16,
                                                                         device=dev)
         for _ in range(2):
@@ -305,9 +355,12 @@ def main():
             "fan_in": Fi,
             "segments": L.n_segments,
             "storage": "bf16 grads and params, fp32 master/m/v",
-            "algorithmic_bytes_per_param": bpp,
-            "achieved_GBps_wall": round(alg_bytes / (ms_per_step / 1e3) / 1e9, 1),
+            "algorithmic_bytes_per_param": bpp if args.path == "fused" else None,
+            "achieved_GBps_wall": round(sum(x["algorithmic_bytes"] for x in stage_info)
+                                        / (ms_per_step / 1e3) / 1e9, 1),
             "kernel_avg_ms": round(avg_kernel_s * 1e3, 4),
+            "path": args.path,
+            "stages": stage_info,
             "groups_per_wave": args.groups_per_wave or "default",
         },
         "roofline": roofline,

@@ -554,9 +554,10 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
 // ------------------------------------------------------------------------------------------------
 // Sum of squares of the reduced gradient (the rank's share of the global norm).
 //
-// Each wave walks G consecutive groups; every lane adds g^2 of its elements in float64 (exact
-// squares of float32 values) in a fixed order, padding excluded; the wave and the work-group then
-// add their lanes in a fixed tree, and one float64 partial per work-group goes to the workspace.
+// Each wave walks G consecutive groups; every lane squares its elements in float64 (exact squares
+// of float32 values), adds each vector's 8 squares in a fixed pairwise tree and the vectors in
+// group order, padding excluded; the wave and the work-group then add their lanes in a fixed
+// tree, and one float64 partial per work-group goes to the workspace.
 // A second kernel adds the partials in a fixed order.  The result depends only on n and the data.
 
 __device__ __forceinline__ double wave_sum(double x) {
@@ -565,8 +566,14 @@ __device__ __forceinline__ double wave_sum(double x) {
     return x;   // valid in lane 0
 }
 
+// Groups whose loads one wave issues together in the sum-of-squares kernel (measured: issuing a
+// second group's loads early does not help on MI355X and costs a quarter at fan-in 1).
+template <int F>
+constexpr int sumsq_batch() { return 1; }
+
 template <int F>
 __global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
+    constexpr int B = sumsq_batch<F>();
     __shared__ double wave_part[kWavesPerBlock];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
@@ -577,50 +584,66 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
     if (base0 < nvec) {
         SegCursor cur;
         cur.init(p.segs, p.n_segs, base0 * kVec);
-        for (int64_t gi = 0; gi < p.groups_per_wave; ++gi) {
-            const int64_t gb = base0 + gi * kWave;
-            if (gb >= nvec) break;
-            int64_t gend = gb + kWave;
-            if (gend > nvec) gend = nvec;
-            cur.seek(gb * kVec);
-            const int64_t vec = gb + lane;
-            const int64_t e0 = vec * kVec;
-            const bool valid = vec < gend;
-            const int cnt = valid ? static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec) : 0;
-            const bool full = cnt == kVec;
-            float g[kVec];
+        for (int64_t g0 = 0; g0 < p.groups_per_wave; g0 += B) {
+            if (base0 + g0 * kWave >= nvec) break;
+            // Loads of B groups first (lanes past the slice end load nothing).
+            float g[B][kVec];
+            int cnt[B];
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
-            if (valid) {
-                if constexpr (F == -1) {
-                    if (full) ld8_f32_nt(p.grad32 + e0, g);
-                    else load8(p.grad32 + e0, false, cnt, g);
-                } else if constexpr (F > 0) {
-                    uint4 raw[F];
+            for (int b = 0; b < B; ++b) {
+                const int64_t e0 = (base0 + (g0 + b) * kWave + lane) * kVec;
+                const int64_t left = p.n - e0;
+                cnt[b] = left <= 0 ? 0 : static_cast<int>(left < kVec ? left : kVec);
+                const bool full = cnt[b] == kVec;
 #pragma unroll
-                    for (int r = 0; r < F; ++r)
-                        raw[r] = full ? ld_u4_nt(p.contrib[r] + e0)
-                                      : ld_u4_partial(p.contrib[r] + e0, cnt);
+                for (int e = 0; e < kVec; ++e) g[b][e] = 0.0f;
+                if (cnt[b] > 0 && g0 + b < p.groups_per_wave) {
+                    if constexpr (F == -1) {
+                        if (full) ld8_f32_nt(p.grad32 + e0, g[b]);
+                        else load8(p.grad32 + e0, false, cnt[b], g[b]);
+                    } else if constexpr (F > 0) {
+                        uint4 raw[F];
 #pragma unroll
-                    for (int r = 0; r < F; ++r) accumulate(g, raw[r]);
-                } else {
-                    for (int r = 0; r < p.fan_in; ++r) {
-                        const uint4 q = full ? ld_u4_nt(p.contrib[r] + e0)
-                                             : ld_u4_partial(p.contrib[r] + e0, cnt);
-                        accumulate(g, q);
+                        for (int r = 0; r < F; ++r)
+                            raw[r] = full ? ld_u4_nt(p.contrib[r] + e0)
+                                          : ld_u4_partial(p.contrib[r] + e0, cnt[b]);
+#pragma unroll
+                        for (int r = 0; r < F; ++r) accumulate(g[b], raw[r]);
+                    } else {
+                        for (int r = 0; r < p.fan_in; ++r) {
+                            const uint4 q = full ? ld_u4_nt(p.contrib[r] + e0)
+                                                 : ld_u4_partial(p.contrib[r] + e0, cnt[b]);
+                            accumulate(g[b], q);
+                        }
                     }
+                } else {
+                    cnt[b] = 0;
                 }
             }
-            uint32_t fl[kVec];
-            int64_t g1 = gend * kVec;
-            if (g1 > p.n) g1 = p.n;
-            element_flags(cur, g1, e0, fl);
+            // Then the squares, group by group, element by element (a fixed order).
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) {
-                const float gs = g[e] * p.scale;
-                const double d = static_cast<double>(gs);
-                const bool use = valid && e < cnt && (fl[e] & FSDPSHARD_SEG_PADDING) == 0u;
-                acc += use ? d * d : 0.0;
+            for (int b = 0; b < B; ++b) {
+                const int64_t gb = base0 + (g0 + b) * kWave;
+                if (gb >= nvec || g0 + b >= p.groups_per_wave) break;
+                int64_t gend = gb + kWave;
+                if (gend > nvec) gend = nvec;
+                cur.seek(gb * kVec);
+                const int64_t e0 = (gb + lane) * kVec;
+                uint32_t fl[kVec];
+                int64_t g1 = gend * kVec;
+                if (g1 > p.n) g1 = p.n;
+                element_flags(cur, g1, e0, fl);
+                // Squares of the vector's 8 elements, added as a fixed pairwise tree, then into
+                // the lane's running sum (shorter dependency chain than 8 sequential adds).
+                double q[kVec];
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    const float gs = g[b][e] * p.scale;
+                    const double d = static_cast<double>(gs);
+                    const bool use = e < cnt[b] && (fl[e] & FSDPSHARD_SEG_PADDING) == 0u;
+                    q[e] = use ? d * d : 0.0;
+                }
+                acc += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
             }
         }
     }
@@ -655,42 +678,83 @@ __global__ __launch_bounds__(kBlock) void sumsq_finish_kernel(SumsqParams p) {
 // ------------------------------------------------------------------------------------------------
 // Standalone reduce and unflatten: one 512-element group per wave.
 
+// Groups per wave of the reduce kernels (measured on MI355X: two groups per wave pay off only
+// when eight or more contribution streams are read; below that one group per wave is fastest).
+template <int F>
+constexpr int reduce_groups() { return F >= 8 ? 2 : 1; }
+
 // ACC = false: out = scale * sum.  ACC = true: out = out + scale * sum (fp32 accumulation of
 // micro-batches; one rounding for the sum, one for the scale, one for the addition).
-template <bool ACC>
+// F >= 1 is a compile-time fan-in, F == 0 the run-time one; each wave owns reduce_groups<F>()
+// consecutive groups, and a complete tile issues all its loads before the first add.
+template <int F, bool ACC>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
+    constexpr int U = reduce_groups<F>();
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
-    const int64_t vec = tile_base(wave, 1) + lane;
-    if (vec >= nvec) return;
-    const int64_t e0 = vec * kVec;
-    const int cnt = static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec);
-    const bool full = cnt == kVec;
-    float acc[kVec];
-    if constexpr (ACC) load8(p.out + e0, full, cnt, acc);
-    float g[kVec];
+    const int64_t base0 = tile_base(wave, U);
+    if (base0 >= nvec) return;
+    if constexpr (F > 0) {
+        if (base0 + kWave * U <= p.n / kVec) {
+            uint4 raw[U][F];
+            float acc[U][kVec];
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
-    for (int r0 = 0; r0 < p.fan_in; r0 += 4) {
-        uint4 raw[4];
+            for (int u = 0; u < U; ++u) {
+                const int64_t e0 = (base0 + u * kWave + lane) * kVec;
+                if constexpr (ACC) load8(p.out + e0, true, kVec, acc[u]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (r0 + q < p.fan_in) {
-                const uint16_t* src = p.contrib[r0 + q] + e0;
-                raw[q] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
+                for (int r = 0; r < F; ++r) raw[u][r] = ld_u4_nt(p.contrib[r] + e0);
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t e0 = (base0 + u * kWave + lane) * kVec;
+                float g[kVec];
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+#pragma unroll
+                for (int r = 0; r < F; ++r) accumulate(g, raw[u][r]);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) {
+                    g[e] = g[e] * p.scale;
+                    if constexpr (ACC) g[e] = acc[u][e] + g[e];
+                }
+                store8(p.out + e0, true, kVec, g);
+            }
+            return;
+        }
+    }
+    for (int u = 0; u < U; ++u) {
+        const int64_t vec = base0 + u * kWave + lane;
+        if (vec >= nvec) continue;
+        const int64_t e0 = vec * kVec;
+        const int cnt = static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec);
+        const bool full = cnt == kVec;
+        float acc[kVec];
+        if constexpr (ACC) load8(p.out + e0, full, cnt, acc);
+        float g[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+        for (int r0 = 0; r0 < p.fan_in; r0 += 4) {
+            uint4 q4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (r0 + q < p.fan_in) {
+                    const uint16_t* src = p.contrib[r0 + q] + e0;
+                    q4[q] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (r0 + q < p.fan_in) accumulate(g, q4[q]);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (r0 + q < p.fan_in) accumulate(g, raw[q]);
+        for (int e = 0; e < kVec; ++e) {
+            g[e] = g[e] * p.scale;
+            if constexpr (ACC) g[e] = acc[e] + g[e];
+        }
+        store8(p.out + e0, full, cnt, g);
     }
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-        g[e] = g[e] * p.scale;
-        if constexpr (ACC) g[e] = acc[e] + g[e];
-    }
-    store8(p.out + e0, full, cnt, g);
 }
 
 __global__ __launch_bounds__(kBlock) void unflatten_kernel(UnflattenParams p) {
@@ -970,12 +1034,29 @@ int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, fl
     p.n = n;
     p.fan_in = fan_in;
     p.scale = scale;
+    const void* k = nullptr;
+    int groups = 1;
+    switch (fan_in) {
+#define FSDPSHARD_REDUCE_CASE(FI)                                                               \
+    case FI:                                                                                    \
+        k = accumulate ? reinterpret_cast<const void*>(&reduce_kernel<FI, true>)               \
+                       : reinterpret_cast<const void*>(&reduce_kernel<FI, false>);             \
+        groups = reduce_groups<FI>();                                                           \
+        break;
+        FSDPSHARD_REDUCE_CASE(1)
+        FSDPSHARD_REDUCE_CASE(2)
+        FSDPSHARD_REDUCE_CASE(4)
+        FSDPSHARD_REDUCE_CASE(8)
+#undef FSDPSHARD_REDUCE_CASE
+        default:
+            k = accumulate ? reinterpret_cast<const void*>(&reduce_kernel<0, true>)
+                           : reinterpret_cast<const void*>(&reduce_kernel<0, false>);
+            groups = reduce_groups<0>();
+    }
     unsigned blocks = 0;
-    rc = tile_grid(n, 1, &blocks);
+    rc = tile_grid(n, groups, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(accumulate ? reinterpret_cast<const void*>(&reduce_kernel<true>)
-                             : reinterpret_cast<const void*>(&reduce_kernel<false>),
-                  blocks, &p, stream);
+    return launch(k, blocks, &p, stream);
 }
 
 // Sum-of-squares grid: each wave walks kSumsqGroups groups; one float64 partial per work-group.
