@@ -26,6 +26,8 @@ What it computes, and where each piece comes from (page titles as published):
                  page, gradient-clipping passage).
 * step also holds the fp32 gradient-shard accumulation across micro-batches and the step that
   consumes such an fp32 shard (mixed-precision passage).
+* reshard     -- shards of one world size (and padding multiple) turned into another's (same page,
+                 checkpointing passage: local state dicts are tied to one configuration).
 
 Precision: the pages fix the precision of every stored quantity on this path (fp32 master, m, v
 and reduction; bf16 params and gradients), so the oracle computes in float32 with one IEEE
@@ -33,4 +35,4 @@ rounding per operation and no fused multiply-add, in a fixed operation order.  A
 the same recurrence (``step.adamw_update_f64``) exists only as a diagnostic.
 """
 
-from . import accounting, bf16, clip, layout, step  # noqa: F401
+from . import accounting, bf16, clip, layout, reshard, step  # noqa: F401
