@@ -45,6 +45,15 @@ class _AdamW(ctypes.Structure):
                 ("max_grad_norm", ctypes.c_double), ("grad_sumsq", c_vp)]
 
 
+class _Piece(ctypes.Structure):
+    _fields_ = [("src_offset", c_i64), ("dst_offset", c_i64), ("length", c_i64),
+                ("src_rank", c_i32), ("reserved", c_i32)]
+
+
+PIECE_DTYPE = np.dtype([("src_offset", "<i8"), ("dst_offset", "<i8"), ("length", "<i8"),
+                        ("src_rank", "<i4"), ("reserved", "<i4")])
+assert PIECE_DTYPE.itemsize == ctypes.sizeof(_Piece) == 32
+
 # numpy view of fsdpshard_segment (32 bytes)
 SEGMENT_DTYPE = np.dtype([("shard_begin", "<i8"), ("length", "<i8"), ("tensor_offset", "<i8"),
                           ("tensor_id", "<i4"), ("flags", "<u4")])
@@ -85,6 +94,10 @@ def lib():
     h.grad_sumsq_workspace_bytes.restype = c_i64
     h.grad_sumsq_shard.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_i64, c_vp, c_i32,
                                    ctypes.c_float, c_vp, c_i64, c_vp, c_vp]
+    h.reshard_plan.argtypes = [ctypes.POINTER(c_i64), c_i32, c_i64, c_i32, c_i64, c_i32, c_i32,
+                               ctypes.POINTER(_Piece), c_i32, ctypes.POINTER(c_i32)]
+    h.reshard_copy.argtypes = [ctypes.POINTER(c_vp), ctypes.POINTER(c_i64), c_i32, c_vp, c_i64,
+                               ctypes.POINTER(_Piece), c_i32, c_i32, c_vp]
     h.fsdpshard_strerror.argtypes = [ctypes.c_int]
     h.fsdpshard_strerror.restype = ctypes.c_char_p
     h.fsdpshard_abi_version.argtypes = []
@@ -94,6 +107,7 @@ def lib():
                                        c_vp]
     for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
                  "adamw_shard_step_f32grad", "reduce_shard_accumulate", "grad_sumsq_shard",
+                 "reshard_plan", "reshard_copy",
                  "fsdpshard_abi_version", "fsdpshard_set_groups_per_wave", "fsdpshard_stream_copy",
                  "fsdpshard_stream_mix"):
         getattr(h, name).restype = ctypes.c_int
@@ -334,3 +348,43 @@ def stream_mix(contribs, s0, s1, s2, out, n=None, stream=None):
     _check("fsdpshard_stream_mix", lib().fsdpshard_stream_mix(
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(s0, "s0"), _ptr(s1, "s1"),
         _ptr(s2, "s2"), _ptr(out, "out"), n, _stream(stream, s0)))
+
+
+# ------------------------------------------------------------------------------ reshard
+
+def reshard_plan(numels, src_pad, src_world, dst_pad, dst_world, dst_rank):
+    """Pieces (numpy array of PIECE_DTYPE) that build destination rank ``dst_rank``'s shard of the
+    (dst_pad, dst_world) layout from the shards of the (src_pad, src_world) layout."""
+    sizes = np.ascontiguousarray(np.asarray(numels, dtype=np.int64).reshape(-1))
+    T = int(sizes.size)
+    sp = sizes.ctypes.data_as(ctypes.POINTER(c_i64)) if T else None
+    count = c_i32(0)
+    h = lib()
+    _check("reshard_plan", h.reshard_plan(sp, T, int(src_pad), int(src_world), int(dst_pad),
+                                          int(dst_world), int(dst_rank), None, 0,
+                                          ctypes.byref(count)))
+    pieces = np.zeros(count.value, dtype=PIECE_DTYPE)
+    if count.value:
+        _check("reshard_plan", h.reshard_plan(
+            sp, T, int(src_pad), int(src_world), int(dst_pad), int(dst_world), int(dst_rank),
+            pieces.ctypes.data_as(ctypes.POINTER(_Piece)), count.value, ctypes.byref(count)))
+    return pieces
+
+
+def reshard_copy(src_shards, dst, pieces, stream=None):
+    """Execute a reshard plan: ``src_shards`` are the source ranks' device tensors (None for a rank
+    no piece reads), ``dst`` the destination shard; all of one dtype (2, 4 or 8 bytes)."""
+    like = next(t for t in list(src_shards) + [dst] if t is not None)
+    elem = like.element_size()
+    n_src = len(src_shards)
+    ptrs = (c_vp * n_src)(*[None if t is None else _ptr(t, f"source shard {i}")
+                            for i, t in enumerate(src_shards)])
+    elems = (c_i64 * n_src)(*[0 if t is None else t.numel() for t in src_shards])
+    for t in src_shards:
+        if t is not None and t.element_size() != elem:
+            raise ValueError("all shards must share one element size")
+    pieces = np.ascontiguousarray(pieces, dtype=PIECE_DTYPE)
+    _check("reshard_copy", lib().reshard_copy(
+        ptrs, elems, n_src, _ptr(dst, "dst"), dst.numel(),
+        pieces.ctypes.data_as(ctypes.POINTER(_Piece)) if pieces.size else None, int(pieces.size),
+        elem, _stream(stream, dst)))

@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfsdpshard.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "shard_step.hip"), os.path.join(CSRC, "layout.cpp")]
+HIP_SOURCES = [os.path.join(CSRC, "shard_step.hip"), os.path.join(CSRC, "reshard.hip")]
+HOST_SOURCES = [os.path.join(CSRC, "layout.cpp")]
 
 
 def clang():
@@ -38,17 +39,21 @@ HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+def _obj(objdir, src):
+    return os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
+
+
 def commands(out=LIB, objdir=None):
     objdir = objdir or os.path.join(PKG, "_build")
-    hip_obj = os.path.join(objdir, "shard_step.o")
-    host_obj = os.path.join(objdir, "layout.o")
     cc = clang()
-    return objdir, [
-        [cc, *COMMON, *HIP_FLAGS, f"-I{INCLUDE}", "-c", SOURCES[0], "-o", hip_obj],
-        [cc, *COMMON, f"-I{INCLUDE}", "-c", SOURCES[1], "-o", host_obj],
-        [cc, "--hip-link", f"--offload-arch={ARCH}", "-shared", "-fPIC", hip_obj, host_obj,
-         "-o", out],
-    ]
+    cmds = [[cc, *COMMON, *HIP_FLAGS, f"-I{INCLUDE}", "-c", src, "-o", _obj(objdir, src)]
+            for src in HIP_SOURCES]
+    cmds += [[cc, *COMMON, f"-I{INCLUDE}", "-c", src, "-o", _obj(objdir, src)]
+             for src in HOST_SOURCES]
+    objs = [_obj(objdir, src) for src in HIP_SOURCES + HOST_SOURCES]
+    cmds.append([cc, "--hip-link", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+                 "-o", out])
+    return objdir, cmds
 
 
 def build(verbose=False):

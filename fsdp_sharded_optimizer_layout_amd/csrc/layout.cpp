@@ -113,6 +113,124 @@ extern "C" int shard_layout(const int64_t* numels, int32_t n_tensors, int64_t pa
     return over ? FSDPSHARD_ERR_CAPACITY : FSDPSHARD_OK;
 }
 
+namespace {
+
+// Flat offsets of the tensors under one padding multiple; offs[T] = P.  Returns a status.
+int flat_offsets(const int64_t* numels, int32_t n_tensors, int64_t pad, std::vector<int64_t>* offs) {
+    offs->assign(static_cast<size_t>(n_tensors) + 1, 0);
+    int64_t pos = 0;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        if (numels[i] < 0) return FSDPSHARD_ERR_INVALID_ARG;
+        const int64_t ps = padded_size(numels[i], pad);
+        if (ps < 0 || ps > kI64Max - pos) return FSDPSHARD_ERR_OVERFLOW;
+        (*offs)[i] = pos;
+        pos += ps;
+    }
+    (*offs)[n_tensors] = pos;
+    return FSDPSHARD_OK;
+}
+
+// Rank that owns flat position u (0 <= u < P) under the floor rule: the k with
+// floor(kP/N) <= u < floor((k+1)P/N), i.e. k = ceil((u+1)N/P) - 1 = floor(((u+1)N - 1)/P).
+int32_t owner_of(int64_t u, int64_t P, int32_t N) {
+    const __int128 a = (static_cast<__int128>(u) + 1) * N - 1;
+    return static_cast<int32_t>(a / P);
+}
+
+struct PieceSink {
+    fsdpshard_piece* out;
+    int32_t capacity;
+    int32_t count;
+    bool over;
+    bool have;
+    fsdpshard_piece cur;
+
+    void flush() {
+        if (!have) return;
+        if (out != nullptr) {
+            if (count < capacity) out[count] = cur;
+            else over = true;
+        }
+        ++count;
+        have = false;
+    }
+    // Append a piece, merging it into the previous one when both are contiguous.
+    void add(int32_t src_rank, int64_t src_off, int64_t dst_off, int64_t len) {
+        if (len <= 0) return;
+        if (have && cur.src_rank == src_rank && cur.dst_offset + cur.length == dst_off &&
+            (src_rank < 0 || cur.src_offset + cur.length == src_off)) {
+            cur.length += len;
+            return;
+        }
+        flush();
+        cur.src_offset = src_rank < 0 ? 0 : src_off;
+        cur.dst_offset = dst_off;
+        cur.length = len;
+        cur.src_rank = src_rank;
+        cur.reserved = 0;
+        have = true;
+    }
+};
+
+}  // namespace
+
+extern "C" int reshard_plan(const int64_t* numels, int32_t n_tensors, int64_t src_pad,
+                            int32_t src_world, int64_t dst_pad, int32_t dst_world, int32_t dst_rank,
+                            fsdpshard_piece* pieces, int32_t capacity, int32_t* n_pieces) {
+    if (n_pieces == nullptr || n_tensors < 0 || (n_tensors > 0 && numels == nullptr) ||
+        src_pad < 1 || dst_pad < 1 || src_world < 1 || dst_world < 1 || dst_rank < 0 ||
+        dst_rank >= dst_world || capacity < 0)
+        return FSDPSHARD_ERR_INVALID_ARG;
+    std::vector<int64_t> oa, ob;
+    int rc = flat_offsets(numels, n_tensors, src_pad, &oa);
+    if (rc != FSDPSHARD_OK) return rc;
+    rc = flat_offsets(numels, n_tensors, dst_pad, &ob);
+    if (rc != FSDPSHARD_OK) return rc;
+    const int64_t Pa = oa[n_tensors], Pb = ob[n_tensors];
+    const int64_t lo = floor_kp_over_n(dst_rank, Pb, dst_world);
+    const int64_t hi = floor_kp_over_n(static_cast<int64_t>(dst_rank) + 1, Pb, dst_world);
+
+    PieceSink sink{pieces, capacity, 0, false, false, {}};
+    // First tensor whose destination extent reaches past lo.
+    int32_t first = 0;
+    {
+        int32_t a = 0, b = n_tensors;
+        while (b - a > 1) {
+            const int32_t mid = a + (b - a) / 2;
+            if (ob[mid] <= lo) a = mid; else b = mid;
+        }
+        first = a;
+        while (first < n_tensors && ob[first + 1] <= lo) ++first;
+    }
+    for (int32_t i = first; i < n_tensors && ob[i] < hi; ++i) {
+        // Real elements of tensor i inside the destination shard: flat [x, y) of the new layout.
+        const int64_t x = ob[i] > lo ? ob[i] : lo;
+        const int64_t real_end = ob[i] + numels[i];
+        const int64_t y = real_end < hi ? real_end : hi;
+        if (x < y) {
+            // The same tensor positions in the source layout, cut by the source ranks' slices.
+            int64_t u = oa[i] + (x - ob[i]);
+            const int64_t w = oa[i] + (y - ob[i]);
+            int32_t r = owner_of(u, Pa, src_world);
+            while (u < w) {
+                const int64_t rlo = floor_kp_over_n(r, Pa, src_world);
+                const int64_t rhi = floor_kp_over_n(static_cast<int64_t>(r) + 1, Pa, src_world);
+                const int64_t e = w < rhi ? w : rhi;
+                if (u < e) sink.add(r, u - rlo, (u - oa[i]) + ob[i] - lo, e - u);
+                u = e > u ? e : u;
+                ++r;
+            }
+        }
+        // Destination padding of tensor i: zero.
+        const int64_t px = real_end > lo ? real_end : lo;
+        const int64_t py = ob[i + 1] < hi ? ob[i + 1] : hi;
+        if (px < py) sink.add(-1, 0, px - lo, py - px);
+    }
+    sink.flush();
+    *n_pieces = sink.count;
+    return sink.over ? FSDPSHARD_ERR_CAPACITY : FSDPSHARD_OK;
+}
+
 extern "C" const char* fsdpshard_strerror(int code) {
     switch (code) {
         case FSDPSHARD_OK: return "ok";

@@ -1,0 +1,183 @@
+// Reshard execution of libfsdpshard.so on gfx950: copy the pieces of a reshard plan.
+//
+// "FSDP: Fully Sharded Data Parallel Training at Scale", checkpointing passage: local state
+// dicts (each rank's own shard) load only under the same rank count; a reshard plan (host code,
+// reshard_plan) maps another rank count's shards onto one destination shard as a list of pieces,
+// each a contiguous run of elements from one source shard, or zeros for destination padding.
+//
+// The copy is a bandwidth-bound stream.  One launch carries up to kMaxPieces pieces in its
+// kernel arguments; every piece is cut into 4 KiB chunks of its destination, one work-group per
+// chunk, and a work-group finds its piece by binary search over the pieces' first chunks.  Each
+// lane stores one 16-byte destination-aligned vector; its source bytes are read with the widest
+// loads their relative alignment allows (16, 4 or 2 bytes).  The at most 14 bytes before the
+// first aligned destination vector and after the last one are copied 2 bytes at a time (every
+// element is at least 2 bytes wide).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <utility>
+#include <vector>
+
+#include "fsdpshard.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int64_t kChunk = 16 * kBlock;   // destination bytes per work-group
+constexpr int kMaxPieces = 96;            // keeps the kernel arguments under 4 KiB
+
+struct CopyPiece {
+    const unsigned char* src;   // null: write zeros
+    unsigned char* dst;
+    int64_t bytes;
+};
+
+struct ReshardParams {
+    CopyPiece piece[kMaxPieces];
+    int64_t first_block[kMaxPieces + 1];   // work-group index where each piece starts
+    int32_t n;
+};
+
+__device__ __forceinline__ uint4 load16(const unsigned char* s, unsigned phase) {
+    if (phase == 0) return *reinterpret_cast<const uint4*>(s);
+    uint32_t w[4];
+    if ((phase & 3u) == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = reinterpret_cast<const uint32_t*>(s)[k];
+    } else {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(s);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w[k] = static_cast<uint32_t>(h[2 * k]) | (static_cast<uint32_t>(h[2 * k + 1]) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(kBlock) void reshard_kernel(ReshardParams p) {
+    const int64_t b = blockIdx.x;
+    int a = 0, z = p.n;   // largest piece index with first_block <= b
+    while (z - a > 1) {
+        const int mid = (a + z) >> 1;
+        if (p.first_block[mid] <= b) a = mid; else z = mid;
+    }
+    const CopyPiece pc = p.piece[a];
+    const int64_t chunk = b - p.first_block[a];
+    const int64_t head_raw = static_cast<int64_t>((16u - (reinterpret_cast<uintptr_t>(pc.dst) & 15u)) & 15u);
+    const int64_t head = head_raw < pc.bytes ? head_raw : pc.bytes;
+    const int64_t body = (pc.bytes - head) & ~static_cast<int64_t>(15);
+    const int64_t tail = pc.bytes - head - body;
+
+    const int64_t off = head + chunk * kChunk + static_cast<int64_t>(threadIdx.x) * 16;
+    if (off + 16 <= head + body) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (pc.src != nullptr) {
+            const unsigned phase = static_cast<unsigned>(reinterpret_cast<uintptr_t>(pc.src + off) & 15u);
+            v = load16(pc.src + off, phase);
+        }
+        *reinterpret_cast<uint4*>(pc.dst + off) = v;
+    }
+    if (chunk == 0) {
+        const int64_t t2 = static_cast<int64_t>(threadIdx.x) * 2;
+        if (t2 < head) {
+            const uint16_t x = pc.src ? *reinterpret_cast<const uint16_t*>(pc.src + t2) : 0;
+            *reinterpret_cast<uint16_t*>(pc.dst + t2) = x;
+        }
+        if (t2 < tail) {
+            const int64_t o = head + body + t2;
+            const uint16_t x = pc.src ? *reinterpret_cast<const uint16_t*>(pc.src + o) : 0;
+            *reinterpret_cast<uint16_t*>(pc.dst + o) = x;
+        }
+    }
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + static_cast<uintptr_t>(bbytes) && y < x + static_cast<uintptr_t>(abytes);
+}
+
+}  // namespace
+
+extern "C" int reshard_copy(const void* const* src_shards, const int64_t* src_elems,
+                            int32_t src_world, void* dst, int64_t dst_elems,
+                            const fsdpshard_piece* pieces, int32_t n_pieces, int32_t elem_bytes,
+                            void* stream) {
+    if (src_shards == nullptr || src_elems == nullptr || src_world < 1 ||
+        (dst == nullptr && dst_elems != 0) || dst_elems < 0 || n_pieces < 0 ||
+        (n_pieces > 0 && pieces == nullptr))
+        return FSDPSHARD_ERR_INVALID_ARG;
+    if (elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return FSDPSHARD_ERR_INVALID_ARG;
+    if (dst_elems > INT64_MAX / 8) return FSDPSHARD_ERR_OVERFLOW;
+    const uintptr_t amask = static_cast<uintptr_t>(elem_bytes - 1);
+    if ((reinterpret_cast<uintptr_t>(dst) & amask) != 0) return FSDPSHARD_ERR_ALIGNMENT;
+    for (int32_t r = 0; r < src_world; ++r) {
+        if (src_elems[r] < 0 || src_elems[r] > INT64_MAX / 8) return FSDPSHARD_ERR_INVALID_ARG;
+        if (src_shards[r] == nullptr) continue;
+        if ((reinterpret_cast<uintptr_t>(src_shards[r]) & amask) != 0) return FSDPSHARD_ERR_ALIGNMENT;
+        if (src_elems[r] > 0 && dst_elems > 0 &&
+            overlaps(src_shards[r], src_elems[r] * elem_bytes, dst, dst_elems * elem_bytes))
+            return FSDPSHARD_ERR_INVALID_ARG;
+    }
+    // Every piece inside its shards; destination pieces pairwise disjoint.
+    int64_t prev_end = -1;
+    bool sorted = true;
+    for (int32_t i = 0; i < n_pieces; ++i) {
+        const fsdpshard_piece& q = pieces[i];
+        if (q.length < 0 || q.dst_offset < 0 || q.dst_offset > dst_elems - q.length)
+            return FSDPSHARD_ERR_INVALID_ARG;
+        if (q.src_rank >= 0) {
+            if (q.src_rank >= src_world || src_shards[q.src_rank] == nullptr || q.src_offset < 0 ||
+                q.src_offset > src_elems[q.src_rank] - q.length)
+                return FSDPSHARD_ERR_INVALID_ARG;
+        } else if (q.src_rank != -1) {
+            return FSDPSHARD_ERR_INVALID_ARG;
+        }
+        if (q.dst_offset < prev_end) sorted = false;
+        prev_end = q.dst_offset + q.length;
+    }
+    if (!sorted) {
+        std::vector<std::pair<int64_t, int64_t>> spans;
+        spans.reserve(static_cast<size_t>(n_pieces));
+        for (int32_t i = 0; i < n_pieces; ++i)
+            if (pieces[i].length > 0) spans.emplace_back(pieces[i].dst_offset, pieces[i].length);
+        std::sort(spans.begin(), spans.end());
+        for (size_t i = 1; i < spans.size(); ++i)
+            if (spans[i - 1].first + spans[i - 1].second > spans[i].first)
+                return FSDPSHARD_ERR_INVALID_ARG;
+    }
+    unsigned char* d = static_cast<unsigned char*>(dst);
+    int32_t i = 0;   // next piece to place; empty pieces are skipped
+    while (i < n_pieces) {
+        ReshardParams p;
+        int32_t cnt = 0;
+        int64_t blocks = 0;
+        for (; i < n_pieces && cnt < kMaxPieces; ++i) {
+            const fsdpshard_piece& q = pieces[i];
+            if (q.length == 0) continue;
+            CopyPiece& c = p.piece[cnt];
+            c.src = q.src_rank < 0 ? nullptr
+                                   : static_cast<const unsigned char*>(src_shards[q.src_rank]) +
+                                         q.src_offset * elem_bytes;
+            c.dst = d + q.dst_offset * elem_bytes;
+            c.bytes = q.length * elem_bytes;
+            const int64_t head = static_cast<int64_t>((16u - (reinterpret_cast<uintptr_t>(c.dst) & 15u)) & 15u);
+            const int64_t body = c.bytes > head ? c.bytes - head : 0;
+            const int64_t nb = (body + kChunk - 1) / kChunk;
+            p.first_block[cnt] = blocks;
+            blocks += nb > 0 ? nb : 1;
+            ++cnt;
+        }
+        if (cnt == 0) continue;
+        p.first_block[cnt] = blocks;
+        p.n = cnt;
+        if (blocks > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
+        void* args[] = {&p};
+        const hipError_t e =
+            hipLaunchKernel(reinterpret_cast<const void*>(&reshard_kernel),
+                            dim3(static_cast<unsigned>(blocks)), dim3(kBlock), args, 0,
+                            static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return FSDPSHARD_ERR_HIP;
+    }
+    return FSDPSHARD_OK;
+}

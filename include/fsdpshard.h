@@ -235,6 +235,54 @@ int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs
                    int32_t n_segments, uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
                    void* stream);
 
+/*
+ * One piece of a reshard plan: `length` elements that land at `dst_offset` of the destination
+ * shard, read from `src_offset` of source rank `src_rank`'s shard, or zeros when src_rank is -1
+ * (destination padding).  32 bytes.
+ */
+typedef struct fsdpshard_piece {
+    int64_t src_offset;
+    int64_t dst_offset;
+    int64_t length;
+    int32_t src_rank;
+    int32_t reserved;   /* 0 */
+} fsdpshard_piece;
+
+/*
+ * reshard_plan -- how destination rank `dst_rank` of a new layout gathers its shard from the
+ * shards of an old one.                                                       (host only, no GPU)
+ *
+ * [FSDP], checkpointing passage: a local state dict holds each rank's own shard and loads only
+ * with the same number of GPUs and wrapping; resharding turns one world size's shards into
+ * another's.  Both layouts flatten the same tensors (numels, in order) under the floor rule of
+ * shard_layout, each with its own padding multiple and world size.  Every tensor keeps its
+ * values; destination padding is zero.  Pieces come in destination order, tile the destination
+ * shard exactly, and contiguous neighbours are merged.
+ *   pieces    host, room for `capacity` pieces, or NULL to count only
+ *   n_pieces  host, receives the number of pieces (always)
+ * Errors: INVALID_ARG, OVERFLOW, CAPACITY (pieces written up to capacity; call again).
+ */
+int reshard_plan(const int64_t* numels, int32_t n_tensors, int64_t src_pad, int32_t src_world,
+                 int64_t dst_pad, int32_t dst_world, int32_t dst_rank, fsdpshard_piece* pieces,
+                 int32_t capacity, int32_t* n_pieces);
+
+/*
+ * reshard_copy -- execute a reshard plan on the GPU: for every piece, copy `length` elements of
+ * `elem_bytes` bytes from src_shards[src_rank] + src_offset to dst + dst_offset, or write zeros.
+ *   src_shards  host array of src_world device pointers (a NULL entry is allowed for a rank no
+ *               piece reads); src_elems: host array, the element count of each source shard
+ *   dst         device pointer to the destination shard of dst_elems elements (may be NULL
+ *               when dst_elems == 0: an empty shard, as P < N produces)
+ *   pieces      host array of n_pieces pieces (as reshard_plan emits them)
+ *   elem_bytes  2, 4 or 8; every pointer aligned to elem_bytes
+ * Every piece is checked against the shard sizes before anything is enqueued.  Pieces may not
+ * overlap in the destination, and no source shard may overlap the destination.
+ * Errors: INVALID_ARG (out-of-range piece, bad rank, overlap), ALIGNMENT, HIP.
+ */
+int reshard_copy(const void* const* src_shards, const int64_t* src_elems, int32_t src_world,
+                 void* dst, int64_t dst_elems, const fsdpshard_piece* pieces, int32_t n_pieces,
+                 int32_t elem_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fsdpshard_strerror(int code);
 

@@ -274,3 +274,92 @@ def test_sumsq_validation_and_workspace():
     assert f(None, 0, g + 8, 100, None, 0, 1.0, ws, 8, res, None) == ALIGN
     assert f(arr, 2, None, -1, None, 0, 1.0, ws, 8, res, None) == INVALID
     assert f(arr, 2, None, 100, None, 0, 1.0, ws, 8, ws, None) == INVALID          # overlap
+
+
+# ---------------------------------------------------------------------------------- reshard plan
+
+def _execute_plan(pieces, src_shards, dst_len, dtype):
+    """Test-side executor of a plan on the host (numpy), to compare with the oracle."""
+    out = np.full(dst_len, 99, dtype=dtype)
+    for q in pieces:
+        a, n_ = int(q["dst_offset"]), int(q["length"])
+        if int(q["src_rank"]) < 0:
+            out[a:a + n_] = 0
+        else:
+            s = int(q["src_offset"])
+            out[a:a + n_] = src_shards[int(q["src_rank"])][s:s + n_]
+    return out
+
+
+def test_reshard_plan_matches_oracle():
+    from oracle import reshard as OR
+    rng = random.Random(9)
+    for trial in range(300):
+        T = rng.randint(0, 8)
+        sizes = [rng.choice([0, 1, 2, 5, 16, 17, 33, 100]) for _ in range(T)]
+        pa, pb = rng.choice([1, 2, 8, 16]), rng.choice([1, 2, 8, 16])
+        na, nb = rng.randint(1, 9), rng.randint(1, 9)
+        offs, Pa = OL.flatten_offsets(sizes, pa)
+        flat = np.zeros(Pa, dtype=np.float32)
+        for o, s in zip(offs, sizes):
+            flat[o:o + s] = np.arange(s) + 1000 * o + 0.25
+        src = OR.shard(flat, sizes, pa, na)
+        want = OR.reshard(src, sizes, pa, pb, nb)
+        for k in range(nb):
+            pieces = F.reshard_plan(sizes, pa, na, pb, nb, k)
+            got = _execute_plan(pieces, src, want[k].size, np.float32)
+            assert np.array_equal(got, want[k])
+            # pieces tile the shard in order and no two neighbours could have been merged
+            pos = 0
+            for a, b in zip(pieces, pieces[1:]):
+                assert not (a["src_rank"] == b["src_rank"] and
+                            (a["src_rank"] < 0 or a["src_offset"] + a["length"] == b["src_offset"]))
+            for q in pieces:
+                assert q["dst_offset"] == pos and q["length"] > 0
+                pos += int(q["length"])
+            assert pos == want[k].size
+
+
+def test_reshard_plan_same_layout_is_one_piece_per_source_overlap():
+    sizes = [1000, 7, 2000]
+    for k in range(4):
+        pieces = F.reshard_plan(sizes, 1, 4, 1, 4, k)
+        assert len(pieces) == 1 and pieces[0]["src_rank"] == k and pieces[0]["src_offset"] == 0
+
+
+def test_reshard_plan_errors_and_capacity():
+    lib = F.lib()
+    sizes = (ctypes.c_int64 * 3)(5, 6, 7)
+    n = ctypes.c_int32(0)
+    assert lib.reshard_plan(sizes, 3, 4, 2, 1, 3, 0, None, 0, ctypes.byref(n)) == OK and n.value > 1
+    buf = (F._Piece * 1)()
+    assert lib.reshard_plan(sizes, 3, 4, 2, 1, 3, 0, buf, 1, ctypes.byref(n)) == CAPACITY
+    assert lib.reshard_plan(sizes, 3, 0, 2, 1, 3, 0, None, 0, ctypes.byref(n)) == INVALID
+    assert lib.reshard_plan(sizes, 3, 4, 2, 1, 3, 3, None, 0, ctypes.byref(n)) == INVALID
+    assert lib.reshard_plan(sizes, 3, 4, 0, 1, 3, 0, None, 0, ctypes.byref(n)) == INVALID
+    assert lib.reshard_plan(sizes, 3, 4, 2, 1, 3, 0, None, 0, None) == INVALID
+
+
+def test_reshard_copy_validation():
+    lib = F.lib()
+    src = (ctypes.c_void_p * 2)(_Fake.at(1), _Fake.at(2))
+    elems = (ctypes.c_int64 * 2)(100, 100)
+    P = F._Piece
+    good = (P * 2)(P(0, 0, 50, 0, 0), P(0, 50, 50, 1, 0))
+    d = _Fake.at(3)
+    assert lib.reshard_copy(src, elems, 2, d, 100, good, 0, 4, None) == OK
+    bad_rank = (P * 1)(P(0, 0, 10, 2, 0))
+    assert lib.reshard_copy(src, elems, 2, d, 100, bad_rank, 1, 4, None) == INVALID
+    oob = (P * 1)(P(95, 0, 10, 0, 0))
+    assert lib.reshard_copy(src, elems, 2, d, 100, oob, 1, 4, None) == INVALID
+    oob_dst = (P * 1)(P(0, 95, 10, 0, 0))
+    assert lib.reshard_copy(src, elems, 2, d, 100, oob_dst, 1, 4, None) == INVALID
+    overlap = (P * 2)(P(0, 10, 20, 0, 0), P(0, 0, 15, 1, 0))
+    assert lib.reshard_copy(src, elems, 2, d, 100, overlap, 2, 4, None) == INVALID
+    assert lib.reshard_copy(src, elems, 2, d + 2, 100, good, 0, 4, None) == ALIGN
+    assert lib.reshard_copy(src, elems, 2, d, 100, good, 0, 3, None) == INVALID
+    assert lib.reshard_copy(src, elems, 2, _Fake.at(1, 16), 100, good, 0, 4, None) == INVALID
+    # an empty destination shard may be NULL; a non-empty one may not
+    assert lib.reshard_copy(src, elems, 2, None, 0, good, 0, 4, None) == OK
+    assert lib.reshard_copy(src, elems, 2, None, 100, good, 0, 4, None) == INVALID
+    assert lib.reshard_copy(src, elems, 2, None, 0, good, 1, 4, None) == INVALID
