@@ -145,6 +145,125 @@ def cpu_baseline(workload, seconds=12.0, sample=1 << 21):
                       f"{steps} oracle steps in {el:.1f} s (NumPy float32, one thread)"}
 
 
+def cpu_baseline_reshard(workload, dst_pad, dst_world, seconds=12.0):
+    """The oracle's reshard as it is (NumPy, one thread) on one decoder layer of the workload's
+    tensors: all destination shards of that layer from the source shards, repeated for about
+    `seconds`.  Rate in destination elements per second."""
+    import numpy as np
+    import workloads as W
+    from oracle import layout as OL
+    from oracle import reshard as OR
+
+    w = W.WORKLOADS[workload]
+    sizes = w.sizes[1:10] if len(w.sizes) > 10 else w.sizes
+    offs, P = OL.flatten_offsets(sizes, w.pad_multiple)
+    flat = np.zeros(P, dtype=np.float32)
+    rng = np.random.default_rng(0)
+    for o, n in zip(offs, sizes):
+        flat[o:o + n] = rng.standard_normal(n, dtype=np.float32)
+    src = OR.shard(flat, sizes, w.pad_multiple, w.world_size)
+    del flat
+    reps, produced = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        out = OR.reshard(src, sizes, w.pad_multiple, dst_pad, dst_world)
+        produced += sum(o.size for o in out)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": produced / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sizes)} tensors ({P} flat elements, fp32) of {workload}, "
+                      f"{w.world_size} -> {dst_world} ranks, padding {w.pad_multiple} -> "
+                      f"{dst_pad}, all destination shards, {reps} repetitions in {el:.1f} s"}
+
+
+def bench_reshard(args, w, F, W, torch):
+    """Reshard path: one destination rank's fp32 optimizer state (master, m, v) built from the
+    source ranks' shards.  A step is the host plan plus three reshard_copy launches; the source
+    shards it reads are resident in HBM (only the ranks the plan touches are allocated)."""
+    dst_pad = args.reshard_pad or w.pad_multiple
+    dst_world, dst_rank = args.reshard_world, args.reshard_rank
+    pieces = F.reshard_plan(w.sizes, w.pad_multiple, w.world_size, dst_pad, dst_world, dst_rank)
+    Ld, _ = F.shard_layout(w.sizes, dst_world, dst_rank, dst_pad)
+    n_dst = Ld.n
+    src_elems = [F.shard_layout(w.sizes, w.world_size, r, w.pad_multiple)[0].n
+                 for r in range(w.world_size)]
+    used = sorted({int(r) for r in pieces["src_rank"] if r >= 0})
+    real = int(pieces["length"][pieces["src_rank"] >= 0].sum())
+    log(f"reshard {w.name}: {w.world_size} ranks pad {w.pad_multiple} -> {dst_world} ranks pad "
+        f"{dst_pad}, rank {dst_rank}: {n_dst} elements, {len(pieces)} pieces, source ranks {used}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    states = []
+    for j in range(3):
+        g = torch.Generator(device=dev)
+        g.manual_seed(100 + j)
+        src = [torch.randn(src_elems[r], dtype=torch.float32, device=dev, generator=g)
+               if r in used else None for r in range(w.world_size)]
+        dst = torch.empty(n_dst, dtype=torch.float32, device=dev)
+        states.append((src, dst))
+    torch.cuda.synchronize()
+    bytes_per_launch = 4 * (real + n_dst)   # real elements read and all destination elements written
+
+    def one_step(ev=None):
+        p = F.reshard_plan(w.sizes, w.pad_multiple, w.world_size, dst_pad, dst_world, dst_rank)
+        for j, (src, dst) in enumerate(states):
+            if ev is not None:
+                ev[j][0].record(stream)
+            F.reshard_copy(src, dst, p, stream=stream)
+            if ev is not None:
+                ev[j][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in states] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(events[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    ms = [events[i][j][0].elapsed_time(events[i][j][1])
+          for i in range(args.steps) for j in range(len(states))]
+    avg = sum(ms) / len(ms)
+    achieved = bytes_per_launch / (avg / 1e3) / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; reshard_copy avg {avg:.3f} ms, "
+        f"{achieved:.1f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline_reshard(w.name, dst_pad, dst_world)
+        log(f"cpu oracle: {cpu['value']:.3e} elements/s")
+    rec = {
+        "metric": "optimizer-state elements resharded/sec per GPU; achieved HBM GB/s vs peak",
+        "value": round(3 * n_dst / (ms_per_step / 1e3), 1),
+        "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {
+            "workload": w.name, "path": "reshard",
+            "src": {"world_size": w.world_size, "pad_multiple": w.pad_multiple},
+            "dst": {"world_size": dst_world, "pad_multiple": dst_pad, "rank": dst_rank,
+                    "elems": n_dst},
+            "pieces": len(pieces), "source_ranks": used, "real_elems": real,
+            "states": "fp32 master, m, v (three reshard_copy launches per step)",
+            "kernel_avg_ms": round(avg, 4), "kernel_min_ms": round(min(ms), 4),
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,9 +272,18 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--groups-per-wave", type=int, default=0,
                     help="512-element groups per wavefront (1, 2, 4; 0 = library default)")
-    ap.add_argument("--path", choices=["fused", "clipped", "accumulate"], default="fused",
+    ap.add_argument("--path", choices=["fused", "clipped", "accumulate", "reshard"],
+                    default="fused",
                     help="fused: the fused step (default); clipped: sum of squares + clipped "
-                         "step; accumulate: fp32 micro-batch accumulation + clipped fp32 step")
+                         "step; accumulate: fp32 micro-batch accumulation + clipped fp32 step; "
+                         "reshard: move one destination rank's fp32 master/m/v to another "
+                         "world size and padding multiple")
+    ap.add_argument("--reshard-world", type=int, default=6,
+                    help="reshard path: destination world size")
+    ap.add_argument("--reshard-pad", type=int, default=0,
+                    help="reshard path: destination padding multiple (0 = the workload's)")
+    ap.add_argument("--reshard-rank", type=int, default=1,
+                    help="reshard path: destination rank")
     ap.add_argument("--micro-batches", type=int, default=4)
     ap.add_argument("--max-grad-norm", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,6 +312,9 @@ def main():
         F.set_groups_per_wave(args.groups_per_wave)
 
     w = W.WORKLOADS[args.workload]
+    if args.path == "reshard":
+        bench_reshard(args, w, F, W, torch)
+        return
     L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
     n, lo, Fi = L.n, L.lo, w.fan_in
     log(f"workload {w.name}: P={L.P} slice [{L.lo}, {L.hi}) n={n} n_real={L.n_real} "

@@ -92,3 +92,63 @@ def test_full_size_many_small_tensors():
         assert np.array_equal(h[4:4 + want[k].size], want[k])
         assert (h[:4] == 123).all() and (h[4 + want[k].size:] == 123).all()
         say(f"  rank {k}: {len(pieces)} pieces ok")
+
+
+def _codes(pos):
+    """32-bit code of a flat source position: a multiplicative hash, one-to-one on 32 bits, so a
+    misplaced element (by anything other than a multiple of 2**32 positions) shows."""
+    return (pos.astype(np.uint64) * np.uint64(2654435761)) & np.uint64(0xFFFFFFFF)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("dst_pad,dst_world,dst_rank", [(1, 6, 1), (16, 6, 5), (8, 12, 0)])
+def test_full_size_dense7b_sampled(dst_pad, dst_world, dst_rank):
+    # The 7B-shaped model's fp32 state from 8 ranks (padding 1) to another layout, as the bench
+    # times it.  Source shards hold the hashed source flat position of each element; sampled
+    # destination elements (every piece boundary and 1M random positions) are checked against
+    # the position the oracle's flat layout gives them.
+    w = W.WORKLOADS["dense7b_n8_rank0"]
+    sizes, pa, na = w.sizes, w.pad_multiple, w.world_size
+    offs_a, Pa = OL.flatten_offsets(sizes, pa)
+    offs_b, Pb = OL.flatten_offsets(sizes, dst_pad)
+    lo_b, hi_b = OL.shard_bounds(Pb, dst_world, dst_rank)
+    n_dst = hi_b - lo_b
+    pieces = F.reshard_plan(sizes, pa, na, dst_pad, dst_world, dst_rank)
+    used = sorted({int(r) for r in pieces["src_rank"] if r >= 0})
+    say(f"dense7b reshard {na}/{pa} -> {dst_world}/{dst_pad} rank {dst_rank}: n={n_dst} "
+        f"pieces={len(pieces)} sources={used}")
+    src = []
+    for r in range(na):
+        if r not in used:
+            src.append(None)
+            continue
+        lo, hi = OL.shard_bounds(Pa, na, r)
+        t = torch.empty(hi - lo, dtype=torch.int32, device="cuda")
+        step = 1 << 27
+        for a in range(lo, hi, step):
+            b = min(hi, a + step)
+            pos = torch.arange(a, b, dtype=torch.int64, device="cuda")
+            t[a - lo:b - lo] = ((pos * 2654435761) & 0xFFFFFFFF).to(torch.int32)
+        src.append(t)
+    dst = torch.full((n_dst + 8,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    F.reshard_copy(src, dst[4:4 + n_dst], pieces)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(dst_rank)
+    bounds = np.concatenate([pieces["dst_offset"], pieces["dst_offset"] + pieces["length"]])
+    near = (bounds[:, None] + np.arange(-3, 3)[None, :]).reshape(-1)
+    j = np.unique(np.concatenate([near, rng.integers(0, n_dst, 1 << 20), [0, n_dst - 1]]))
+    j = j[(j >= 0) & (j < n_dst)]
+    q = lo_b + j                                       # flat position in the destination layout
+    ob = np.asarray(offs_b + [Pb], dtype=np.int64)
+    oa = np.asarray(offs_a, dtype=np.int64)
+    ti = np.searchsorted(ob, q, side="right") - 1
+    off = q - ob[ti]
+    real = off < np.asarray(sizes, dtype=np.int64)[ti]
+    want = np.where(real, _codes(oa[ti] + off), 0).astype(np.uint32)
+    got = dst[4:4 + n_dst][torch.from_numpy(j).cuda()].cpu().numpy().view(np.uint32)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (j[bad[:5]], got[bad[:5]], want[bad[:5]])
+    guard = torch.cat([dst[:4], dst[4 + n_dst:]]).cpu().numpy()
+    assert (guard == 0x5A5A5A5A).all()
+    say(f"  {j.size} sampled elements ok ({int(real.sum())} real)")
