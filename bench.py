@@ -30,6 +30,9 @@ PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 DEFAULT_WORKLOAD = "dense7b_n8_rank0"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc", "shard_step.hip")
+RESHARD_SOURCE = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc", "reshard.hip")
+STEP_KERNEL = "void (anonymous namespace)::fused_step_kernel"
+RESHARD_KERNEL = "(anonymous namespace)::reshard_kernel"
 
 
 def log(msg):
@@ -47,12 +50,12 @@ def algorithmic_bytes_per_param_f32grad():
     return 4 + 3 * 4 * 2 + 2
 
 
-def source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
+def source_digest(source=KERNEL_SOURCE):
+    with open(source, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counter_traffic(workload):
+def counter_traffic(key, source=KERNEL_SOURCE):
     """Per-launch HBM bytes from the committed rocprofv3 counter summary, if it was taken on the
     kernel source as it is now (otherwise None)."""
     try:
@@ -60,18 +63,22 @@ def counter_traffic(workload):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload)
-    if not entry or entry.get("kernel_source_sha256_16") != source_digest():
+    entry = rec.get(key)
+    if not entry or entry.get("kernel_source_sha256_16") != source_digest(source):
         return None
     return entry.get("bytes_per_launch")
 
 
-def summarize_counters(workload, fetch_dir, write_dir, kernel_prefix="void (anonymous namespace)::fused_step_kernel",
+def reshard_key(workload, dst_world, dst_pad, dst_rank):
+    return f"reshard:{workload}:{dst_world}:{dst_pad}:{dst_rank}"
+
+
+def summarize_counters(key, fetch_dir, write_dir, kernel_prefix=STEP_KERNEL, source=KERNEL_SOURCE,
                        calib_kernel="stream_copy_kernel", calib_bytes=4 << 30):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, in KiB per
-    dispatch) into per-launch HBM bytes of the step kernel, each counter scaled by what it reads
-    for the plain copy kernel, whose true traffic is calib_bytes read and calib_bytes written.
-    Writes the result into profiles/traffic.json under the workload's name."""
+    dispatch) into per-launch HBM bytes of the measured kernel, each counter scaled by what it
+    reads for the plain copy kernel, whose true traffic is calib_bytes read and calib_bytes
+    written.  Writes the result into profiles/traffic.json under `key`."""
     import csv
     import statistics
 
@@ -100,17 +107,17 @@ def summarize_counters(workload, fetch_dir, write_dir, kernel_prefix="void (anon
             rec = json.load(fh)
     except (OSError, ValueError):
         rec = {}
-    rec[workload] = {
+    rec[key] = {
         "bytes_per_launch": round(fetch + write),
         "fetch_bytes": round(fetch), "write_bytes": round(write),
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
         "dispatches": [nf, nw],
-        "kernel_source_sha256_16": source_digest(),
+        "kernel_source_sha256_16": source_digest(source),
     }
     with open(PROFILE_TRAFFIC, "w") as fh:
         json.dump(rec, fh, indent=1, sort_keys=True)
         fh.write("\n")
-    print(json.dumps(rec[workload]))
+    print(json.dumps(rec[key]))
 
 
 def cpu_baseline(workload, seconds=12.0, sample=1 << 21):
@@ -143,6 +150,28 @@ def cpu_baseline(workload, seconds=12.0, sample=1 << 21):
     return {"value": n_real * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} elements of the {workload} slice, fan-in {w.fan_in}, "
                       f"{steps} oracle steps in {el:.1f} s (NumPy float32, one thread)"}
+
+
+def copy_reference(F, torch, dev, stream, nbytes=4 << 30):
+    """Plain 16-byte copy of nbytes (non-temporal loads and stores): the bandwidth a pure
+    read+write stream reaches, and the calibration kernel of the counter runs."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        F.stream_copy(src, dst, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    reps = 10
+    for _ in range(reps):
+        F.stream_copy(src, dst, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = a.elapsed_time(b) / reps
+    ref = {"GBps": round(2 * nbytes / (copy_ms / 1e3) / 1e9, 1), "bytes_moved": 2 * nbytes,
+           "kernel": "fsdpshard_stream_copy (16-byte loads and stores)"}
+    log(f"copy reference: {ref['GBps']} GB/s")
+    del src, dst
+    return ref
 
 
 def cpu_baseline_reshard(workload, dst_pad, dst_world, seconds=12.0):
@@ -233,6 +262,11 @@ def bench_reshard(args, w, F, W, torch):
     achieved = bytes_per_launch / (avg / 1e3) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; reshard_copy avg {avg:.3f} ms, "
         f"{achieved:.1f} GB/s")
+    copy_ref = None
+    if not args.no_copy_reference:
+        del states
+        torch.cuda.empty_cache()
+        copy_ref = copy_reference(F, torch, dev, stream)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
@@ -258,7 +292,9 @@ def bench_reshard(args, w, F, W, torch):
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": None},
+                     "traffic": counter_traffic(reshard_key(w.name, dst_world, dst_pad, dst_rank),
+                                                RESHARD_SOURCE)},
+        "copy_reference": copy_ref,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -292,7 +328,15 @@ def main():
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(args.workload, *args.summarize_counters)
+        if args.path == "reshard":
+            import workloads as W
+            w = W.WORKLOADS[args.workload]
+            key = reshard_key(w.name, args.reshard_world, args.reshard_pad or w.pad_multiple,
+                              args.reshard_rank)
+            summarize_counters(key, *args.summarize_counters, kernel_prefix=RESHARD_KERNEL,
+                               source=RESHARD_SOURCE)
+        else:
+            summarize_counters(args.workload, *args.summarize_counters)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -437,23 +481,7 @@ def main():
     if not args.no_copy_reference:
         del grads
         torch.cuda.empty_cache()
-        nbytes = 4 << 30
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            F.stream_copy(src, dst, stream=stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        reps = 10
-        for _ in range(reps):
-            F.stream_copy(src, dst, stream=stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        copy_ms = a.elapsed_time(b) / reps
-        copy_ref = {"GBps": round(2 * nbytes / (copy_ms / 1e3) / 1e9, 1), "bytes_moved": 2 * nbytes,
-                    "kernel": "fsdpshard_stream_copy (16-byte loads and stores)"}
-        log(f"copy reference: {copy_ref['GBps']} GB/s")
-        del src, dst
+        copy_ref = copy_reference(F, torch, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -8,10 +8,17 @@
 // The copy is a bandwidth-bound stream.  One launch carries up to kMaxPieces pieces in its
 // kernel arguments; every piece is cut into 4 KiB chunks of its destination, one work-group per
 // chunk, and a work-group finds its piece by binary search over the pieces' first chunks.  Each
-// lane stores one 16-byte destination-aligned vector; its source bytes are read with the widest
-// loads their relative alignment allows (16, 4 or 2 bytes).  The at most 14 bytes before the
-// first aligned destination vector and after the last one are copied 2 bytes at a time (every
-// element is at least 2 bytes wide).
+// lane stores one 16-byte destination-aligned vector.  Source and destination of a piece may sit
+// at different offsets within 16 bytes (a new world size or padding multiple moves every shard
+// boundary); then every lane still issues one aligned 16-byte load, takes the next aligned
+// vector from its neighbour lane, and funnel-shifts the pair into place, so the source stream is
+// read with full-width loads whatever its phase.  Loads and stores are non-temporal: every byte
+// is touched once.  The at most 14 bytes before the first aligned destination vector and after
+// the last one are copied 2 bytes at a time (every element is at least 2 bytes wide).
+//
+// An aligned 16-byte load that holds at least one byte of a piece may also cover a few bytes on
+// either side of it; those lie in the same 16-byte block, hence in the same page, and are
+// discarded.
 
 #include <hip/hip_runtime.h>
 
@@ -27,6 +34,7 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int64_t kChunk = 16 * kBlock;   // destination bytes per work-group
 constexpr int kMaxPieces = 96;            // keeps the kernel arguments under 4 KiB
+constexpr int kWaveShl1 = 0x130;          // DPP control: lane l reads lane l + 1 of the wave
 
 struct CopyPiece {
     const unsigned char* src;   // null: write zeros
@@ -40,19 +48,26 @@ struct ReshardParams {
     int32_t n;
 };
 
-__device__ __forceinline__ uint4 load16(const unsigned char* s, unsigned phase) {
-    if (phase == 0) return *reinterpret_cast<const uint4*>(s);
-    uint32_t w[4];
-    if ((phase & 3u) == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) w[k] = reinterpret_cast<const uint32_t*>(s)[k];
-    } else {
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(s);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = static_cast<uint32_t>(h[2 * k]) | (static_cast<uint32_t>(h[2 * k + 1]) << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+using u32x4_t = uint32_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t load_nt(const unsigned char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ void store_nt(unsigned char* p, u32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
+// Bytes [4W + sh/8, 4W + sh/8 + 16) of the 32 bytes lo:hi (little-endian words).
+template <int W>
+__device__ __forceinline__ u32x4_t funnel(u32x4_t lo, u32x4_t hi, uint32_t sh) {
+    const uint32_t c[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    u32x4_t r;
+    r.x = __builtin_amdgcn_alignbit(c[W + 1], c[W], sh);
+    r.y = __builtin_amdgcn_alignbit(c[W + 2], c[W + 1], sh);
+    r.z = __builtin_amdgcn_alignbit(c[W + 3], c[W + 2], sh);
+    r.w = __builtin_amdgcn_alignbit(c[W + 4], c[W + 3], sh);
+    return r;
 }
 
 __global__ __launch_bounds__(kBlock) void reshard_kernel(ReshardParams p) {
@@ -66,17 +81,47 @@ __global__ __launch_bounds__(kBlock) void reshard_kernel(ReshardParams p) {
     const int64_t chunk = b - p.first_block[a];
     const int64_t head_raw = static_cast<int64_t>((16u - (reinterpret_cast<uintptr_t>(pc.dst) & 15u)) & 15u);
     const int64_t head = head_raw < pc.bytes ? head_raw : pc.bytes;
-    const int64_t body = (pc.bytes - head) & ~static_cast<int64_t>(15);
-    const int64_t tail = pc.bytes - head - body;
+    const int64_t body_end = head + ((pc.bytes - head) & ~static_cast<int64_t>(15));
+    const int64_t tail = pc.bytes - body_end;
 
+    const int lane = threadIdx.x & 63;
     const int64_t off = head + chunk * kChunk + static_cast<int64_t>(threadIdx.x) * 16;
-    if (off + 16 <= head + body) {
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (pc.src != nullptr) {
-            const unsigned phase = static_cast<unsigned>(reinterpret_cast<uintptr_t>(pc.src + off) & 15u);
-            v = load16(pc.src + off, phase);
+    const bool active = off + 16 <= body_end;
+    if (pc.src == nullptr) {
+        if (active) store_nt(pc.dst + off, u32x4_t{0u, 0u, 0u, 0u});
+    } else {
+        // The source phase is the same for every lane of the piece (off is head + 16k).
+        const uint32_t ph = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(pc.src + off) & 15u);
+        const unsigned char* base = pc.src + (off - ph);
+        if (ph == 0) {
+            if (active) store_nt(pc.dst + off, load_nt(base));
+        } else {
+            // Each active lane loads its own aligned vector; the next one comes from lane + 1
+            // through a one-lane wave shift (DPP wave_shl), except where lane + 1 is past the
+            // piece or in the next wave: there the lane loads it itself, issued together with its
+            // first load so that no wave waits for a second round trip.
+            const bool next_active = lane < 63 && off + 32 <= body_end;
+            u32x4_t lo = {0u, 0u, 0u, 0u}, extra = {0u, 0u, 0u, 0u};
+            if (active) lo = load_nt(base);
+            if (active && !next_active) extra = load_nt(base + 16);
+            u32x4_t hi;
+            hi.x = __builtin_amdgcn_mov_dpp(static_cast<int>(lo.x), kWaveShl1, 0xF, 0xF, false);
+            hi.y = __builtin_amdgcn_mov_dpp(static_cast<int>(lo.y), kWaveShl1, 0xF, 0xF, false);
+            hi.z = __builtin_amdgcn_mov_dpp(static_cast<int>(lo.z), kWaveShl1, 0xF, 0xF, false);
+            hi.w = __builtin_amdgcn_mov_dpp(static_cast<int>(lo.w), kWaveShl1, 0xF, 0xF, false);
+            if (!next_active) hi = extra;
+            if (active) {
+                const uint32_t sh = (ph & 3u) * 8u;
+                u32x4_t v;
+                switch (ph >> 2) {
+                    case 0: v = funnel<0>(lo, hi, sh); break;
+                    case 1: v = funnel<1>(lo, hi, sh); break;
+                    case 2: v = funnel<2>(lo, hi, sh); break;
+                    default: v = funnel<3>(lo, hi, sh); break;
+                }
+                store_nt(pc.dst + off, v);
+            }
         }
-        *reinterpret_cast<uint4*>(pc.dst + off) = v;
     }
     if (chunk == 0) {
         const int64_t t2 = static_cast<int64_t>(threadIdx.x) * 2;
@@ -85,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void reshard_kernel(ReshardParams p) {
             *reinterpret_cast<uint16_t*>(pc.dst + t2) = x;
         }
         if (t2 < tail) {
-            const int64_t o = head + body + t2;
+            const int64_t o = body_end + t2;
             const uint16_t x = pc.src ? *reinterpret_cast<const uint16_t*>(pc.src + o) : 0;
             *reinterpret_cast<uint16_t*>(pc.dst + o) = x;
         }
