@@ -152,6 +152,70 @@ def cpu_baseline(workload, seconds=12.0, sample=1 << 21):
                       f"{steps} oracle steps in {el:.1f} s (NumPy float32, one thread)"}
 
 
+def _oracle_chunk(args):
+    """Worker of the parallel baseline: the oracle on elements [a, b) of the sampled slice."""
+    workload, a, b, seconds = args
+    import numpy as np
+    import workloads as W
+    from oracle import layout as OL
+    from oracle import step as OS
+
+    w = W.WORKLOADS[workload]
+    lo, hi, osegs = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
+    flags = np.zeros(b - a, dtype=np.int64)
+    for s in osegs:
+        x, y = max(a, s["shard_begin"]), min(b, s["shard_begin"] + s["length"])
+        if x < y:
+            flags[x - a:y - a] = s["flags"]
+    master, m, v = W.np_state(w, b - a, a)
+    grads = W.np_grads(w, b - a, 1, a)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        steps += 1
+        master, m, v, _ = OS.shard_step(master, m, v, grads, flags, w.hp, steps)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return int(np.count_nonzero((flags & OL.PADDING) == 0)) * steps
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_parallel(workload, procs, seconds=12.0, chunk=1 << 20):
+    """The same oracle in `procs` processes, each stepping its own contiguous chunk of the slice
+    (valid because the step is elementwise once the layout is fixed).  Rate = all processes'
+    real parameters x steps / the wall time of the whole pool."""
+    import multiprocessing as mp
+
+    import workloads as W
+    from oracle import layout as OL
+
+    w = W.WORKLOADS[workload]
+    lo, hi, _ = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
+    n = hi - lo
+    procs = max(1, min(procs, n // chunk if n >= chunk else 1))
+    jobs = [(workload, i * chunk, min(n, (i + 1) * chunk), seconds) for i in range(procs)]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(procs) as pool:
+        done = sum(pool.map(_oracle_chunk, jobs))
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "params/s", "cores": procs, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"{procs} processes, each stepping the oracle on its own "
+                      f"{chunk}-element chunk of the {workload} slice for about {seconds:.0f} s "
+                      f"(NumPy float32); rate over the pool's wall time including start-up"}
+
+
 def copy_reference(F, torch, dev, stream, nbytes=4 << 30):
     """Plain 16-byte copy of nbytes (non-temporal loads and stores): the bandwidth a pure
     read+write stream reaches, and the calibration kernel of the counter runs."""
@@ -322,6 +386,12 @@ def main():
                     help="reshard path: destination rank")
     ap.add_argument("--micro-batches", type=int, default=4)
     ap.add_argument("--max-grad-norm", type=float, default=1.0)
+    ap.add_argument("--evict-mb", type=int, default=-1,
+                    help="MiB written between timed steps to flush the 256 MB last-level cache "
+                         "(-1: 1024 when one step moves under 2 GB, else 0); with eviction the "
+                         "per-step time is the sum of the step's HIP-event kernel times")
+    ap.add_argument("--cpu-procs", type=int, default=16,
+                    help="processes for the parallel oracle baseline (0: skip it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-reference", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -413,7 +483,14 @@ def main():
                 master, m, v, acc, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
                 **common), L.n_real * algorithmic_bytes_per_param_f32grad()))
 
+    step_bytes = sum(b for _, _, b in stages)
+    evict_mb = args.evict_mb if args.evict_mb >= 0 else (1024 if step_bytes < 2e9 else 0)
+    evict = (torch.zeros(evict_mb << 18, dtype=torch.float32, device=dev) if evict_mb
+             else None)
+
     def one_step(t, ev=None):
+        if evict is not None:
+            evict.add_(1.0)   # outside the kernel events: flushes the last-level cache
         F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
         for i, (_, launch, _) in enumerate(stages):
             if ev is not None:
@@ -435,12 +512,21 @@ def main():
         one_step(args.warmup + 1 + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
+    step_ms = [sum(events[i][j][0].elapsed_time(events[i][j][1]) for j in range(len(stages)))
+               for i in range(args.steps)]
+    if evict is None:
+        ms_per_step = wall / args.steps * 1e3
+        timing = "wall clock over the timed steps"
+    else:
+        ms_per_step = sum(step_ms) / len(step_ms)
+        timing = (f"sum of each step's HIP-event kernel times; {evict_mb} MiB written between "
+                  "steps to flush the last-level cache")
     stage_info = []
     for j, (name, _, nbytes) in enumerate(stages):
         ms = [events[i][j][0].elapsed_time(events[i][j][1]) for i in range(args.steps)]
         avg = sum(ms) / len(ms)
         stage_info.append({"call": name, "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4),
+                           "median_ms": round(sorted(ms)[len(ms) // 2], 4),
                            "algorithmic_bytes": nbytes,
                            "GBps": round(nbytes / (avg / 1e3) / 1e9, 1)})
     main_stage = max(stage_info, key=lambda x: x["avg_ms"])
@@ -483,11 +569,14 @@ def main():
         torch.cuda.empty_cache()
         copy_ref = copy_reference(F, torch, dev, stream)
 
-    cpu = None
+    cpu = cpu_par = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         cpu = cpu_baseline(w.name)
         log(f"cpu oracle: {cpu['value']:.3e} params/s")
+        if args.cpu_procs > 0:
+            cpu_par = cpu_baseline_parallel(w.name, args.cpu_procs)
+            log(f"cpu oracle, {cpu_par['cores']} processes: {cpu_par['value']:.3e} params/s")
 
     value = L.n_real / (ms_per_step / 1e3)
     rec = {
@@ -518,6 +607,9 @@ def main():
             "achieved_GBps_wall": round(sum(x["algorithmic_bytes"] for x in stage_info)
                                         / (ms_per_step / 1e3) / 1e9, 1),
             "kernel_avg_ms": round(avg_kernel_s * 1e3, 4),
+            "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+            "step_ms_min": round(min(step_ms), 4),
+            "timing": timing,
             "path": args.path,
             "stages": stage_info,
             "groups_per_wave": args.groups_per_wave or "default",
@@ -526,6 +618,7 @@ def main():
         "mix_reference": mix_ref,
         "copy_reference": copy_ref,
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": cpu_par,
     }
     print(json.dumps(rec), flush=True)
 

@@ -2,8 +2,8 @@
 benchmark times, compared with the oracle on sampled windows of the slice.
 
 The step is elementwise once the layout is fixed, so the oracle can recompute any subset of
-elements from the same inputs.  Windows: the first and last 64 Ki elements, +-4 Ki around every
-segment edge inside the slice, and 16 random 64 Ki windows.  Inputs are drawn on the device with
+elements from the same inputs.  Windows: the first and last 1 Mi elements, +-4 Ki around every
+segment edge inside the slice, and 64 random 64 Ki windows.  Inputs are drawn on the device with
 seeded generators (no value comes from the library); the oracle receives copies of exactly the
 windowed inputs.  The bf16 destination uses the phase the slice has in a 16-byte aligned flat
 vector (lo mod 8), and a guarded prefix / suffix of the flat window must survive.
@@ -21,12 +21,13 @@ from gpu_helpers import SENT16, assert_bf16, assert_f32, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 WIN = 65536
+END = 1 << 20
 EDGE = 4096
 
 
 def _windows(n, edges, rng):
-    spans = [(0, WIN), (n - WIN, n)] + [(e - EDGE, e + EDGE) for e in edges]
-    for s in rng.integers(0, max(1, n - WIN), 16):
+    spans = [(0, END), (n - END, n)] + [(e - EDGE, e + EDGE) for e in edges]
+    for s in rng.integers(0, max(1, n - WIN), 64):
         spans.append((int(s), int(s) + WIN))
     mask_idx = []
     for a, b in spans:
