@@ -18,8 +18,10 @@
 //   * One tile per wave: each wave owns U consecutive 512-element groups (U = 1 by default; 2
 //     and 4 selectable) and issues every HBM load of its tile before the first arithmetic
 //     instruction; the grid has one work-group of 4 waves per 4U groups (hundreds of thousands
-//     for a 7B-model slice), so the hardware dispatcher feeds all 256 CUs in address order.  Gradient loads and all
-//     full-vector stores carry the non-temporal hint (single-use streams); the state loads do not.
+//     for a 7B-model slice), enough to keep all 256 CUs fed.  Work-groups map to tiles so that
+//     each of the 8 XCDs streams runs of 64 consecutive tiles (tile_index).  Gradient loads and
+//     all full-vector stores carry the non-temporal hint (single-use streams); the state loads
+//     do not.
 //   * Contributions are reduced in registers in rank order 0..F-1 from +0 (fixed order, so the
 //     result is deterministic and matches a sequential float32 sum bit for bit).
 //   * Segment flags (padding, weight decay) come from a per-wave cursor over the segment table:
