@@ -7,7 +7,8 @@
 //
 // The copy is a bandwidth-bound stream.  One launch carries up to kMaxPieces pieces in its
 // kernel arguments; every piece is cut into 4 KiB chunks of its destination, one work-group per
-// chunk, and a work-group finds its piece by binary search over the pieces' first chunks.  Each
+// chunk (XCD-aware order, chunk_index), and a work-group finds its piece by binary search over
+// the pieces' first chunks.  Each
 // lane stores one 16-byte destination-aligned vector.  Source and destination of a piece may sit
 // at different offsets within 16 bytes (a new world size or padding multiple moves every shard
 // boundary); then every lane still issues one aligned 16-byte load, takes the next aligned
@@ -70,8 +71,24 @@ __device__ __forceinline__ u32x4_t funnel(u32x4_t lo, u32x4_t hi, uint32_t sh) {
     return r;
 }
 
-__global__ __launch_bounds__(kBlock) void reshard_kernel(ReshardParams p) {
+// Work-group -> chunk.  The hardware deals work-groups to the 8 XCDs in turn; this permutation
+// gives each XCD runs of kXcdRun consecutive chunks (1 MiB of destination) instead of every
+// eighth chunk, and keeps the identity past the last whole block of 8 * kXcdRun chunks.
+// Measured on one GPU against the identity map: 3-5 % faster on misaligned pieces, 1 % on
+// aligned ones; runs of 16 chunks were slower, 128-512 about the same as 256.
+constexpr int64_t kXcds = 8;
+constexpr int64_t kXcdRun = 256;
+
+__device__ __forceinline__ int64_t chunk_index() {
     const int64_t b = blockIdx.x;
+    const int64_t whole = static_cast<int64_t>(gridDim.x) / (kXcds * kXcdRun) * (kXcds * kXcdRun);
+    if (b >= whole) return b;
+    const int64_t x = b % kXcds, q = b / kXcds;
+    return (q / kXcdRun) * (kXcds * kXcdRun) + x * kXcdRun + q % kXcdRun;
+}
+
+__global__ __launch_bounds__(kBlock) void reshard_kernel(ReshardParams p) {
+    const int64_t b = chunk_index();
     int a = 0, z = p.n;   // largest piece index with first_block <= b
     while (z - a > 1) {
         const int mid = (a + z) >> 1;
