@@ -127,6 +127,40 @@ def test_sumsq_fp32_grad_and_padding():
     assert abs(got - want) <= SUMSQ_RTOL * want
 
 
+@pytest.mark.parametrize("n", [32768, 32769, 262144 + 8, 1_000_003, 2_500_001])
+def test_sumsq_fp32_grad_sizes(n):
+    # Several whole 32,768-element tiles (the straight-line path, 8 groups per batch) and a tail.
+    say(f"sumsq fp32 n={n}")
+    grad = W.np_f32_normal([67, n], n, 1e-2)
+    got = _gpu_sumsq(grad=torch.from_numpy(grad).cuda(), n=n, scale=0.25)
+    want = OC.sumsq_exact(grad * np.float32(0.25))
+    assert abs(got - want) <= SUMSQ_RTOL * want, (got, want)
+
+
+@pytest.mark.parametrize("F_in", [-1, 1, 4, 8])
+def test_sumsq_padding_inside_whole_tiles(F_in):
+    # 300 small tensors padded to 16 (padding every few hundred elements, NaN-filled) across
+    # many whole tiles: the straight-line path must drop padding exactly as the checked path.
+    sizes = [(i * 7919) % 3001 + 1 for i in range(300)]
+    L, segs, flags = _layout(sizes, 16, None, 2, 1)
+    n = L.n
+    real = (flags & OL.PADDING) == 0
+    say(f"sumsq padded tiles F={F_in} n={n} segments={L.n_segments}")
+    sd, ns = F.segments_to_device(segs), L.n_segments
+    if F_in == -1:
+        grad = W.np_f32_normal([68, 1], n, 1e-2)
+        grad[~real] = np.nan
+        got = _gpu_sumsq(grad=torch.from_numpy(grad).cuda(), n=n, segs=sd, nseg=ns)
+        want = OC.sumsq_exact(grad, real)
+    else:
+        contribs = [W.np_bf16_normal([69, r], n, 1e-2) for r in range(F_in)]
+        for c in contribs:
+            c[~real] = 0x7FC0
+        got = _gpu_sumsq(contribs=[to_dev16(c) for c in contribs], n=n, segs=sd, nseg=ns)
+        want = OC.grad_sumsq(contribs, real)
+    assert abs(got - want) <= SUMSQ_RTOL * want, (got, want)
+
+
 @pytest.mark.parametrize("max_norm", [1e-3, 0.5, 1e9])
 def test_clipped_step_all_ranks(max_norm):
     """Every rank of a small model computes its part of the squared norm on the GPU; the parts
