@@ -199,6 +199,20 @@ def _ptr(t, what, dtypes=None, numel=None):
     return t.data_ptr()
 
 
+def _need_bytes(t, what, nbytes):
+    """The library sees only pointers, so the binding checks that a tensor holds `nbytes`."""
+    if t is None or isinstance(t, int):
+        return
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes, {nbytes} needed")
+
+
+def _segs(segs, n_segments):
+    _need_bytes(segs, "segs", SEGMENT_DTYPE.itemsize * int(n_segments))
+    return _ptr(segs, "segs")
+
+
 def _stream(stream, like=None):
     if stream is None:
         import torch
@@ -260,7 +274,7 @@ def adamw_shard_step(master, m, v, contribs, step, lr, beta1=0.9, beta2=0.999, e
     _check("adamw_shard_step", lib().adamw_shard_step(
         _ptr(master, "master", f32, n), _ptr(m, "m", f32, n), _ptr(v, "v", f32, n),
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n,
-        _ptr(segs, "segs"), int(n_segments), ctypes.byref(hp),
+        _segs(segs, n_segments), int(n_segments), ctypes.byref(hp),
         _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
 
 
@@ -277,7 +291,7 @@ def adamw_shard_step_f32grad(master, m, v, grad, step, lr, beta1=0.9, beta2=0.99
         _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
     _check("adamw_shard_step_f32grad", lib().adamw_shard_step_f32grad(
         _ptr(master, "master", f32, n), _ptr(m, "m", f32, n), _ptr(v, "v", f32, n),
-        _ptr(grad, "grad", f32, n), n, _ptr(segs, "segs"), int(n_segments), ctypes.byref(hp),
+        _ptr(grad, "grad", f32, n), n, _segs(segs, n_segments), int(n_segments), ctypes.byref(hp),
         _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
 
 
@@ -317,7 +331,7 @@ def grad_sumsq_shard(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=No
     else:
         arr_p, fan_in, gp = None, 0, _ptr(grad, "grad", {torch.float32}, n)
     _check("grad_sumsq_shard", lib().grad_sumsq_shard(
-        arr_p, fan_in, gp, n, _ptr(segs, "segs"), int(n_segments), float(scale),
+        arr_p, fan_in, gp, n, _segs(segs, n_segments), int(n_segments), float(scale),
         _ptr(workspace, "workspace"), wbytes, _ptr(sumsq, "sumsq", {torch.float64}, 1),
         _stream(stream, sumsq)))
 
@@ -330,13 +344,15 @@ def unflatten_bf16(master, flat, flat_index0=0, lo=0, segs=None, n_segments=0, n
     if not isinstance(flat, int):
         _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
     _check("unflatten_bf16", lib().unflatten_bf16(
-        _ptr(master, "master", {torch.float32}, n), n, _ptr(segs, "segs"), int(n_segments),
+        _ptr(master, "master", {torch.float32}, n), n, _segs(segs, n_segments), int(n_segments),
         _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
 
 
 def stream_copy(src, dst, nbytes=None, stream=None):
     """Measurement aid: plain 16-byte-vector device copy (bandwidth reference)."""
     nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _need_bytes(src, "src", nbytes)
+    _need_bytes(dst, "dst", nbytes)
     _check("fsdpshard_stream_copy", lib().fsdpshard_stream_copy(
         _ptr(src, "src"), _ptr(dst, "dst"), nbytes, _stream(stream, src)))
 
@@ -345,6 +361,8 @@ def stream_mix(contribs, s0, s1, s2, out, n=None, stream=None):
     """Measurement aid: the fused step's traffic with trivial arithmetic (n a multiple of 8)."""
     n = s0.numel() if n is None else int(n)
     arr = _contrib_array(contribs, n)
+    for t, what, b in ((s0, "s0", 4), (s1, "s1", 4), (s2, "s2", 4), (out, "out", 2)):
+        _need_bytes(t, what, b * n)
     _check("fsdpshard_stream_mix", lib().fsdpshard_stream_mix(
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(s0, "s0"), _ptr(s1, "s1"),
         _ptr(s2, "s2"), _ptr(out, "out"), n, _stream(stream, s0)))
@@ -376,13 +394,13 @@ def reshard_copy(src_shards, dst, pieces, stream=None):
     no piece reads), ``dst`` the destination shard; all of one dtype (2, 4 or 8 bytes)."""
     like = next(t for t in list(src_shards) + [dst] if t is not None)
     elem = like.element_size()
+    for t in list(src_shards) + [dst]:
+        if t is not None and t.element_size() != elem:
+            raise ValueError("all shards must share one element size")
     n_src = len(src_shards)
     ptrs = (c_vp * n_src)(*[None if t is None else _ptr(t, f"source shard {i}")
                             for i, t in enumerate(src_shards)])
     elems = (c_i64 * n_src)(*[0 if t is None else t.numel() for t in src_shards])
-    for t in src_shards:
-        if t is not None and t.element_size() != elem:
-            raise ValueError("all shards must share one element size")
     pieces = np.ascontiguousarray(pieces, dtype=PIECE_DTYPE)
     _check("reshard_copy", lib().reshard_copy(
         ptrs, elems, n_src, _ptr(dst, "dst"), dst.numel(),

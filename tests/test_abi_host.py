@@ -363,3 +363,17 @@ def test_reshard_copy_validation():
     assert lib.reshard_copy(src, elems, 2, None, 0, good, 0, 4, None) == OK
     assert lib.reshard_copy(src, elems, 2, None, 100, good, 0, 4, None) == INVALID
     assert lib.reshard_copy(src, elems, 2, None, 0, good, 1, 4, None) == INVALID
+
+
+def test_binding_checks_buffer_sizes_before_any_call():
+    # The library sees only pointers; the binding rejects buffers too small for the call (these
+    # checks run before any device pointer is taken, so CPU tensors exercise them).
+    import torch
+    with pytest.raises(ValueError, match="segs holds 31 bytes, 32 needed"):
+        F._segs(torch.zeros(31, dtype=torch.uint8), 1)
+    F._segs(None, 0)
+    with pytest.raises(ValueError, match="dst holds 8 bytes, 16 needed"):
+        F.stream_copy(torch.zeros(4, dtype=torch.float32), torch.zeros(2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="one element size"):
+        F.reshard_copy([torch.zeros(4, dtype=torch.float32)], torch.zeros(4, dtype=torch.int16),
+                       np.zeros(0, dtype=F.PIECE_DTYPE))
