@@ -379,10 +379,11 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--groups-per-wave", type=int, default=0,
                     help="512-element groups per wavefront (1, 2, 4; 0 = library default)")
-    ap.add_argument("--path", choices=["fused", "clipped", "accumulate", "reshard"],
+    ap.add_argument("--path", choices=["fused", "clipped", "accumulate", "split", "reshard"],
                     default="fused",
                     help="fused: the fused step (default); clipped: sum of squares + clipped "
                          "step; accumulate: fp32 micro-batch accumulation + clipped fp32 step; "
+                         "split: the step without its bf16 output, then unflatten_bf16; "
                          "reshard: move one destination rank's fp32 master/m/v to another "
                          "world size and padding multiple")
     ap.add_argument("--reshard-world", type=int, default=6,
@@ -466,6 +467,13 @@ def main():
     if args.path == "fused":
         stages.append(("adamw_shard_step", lambda t: F.adamw_shard_step(
             master, m, v, grads, step=t, **common), L.n_real * bpp))
+    elif args.path == "split":
+        no_out = {k: v for k, v in common.items() if k not in ("flat", "flat_index0", "lo")}
+        stages.append(("adamw_shard_step (no bf16 output)", lambda t: F.adamw_shard_step(
+            master, m, v, grads, step=t, **no_out), L.n_real * (bpp - 2)))
+        stages.append(("unflatten_bf16", lambda t: F.unflatten_bf16(
+            master, flat, flat_index0=lo - phase, lo=lo, segs=segs_dev,
+            n_segments=L.n_segments, stream=stream), L.n_real * 4 + n * 2))
     else:
         sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
         ws = torch.empty(max(8, F.grad_sumsq_workspace_bytes(n)), dtype=torch.uint8, device=dev)
