@@ -864,7 +864,8 @@ __global__ __launch_bounds__(kBlock) void stream_copy_kernel(const uint4* __rest
 
 // Measurement aid: the fused step's exact streams (F non-temporal bf16 loads, three fp32
 // read-modify-write streams, one bf16 store per 8-element vector, one 512-element group per wave)
-// with trivial integer arithmetic in place of the reduction and the optimizer.
+// with trivial integer arithmetic in place of the reduction and the optimizer, launched with the
+// same grid and the same work-groups per CU as the step.
 struct MixParams {
     const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
     float* s[3];
@@ -930,10 +931,52 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     return x < y + static_cast<uintptr_t>(bbytes) && y < x + static_cast<uintptr_t>(abytes);
 }
 
-int launch(const void* kernel, unsigned blocks, void* params, void* stream) {
+// Resident work-groups per CU.  The streaming kernels lose bandwidth when every CU holds as
+// many work-groups as its registers allow: with fewer waves in flight the HBM sees fewer
+// concurrent access streams.  The cap is set by reserving LDS that the kernels never touch (a
+// dynamic LDS size at launch), sized from the device's LDS per CU so that exactly `per_cu`
+// work-groups fit: halfway between lds/(per_cu+1) and lds/per_cu.  Measured on one GPU against the
+// register-limited occupancy: the fused step is 4-10 % faster with 2 per CU at fan-in 1 and 8 and
+// from an fp32 gradient; at fan-in 4 the 2,000-tensor slice is 5 % faster with 3 per CU (2 gains
+// nothing there), and at fan-in 2 and 16 both are within 1 %, so other fan-ins take 3.  The fp32
+// accumulation is 4-10 % faster with 2 per CU; the plain reduction of a single contribution wants
+// 4 per CU (2 cost it a quarter); the sum of squares, unflatten and plain copies are fastest
+// uncapped.
+constexpr int step_groups_per_cu(int fan_in) {
+    return fan_in == 1 || fan_in == 8 || fan_in == -1 ? 2 : 3;
+}
+constexpr int kReduceGroupsPerCU = 2;
+constexpr int kReduceOneStreamGroupsPerCU = 4;
+constexpr int kMaxDevices = 64;
+std::atomic<int64_t> g_lds_per_cu[kMaxDevices];   // 0: not queried yet; -1: unknown
+
+int64_t lds_per_cu() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    int64_t v = g_lds_per_cu[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int bytes = 0;
+        const hipError_t e = hipDeviceGetAttribute(
+            &bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+        v = (e == hipSuccess && bytes > 0) ? bytes : -1;
+        g_lds_per_cu[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// Dynamic LDS bytes that leave room for exactly `per_cu` work-groups (0: no cap).
+size_t occupancy_lds(int per_cu) {
+    if (per_cu <= 0) return 0;
+    const int64_t lds = lds_per_cu();
+    if (lds <= 0) return 0;
+    const int64_t bytes = (lds / (per_cu + 1) + lds / per_cu) / 2;
+    return static_cast<size_t>(bytes & ~static_cast<int64_t>(1023));
+}
+
+int launch(const void* kernel, unsigned blocks, void* params, void* stream, int per_cu = 0) {
     void* args[] = {params};
-    const hipError_t e = hipLaunchKernel(kernel, dim3(blocks), dim3(kBlock), args, 0,
-                                         static_cast<hipStream_t>(stream));
+    const hipError_t e = hipLaunchKernel(kernel, dim3(blocks), dim3(kBlock), args,
+                                         occupancy_lds(per_cu), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
 }
 
@@ -1078,7 +1121,8 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     unsigned blocks = 0;
     rc = tile_grid(n, groups, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(pick_step_kernel(fan_in, out != nullptr, groups), blocks, &p, stream);
+    return launch(pick_step_kernel(fan_in, out != nullptr, groups), blocks, &p, stream,
+                  step_groups_per_cu(fan_in));
 }
 
 int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, float scale,
@@ -1119,7 +1163,8 @@ int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, fl
     unsigned blocks = 0;
     rc = tile_grid(n, groups, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(k, blocks, &p, stream);
+    return launch(k, blocks, &p, stream,
+                  fan_in == 1 && !accumulate ? kReduceOneStreamGroupsPerCU : kReduceGroupsPerCU);
 }
 
 int64_t sumsq_partials(int64_t n) {
@@ -1305,5 +1350,5 @@ extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan
     const void* k = fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1>)
                     : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8>)
                                   : reinterpret_cast<const void*>(&stream_mix_kernel<0>);
-    return launch(k, blocks, &p, stream);
+    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in));   // as the step
 }
