@@ -522,15 +522,18 @@ __device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, in
 // Wave w of the grid owns vectors [w * 64U, (w + 1) * 64U) of the slice.
 // Work-group -> tile.  MI355X deals a launch's work-groups to its 8 XCDs in turn, so with the
 // identity map neighbouring tiles run on different XCDs at the same moment.  Here work-group b on
-// XCD x = b mod 8 takes the (b / 8 mod kXcdRun)-th tile of the x-th run of kXcdRun consecutive
-// tiles in each block of 8 * kXcdRun tiles: every XCD streams its own 64-tile run (512 KiB of
-// each fp32 stream).  Work-groups past the last whole block keep the identity map, so the map is
-// a permutation of [0, gridDim.x) for any grid.  Measured on one GPU against the identity map:
-// the fused step 3-4 % faster on the 7B-shaped slice and 0.4-1.4 % on the 70B-shaped one, the
-// fp32 accumulation 2-5 % faster; runs of 8 or 96 tiles were slower than 64 or 128.  Results never
-// depend on the map: a tile's work is the same wherever it runs.
+// XCD x = b mod 8 takes the (b / 8 mod Run)-th tile of the x-th run of Run consecutive tiles in
+// each block of 8 * Run tiles: every XCD streams its own run of tiles.  Work-groups past the last
+// whole block keep the identity map, so the map is a permutation of [0, gridDim.x) for any grid.
+// Measured on one GPU against the identity map, with runs of 64 tiles (512 KiB of each fp32
+// stream): the fused step 3-4 % faster on the 7B-shaped slice and 0.4-1.4 % on the 70B-shaped
+// one, the fp32 accumulation 2-5 % faster; runs of 8 or 96 tiles were slower than 64 or 128.  With
+// the cap on work-groups per CU (launch), the fused step does 0.5-1 % better with runs of 32 tiles
+// on the large slices, while the reduction keeps 64 (2 % better than 32).  Results never depend
+// on the map: a tile's work is the same wherever it runs.
 constexpr int64_t kXcds = 8;
-constexpr int64_t kXcdRun = 64;
+constexpr int64_t kXcdRun = 64;       // reduction, unflatten
+constexpr int64_t kStepXcdRun = 32;   // fused step and its traffic replica
 
 template <int64_t Run = kXcdRun>
 __device__ __forceinline__ int64_t tile_index() {
@@ -541,8 +544,9 @@ __device__ __forceinline__ int64_t tile_index() {
     return (q / Run) * (kXcds * Run) + x * Run + q % Run;
 }
 
+template <int64_t Run = kXcdRun>
 __device__ __forceinline__ int64_t tile_base(int wave, int groups) {
-    return (tile_index() * kWavesPerBlock + wave) * (kWave * groups);
+    return (tile_index<Run>() * kWavesPerBlock + wave) * (kWave * groups);
 }
 
 template <int F, bool OUT, int U>
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
-    const int64_t base0 = tile_base(wave, U);
+    const int64_t base0 = tile_base<kStepXcdRun>(wave, U);
     if (base0 >= nvec) return;
     if constexpr (F != 0) {
         if (base0 + kWave * U <= p.n / kVec) {
@@ -878,7 +882,7 @@ template <int F>
 __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
-    const int64_t vec = tile_base(wave, 1) + lane;
+    const int64_t vec = tile_base<kStepXcdRun>(wave, 1) + lane;
     if (vec >= p.nvec) return;
     const int64_t e0 = vec * kVec;
     const int fan_in = F > 0 ? F : p.fan_in;
