@@ -1,0 +1,45 @@
+"""Host-side checks of bench.py that need no GPU: the one-GPU contract and the counter digest."""
+
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    for n in (2, 8):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2
+        assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text("// note\nint f(int x) { return x + 1; } /* block\n comment */\n")
+    b.write_text("// another note\n\nint f(int x)  {\n  return x + 1;\n}\n")
+    c.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.source_digest(str(a)) == bench.source_digest(str(b))
+    assert bench.source_digest(str(a)) != bench.source_digest(str(c))
+
+
+def test_counter_traffic_is_reported_only_for_the_measured_code(tmp_path, monkeypatch):
+    # A traffic entry counts only while its digest matches the kernel code; otherwise the bench
+    # reports no traffic (the counters must be taken again).
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }\n")
+    table = tmp_path / "traffic.json"
+    table.write_text(json.dumps({"w": {"bytes_per_launch": 123,
+                                       "kernel_source_sha256_16": bench.source_digest(str(src))}}))
+    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(table))
+    assert bench.counter_traffic("w", str(src)) == 123
+    assert bench.counter_traffic("other", str(src)) is None
+    src.write_text("int f() { return 2; }\n")
+    assert bench.counter_traffic("w", str(src)) is None
