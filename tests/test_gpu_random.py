@@ -1,0 +1,112 @@
+"""Randomized GPU parity sweep of the fused step against the oracle.
+
+Each trial draws a whole case from a seeded generator: tensor sizes and padding multiple, world
+size and rank, per-tensor weight-decay mask, fan-in (compile-time and run-time fan-ins up to 64)
+or an fp32 gradient shard, AdamW hyperparameters, gradient scale, clipping by the global norm
+(the squared norm taken on the GPU, as a caller would), the bf16 window's phase and the groups
+per wave.  Two steps per trial; fp32 state within relative 1e-5, bf16 within 1 ulp, NaN padding
+gradients ignored, guard bands intact.
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_layout_amd as F
+import workloads as W
+from oracle import clip as OC
+from oracle import layout as OL
+from oracle import step as OS
+from gpu_helpers import Guarded, assert_bf16, assert_f32, say, to_dev16
+
+pytestmark = pytest.mark.gpu
+SIZE_CHOICES = [1, 3, 7, 16, 100, 513, 2049, 4099, 30001, 70003]
+FAN_CHOICES = [-1, 1, 2, 3, 4, 5, 7, 8, 9, 16, 33, 64]   # -1: one fp32 gradient shard
+
+
+def _draw(rng):
+    while True:
+        T = rng.randint(1, 8)
+        sizes = [rng.choice(SIZE_CHOICES) for _ in range(T)]
+        pad = rng.choice([1, 2, 4, 8, 16])
+        N = rng.randint(1, 9)
+        k = rng.randrange(N)
+        _, P = OL.flatten_offsets(sizes, pad)
+        lo, hi = OL.shard_bounds(P, N, k)
+        if hi > lo:
+            break
+    wd = [int(rng.random() < 0.6) for _ in range(T)]
+    hp = dict(lr=rng.choice([1e-3, 3e-4, 1e-2]), beta1=rng.choice([0.9, 0.8]),
+              beta2=rng.choice([0.999, 0.95]), eps=rng.choice([1e-8, 1e-6]),
+              weight_decay=rng.choice([0.0, 0.01, 0.1]),
+              grad_scale=rng.choice([1.0, 0.5, 0.125]))
+    return dict(sizes=sizes, pad=pad, N=N, k=k, wd=wd, F_in=rng.choice(FAN_CHOICES), hp=hp,
+                clip=rng.choice([0.0, 0.0, 1e-3, 10.0]), d=rng.randrange(8),
+                groups=rng.choice([0, 1, 2, 4]))
+
+
+@pytest.mark.parametrize("trial", range(40))
+def test_random_fused_steps(trial):
+    c = _draw(random.Random(1000 + trial))
+    L, segs = F.shard_layout(c["sizes"], c["N"], c["k"], c["pad"], c["wd"])
+    lo, hi, osegs = OL.segments(c["sizes"], c["pad"], c["wd"], c["N"], c["k"])
+    assert (L.lo, L.hi) == (lo, hi)
+    n = hi - lo
+    flags = np.zeros(n, dtype=np.int64)
+    for s in osegs:
+        flags[s["shard_begin"]: s["shard_begin"] + s["length"]] = s["flags"]
+    real = (flags & OL.PADDING) == 0
+    F_in, hp, clip, d = c["F_in"], c["hp"], c["clip"], c["d"]
+    say(f"random trial {trial}: n={n} lo={lo} segs={L.n_segments} F={F_in} clip={clip} d={d} "
+        f"groups={c['groups']} hp={hp}")
+    sd = F.segments_to_device(segs)
+    seed = 5000 + trial
+    master0 = W.np_f32_normal([seed, 1], n, 0.02)
+    m0 = W.np_f32_normal([seed, 2], n, 1e-3)
+    v0 = (np.abs(W.np_f32_normal([seed, 3], n, 1e-3)) ** 2).astype(np.float32)
+    gm, gmm, gv = Guarded(master0), Guarded(m0), Guarded(v0)
+    flat = Guarded(np.zeros(n, np.uint16), pre=d)
+    om, omm, ov = master0.copy(), m0.copy(), v0.copy()
+    sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    prev = F.set_groups_per_wave(c["groups"])
+    try:
+        for t in (1, 2):
+            ohp = dict(hp)
+            kw = dict(step=t, segs=sd, n_segments=L.n_segments, flat=flat.window(),
+                      flat_index0=lo - d, lo=lo, **hp)
+            if F_in == -1:
+                grad = W.np_f32_normal([seed, 10 + t], n, 1e-2)
+                grad[~real] = np.nan
+                gdev = torch.from_numpy(grad).cuda()
+                if clip:
+                    F.grad_sumsq_shard(sumsq, grad=gdev, n=n, scale=hp["grad_scale"], segs=sd,
+                                       n_segments=L.n_segments)
+                    osum = OC.sumsq_exact(grad * np.float32(hp["grad_scale"]), real)
+                    ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                    kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
+                F.adamw_shard_step_f32grad(gm.data(), gmm.data(), gv.data(), gdev, **kw)
+                om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, grad, flags, ohp, t)
+            else:
+                contribs = [W.np_bf16_normal([seed, 20 + t, r], n, 1e-2) for r in range(F_in)]
+                for cb in contribs:
+                    cb[~real] = 0x7FC0
+                dev = [to_dev16(cb) for cb in contribs]
+                if clip:
+                    F.grad_sumsq_shard(sumsq, contribs=dev, n=n, scale=hp["grad_scale"],
+                                       segs=sd, n_segments=L.n_segments)
+                    osum = OC.grad_sumsq(contribs, real, hp["grad_scale"])
+                    ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                    kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
+                F.adamw_shard_step(gm.data(), gmm.data(), gv.data(), dev, **kw)
+                om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, ohp, t)
+            torch.cuda.synchronize()
+            assert_f32(gm.data_host(), om, f"master step {t}")
+            assert_f32(gmm.data_host(), omm, f"m step {t}")
+            assert_f32(gv.data_host(), ov, f"v step {t}")
+            assert_bf16(flat.data_host(), oout, f"bf16 step {t}")
+        for g, what in ((gm, "master"), (gmm, "m"), (gv, "v"), (flat, "flat window")):
+            g.assert_guards(what)
+    finally:
+        F.set_groups_per_wave(prev)
