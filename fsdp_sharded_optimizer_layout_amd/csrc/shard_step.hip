@@ -745,18 +745,19 @@ __global__ __launch_bounds__(kBlock) void sumsq_finish_kernel(SumsqParams p) {
 // ------------------------------------------------------------------------------------------------
 // Standalone reduce and unflatten: one 512-element group per wave.
 
-// Groups per wave of the reduce kernels (measured on MI355X: two groups per wave pay off only
-// when eight or more contribution streams are read; below that one group per wave is fastest).
-template <int F>
-constexpr int reduce_groups() { return F >= 8 ? 2 : 1; }
+// Groups per wave of the reduce kernels (measured on MI355X: two groups per wave pay off only for
+// the plain reduction of eight or more contribution streams; below that, and for the fp32
+// accumulation under the work-group cap, one group per wave is fastest).
+template <int F, bool ACC>
+constexpr int reduce_groups() { return F >= 8 && !ACC ? 2 : 1; }
 
 // ACC = false: out = scale * sum.  ACC = true: out = out + scale * sum (fp32 accumulation of
 // micro-batches; one rounding for the sum, one for the scale, one for the addition).
-// F >= 1 is a compile-time fan-in, F == 0 the run-time one; each wave owns reduce_groups<F>()
+// F >= 1 is a compile-time fan-in, F == 0 the run-time one; each wave owns reduce_groups<F, ACC>()
 // consecutive groups, and a complete tile issues all its loads before the first add.
 template <int F, bool ACC>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
-    constexpr int U = reduce_groups<F>();
+    constexpr int U = reduce_groups<F, ACC>();
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
@@ -1152,7 +1153,7 @@ int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, fl
     case FI:                                                                                    \
         k = accumulate ? reinterpret_cast<const void*>(&reduce_kernel<FI, true>)               \
                        : reinterpret_cast<const void*>(&reduce_kernel<FI, false>);             \
-        groups = reduce_groups<FI>();                                                           \
+        groups = accumulate ? reduce_groups<FI, true>() : reduce_groups<FI, false>();          \
         break;
         FSDPSHARD_REDUCE_CASE(1)
         FSDPSHARD_REDUCE_CASE(2)
@@ -1162,7 +1163,7 @@ int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, fl
         default:
             k = accumulate ? reinterpret_cast<const void*>(&reduce_kernel<0, true>)
                            : reinterpret_cast<const void*>(&reduce_kernel<0, false>);
-            groups = reduce_groups<0>();
+            groups = accumulate ? reduce_groups<0, true>() : reduce_groups<0, false>();
     }
     unsigned blocks = 0;
     rc = tile_grid(n, groups, &blocks);
