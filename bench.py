@@ -379,10 +379,14 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--groups-per-wave", type=int, default=0,
                     help="512-element groups per wavefront (1, 2, 4; 0 = library default)")
-    ap.add_argument("--path", choices=["fused", "clipped", "accumulate", "split", "reshard"],
+    ap.add_argument("--path", choices=["fused", "clipped", "clipped32", "accumulate", "split",
+                                       "reshard"],
                     default="fused",
                     help="fused: the fused step (default); clipped: sum of squares + clipped "
-                         "step; accumulate: fp32 micro-batch accumulation + clipped fp32 step; "
+                         "step; clipped32: reduction fused with the sum of squares into an fp32 "
+                         "shard + clipped fp32-gradient step; accumulate: fp32 micro-batch "
+                         "accumulation (the last fused with the sum of squares) + clipped fp32 "
+                         "step; "
                          "split: the step without its bf16 output, then unflatten_bf16; "
                          "reshard: move one destination rank's fp32 master/m/v to another "
                          "world size and padding multiple")
@@ -484,16 +488,31 @@ def main():
             stages.append(("adamw_shard_step (clipped)", lambda t: F.adamw_shard_step(
                 master, m, v, grads, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
                 **common), L.n_real * bpp))
+        elif args.path == "clipped32":
+            acc = torch.empty(n, dtype=torch.float32, device=dev)
+            stages.append(("reduce_shard_sumsq", lambda t: F.reduce_shard_sumsq(
+                grads, acc, sumsq, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
+                stream=stream), n * (2 * Fi + 4)))
+            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: F.adamw_shard_step_f32grad(
+                master, m, v, acc, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
+                **common), L.n_real * algorithmic_bytes_per_param_f32grad()))
         else:
             acc = torch.empty(n, dtype=torch.float32, device=dev)
             stages.append(("reduce_shard", lambda t: F.reduce_shard(grads, acc, stream=stream),
                            n * (2 * Fi + 4)))
-            for mb in range(1, args.micro_batches):
+            for mb in range(1, args.micro_batches - 1):
                 stages.append((f"reduce_shard_accumulate[{mb}]", lambda t: F.reduce_shard_accumulate(
                     grads, acc, stream=stream), n * (2 * Fi + 8)))
-            stages.append(("grad_sumsq_shard (fp32)", lambda t: F.grad_sumsq_shard(
-                sumsq, grad=acc, n=n, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
-                stream=stream), n * 4))
+            if args.micro_batches > 1:
+                stages.append((f"reduce_shard_sumsq (accumulate)[{args.micro_batches - 1}]",
+                               lambda t: F.reduce_shard_sumsq(
+                                   grads, acc, sumsq, accumulate=True, segs=segs_dev,
+                                   n_segments=L.n_segments, workspace=ws, stream=stream),
+                               n * (2 * Fi + 8)))
+            else:
+                stages.append(("grad_sumsq_shard (fp32)", lambda t: F.grad_sumsq_shard(
+                    sumsq, grad=acc, n=n, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
+                    stream=stream), n * 4))
             stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: F.adamw_shard_step_f32grad(
                 master, m, v, acc, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
                 **common), L.n_real * algorithmic_bytes_per_param_f32grad()))

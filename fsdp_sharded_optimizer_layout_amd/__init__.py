@@ -94,6 +94,8 @@ def lib():
     h.grad_sumsq_workspace_bytes.restype = c_i64
     h.grad_sumsq_shard.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_i64, c_vp, c_i32,
                                    ctypes.c_float, c_vp, c_i64, c_vp, c_vp]
+    h.reduce_shard_sumsq.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float, c_vp,
+                                     c_i32, c_vp, c_i32, c_vp, c_i64, c_vp, c_vp]
     h.reshard_plan.argtypes = [ctypes.POINTER(c_i64), c_i32, c_i64, c_i32, c_i64, c_i32, c_i32,
                                ctypes.POINTER(_Piece), c_i32, ctypes.POINTER(c_i32)]
     h.reshard_copy.argtypes = [ctypes.POINTER(c_vp), ctypes.POINTER(c_i64), c_i32, c_vp, c_i64,
@@ -334,6 +336,26 @@ def grad_sumsq_shard(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=No
         arr_p, fan_in, gp, n, _segs(segs, n_segments), int(n_segments), float(scale),
         _ptr(workspace, "workspace"), wbytes, _ptr(sumsq, "sumsq", {torch.float64}, 1),
         _stream(stream, sumsq)))
+
+
+def reduce_shard_sumsq(contribs, out, sumsq, accumulate=False, scale=1.0, n=None, segs=None,
+                       n_segments=0, workspace=None, stream=None):
+    """out = scale * sum (or out += scale * sum with ``accumulate``) over the contributions in
+    rank order, in float32, and ``sumsq`` (device float64) = sum over real elements of out**2.
+    ``workspace``: device tensor of at least grad_sumsq_workspace_bytes(n) bytes (allocated here
+    through PyTorch when omitted)."""
+    import torch
+    n = out.numel() if n is None else int(n)
+    need = grad_sumsq_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=sumsq.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    arr = _contrib_array(contribs, n)
+    _check("reduce_shard_sumsq", lib().reduce_shard_sumsq(
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n, float(scale),
+        _ptr(out, "out", {torch.float32}, n), 1 if accumulate else 0,
+        _segs(segs, n_segments), int(n_segments), _ptr(workspace, "workspace"), wbytes,
+        _ptr(sumsq, "sumsq", {torch.float64}, 1), _stream(stream, out)))
 
 
 def unflatten_bf16(master, flat, flat_index0=0, lo=0, segs=None, n_segments=0, n=None,

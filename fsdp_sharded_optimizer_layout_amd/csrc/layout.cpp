@@ -236,7 +236,7 @@ extern "C" const char* fsdpshard_strerror(int code) {
         case FSDPSHARD_OK: return "ok";
         case FSDPSHARD_ERR_INVALID_ARG: return "invalid argument";
         case FSDPSHARD_ERR_OVERFLOW: return "integer overflow in the flat layout";
-        case FSDPSHARD_ERR_CAPACITY: return "segment array too small";
+        case FSDPSHARD_ERR_CAPACITY: return "output array or workspace too small";
         case FSDPSHARD_ERR_ALIGNMENT: return "misaligned pointer";
         case FSDPSHARD_ERR_UNSUPPORTED: return "unsupported fan-in";
         case FSDPSHARD_ERR_HIP: return "HIP runtime error";

@@ -603,28 +603,38 @@ constexpr int64_t kSumsqGroups = 16;
 template <int F>
 constexpr int sumsq_batch() { return F == -1 ? 8 : 1; }
 
-// One group's squares for this lane: the 8 elements, padding and elements past the slice left
-// out, added as a fixed pairwise tree and then into the lane's running sum.
-__device__ __forceinline__ void square_group(const SumsqParams& p, SegCursor& cur, int64_t gb,
-                                             int64_t nvec, int lane, const float (&g)[kVec],
-                                             int cnt, double& acc) {
+// One group's squares for this lane: the 8 float32 values x, padding and elements past the slice
+// (n elements) left out, each squared in float64 (exact) and added as a fixed pairwise tree, then
+// into the lane's running sum.
+__device__ __forceinline__ void add_squares(SegCursor& cur, int64_t n, int64_t gb, int64_t nvec,
+                                            int lane, const float (&x)[kVec], int cnt,
+                                            double& acc) {
     int64_t gend = gb + kWave;
     if (gend > nvec) gend = nvec;
     cur.seek(gb * kVec);
     const int64_t e0 = (gb + lane) * kVec;
     uint32_t fl[kVec];
     int64_t g1 = gend * kVec;
-    if (g1 > p.n) g1 = p.n;
+    if (g1 > n) g1 = n;
     element_flags(cur, g1, e0, fl);
     double q[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-        const float gs = g[e] * p.scale;
-        const double d = static_cast<double>(gs);
+        const double d = static_cast<double>(x[e]);
         const bool use = e < cnt && (fl[e] & FSDPSHARD_SEG_PADDING) == 0u;
         q[e] = use ? d * d : 0.0;
     }
     acc += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+}
+
+// The sum of squares of scale * g for one group.
+__device__ __forceinline__ void square_group(const SumsqParams& p, SegCursor& cur, int64_t gb,
+                                             int64_t nvec, int lane, const float (&g)[kVec],
+                                             int cnt, double& acc) {
+    float gs[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) gs[e] = g[e] * p.scale;
+    add_squares(cur, p.n, gb, nvec, lane, gs, cnt, acc);
 }
 
 template <int F>
@@ -739,6 +749,103 @@ __global__ __launch_bounds__(kBlock) void sumsq_finish_kernel(SumsqParams p) {
 #pragma unroll
         for (int w = 1; w < kWavesPerBlock; ++w) b += wave_part[w];
         *p.result = b;
+    }
+}
+
+// Reduction into an fp32 shard fused with that shard's sum of squares: out = scale * sum (or
+// out + scale * sum when ACC), exactly as reduce_kernel computes it, and one float64 partial per
+// work-group of the sum of out^2 over the real elements, added in the same fixed order as
+// sumsq_kernel (each work-group covers kSumsqGroups groups per wave, so the partials fill the
+// same workspace).  Whole tiles take a straight-line path; the slice's last tile and run-time
+// fan-ins take the bounds-checked path.
+struct ReduceSqParams {
+    const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
+    float* out;
+    const fsdpshard_segment* segs;
+    double* partials;
+    int64_t n;
+    int32_t n_segs;
+    int32_t fan_in;
+    float scale;
+};
+
+template <int F, bool ACC>
+__global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) {
+    __shared__ double wave_part[kWavesPerBlock];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int64_t nvec = (p.n + kVec - 1) / kVec;
+    const int64_t tile = tile_index<1>();
+    const int64_t base0 = (tile * kWavesPerBlock + wave) * (kWave * kSumsqGroups);
+    double sq = 0.0;
+    if (base0 < nvec) {
+        SegCursor cur;
+        cur.init(p.segs, p.n_segs, base0 * kVec);
+        bool done = false;
+        if constexpr (F > 0) {
+            if (base0 + kSumsqGroups * kWave <= p.n / kVec) {
+                for (int g0 = 0; g0 < kSumsqGroups; ++g0) {
+                    const int64_t gb = base0 + g0 * kWave;
+                    const int64_t e0 = (gb + lane) * kVec;
+                    uint4 raw[F];
+                    float acc[kVec];
+                    if constexpr (ACC) load8(p.out + e0, true, kVec, acc);
+#pragma unroll
+                    for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
+                    float g[kVec];
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < F; ++r) accumulate(g, raw[r]);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        g[e] = g[e] * p.scale;
+                        if constexpr (ACC) g[e] = acc[e] + g[e];
+                    }
+                    store8(p.out + e0, true, kVec, g);
+                    add_squares(cur, p.n, gb, nvec, lane, g, kVec, sq);
+                }
+                done = true;
+            }
+        }
+        if (!done) {
+            for (int g0 = 0; g0 < kSumsqGroups; ++g0) {
+                const int64_t gb = base0 + g0 * kWave;
+                if (gb >= nvec) break;
+                const int64_t e0 = (gb + lane) * kVec;
+                const int64_t left = p.n - e0;
+                const int cnt = left <= 0 ? 0 : static_cast<int>(left < kVec ? left : kVec);
+                const bool full = cnt == kVec;
+                float g[kVec];
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+                if (cnt > 0) {
+                    float acc[kVec];
+                    if constexpr (ACC) load8(p.out + e0, full, cnt, acc);
+                    for (int r = 0; r < p.fan_in; ++r) {
+                        const uint4 q = full ? ld_u4_nt(p.contrib[r] + e0)
+                                             : ld_u4_partial(p.contrib[r] + e0, cnt);
+                        accumulate(g, q);
+                    }
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        g[e] = g[e] * p.scale;
+                        if constexpr (ACC) g[e] = acc[e] + g[e];
+                    }
+                    store8(p.out + e0, full, cnt, g);
+                }
+                add_squares(cur, p.n, gb, nvec, lane, g, cnt, sq);
+            }
+        }
+    }
+    sq = wave_sum(sq);
+    if (lane == 0) wave_part[wave] = sq;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double b = wave_part[0];
+#pragma unroll
+        for (int w = 1; w < kWavesPerBlock; ++w) b += wave_part[w];
+        p.partials[tile] = b;
     }
 }
 
@@ -952,6 +1059,8 @@ constexpr int step_groups_per_cu(int fan_in) {
 }
 constexpr int kReduceGroupsPerCU = 2;
 constexpr int kReduceOneStreamGroupsPerCU = 4;
+constexpr int kReduceSqGroupsPerCU = 2;
+constexpr int kReduceOneStreamSqGroupsPerCU = 3;
 constexpr int kMaxDevices = 64;
 std::atomic<int64_t> g_lds_per_cu[kMaxDevices];   // 0: not queried yet; -1: unknown
 
@@ -1267,6 +1376,79 @@ extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
     }
     // One work-group adds the partials (or writes +0 for an empty slice).
     return launch(reinterpret_cast<const void*>(&sumsq_finish_kernel), 1, &p, stream);
+}
+
+extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                                 float scale, float* out, int32_t accumulate,
+                                 const fsdpshard_segment* segs, int32_t n_segments,
+                                 void* workspace, int64_t workspace_bytes, double* sumsq,
+                                 void* stream) {
+    if (out == nullptr || n < 0 || sumsq == nullptr || n_segments < 0 ||
+        (n_segments > 0 && segs == nullptr) || (accumulate != 0 && accumulate != 1))
+        return FSDPSHARD_ERR_INVALID_ARG;
+    int rc = check_contribs(contribs, fan_in, n);
+    if (rc != FSDPSHARD_OK) return rc;
+    if (!aligned16(out)) return FSDPSHARD_ERR_ALIGNMENT;
+    if ((reinterpret_cast<uintptr_t>(sumsq) & 7u) != 0) return FSDPSHARD_ERR_ALIGNMENT;
+    if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
+        return FSDPSHARD_ERR_ALIGNMENT;
+    if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
+    const int64_t parts = sumsq_partials(n);
+    if (parts > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
+    const int64_t need = parts * static_cast<int64_t>(sizeof(double));
+    if (parts > 0 && (workspace == nullptr || workspace_bytes < need)) return FSDPSHARD_ERR_CAPACITY;
+    if (parts > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+        return FSDPSHARD_ERR_ALIGNMENT;
+    for (int r = 0; r < fan_in && n > 0; ++r)
+        if (overlaps(out, n * 4, contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+    if (n > 0 && overlaps(out, n * 4, sumsq, 8)) return FSDPSHARD_ERR_INVALID_ARG;
+    if (parts > 0 && (overlaps(workspace, need, sumsq, 8) || overlaps(workspace, need, out, n * 4)))
+        return FSDPSHARD_ERR_INVALID_ARG;
+    ReduceSqParams p;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
+    p.out = out;
+    p.segs = segs;
+    p.partials = static_cast<double*>(workspace);
+    p.n = n;
+    p.n_segs = segs == nullptr ? 0 : n_segments;
+    p.fan_in = fan_in;
+    p.scale = scale;
+    if (parts > 0) {
+        const bool acc = accumulate != 0;
+        const void* k = nullptr;
+        switch (fan_in) {
+#define FSDPSHARD_REDUCE_SQ_CASE(FI)                                                            \
+    case FI:                                                                                    \
+        k = acc ? reinterpret_cast<const void*>(&reduce_sumsq_kernel<FI, true>)                \
+                : reinterpret_cast<const void*>(&reduce_sumsq_kernel<FI, false>);              \
+        break;
+            FSDPSHARD_REDUCE_SQ_CASE(1)
+            FSDPSHARD_REDUCE_SQ_CASE(2)
+            FSDPSHARD_REDUCE_SQ_CASE(4)
+            FSDPSHARD_REDUCE_SQ_CASE(8)
+#undef FSDPSHARD_REDUCE_SQ_CASE
+            default:
+                k = acc ? reinterpret_cast<const void*>(&reduce_sumsq_kernel<0, true>)
+                        : reinterpret_cast<const void*>(&reduce_sumsq_kernel<0, false>);
+        }
+        rc = launch(k, static_cast<unsigned>(parts), &p, stream,
+                    fan_in == 1 && !acc ? kReduceOneStreamSqGroupsPerCU : kReduceSqGroupsPerCU);
+        if (rc != FSDPSHARD_OK) return rc;
+    }
+    SumsqParams f;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) f.contrib[r] = nullptr;
+    f.grad32 = nullptr;
+    f.segs = nullptr;
+    f.partials = static_cast<double*>(workspace);
+    f.result = sumsq;
+    f.n = n;
+    f.groups_per_wave = kSumsqGroups;
+    f.n_segs = 0;
+    f.fan_in = 0;
+    f.n_partials = static_cast<int32_t>(parts);
+    f.scale = 1.0f;
+    // One work-group adds the partials (or writes +0 for an empty slice).
+    return launch(reinterpret_cast<const void*>(&sumsq_finish_kernel), 1, &f, stream);
 }
 
 extern "C" int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs,

@@ -34,7 +34,7 @@ typedef enum fsdpshard_status {
     FSDPSHARD_OK = 0,
     FSDPSHARD_ERR_INVALID_ARG = 1,  /* null pointer, negative size, rank >= world, overlap, ... */
     FSDPSHARD_ERR_OVERFLOW = 2,     /* a flat offset, P, or k*P does not fit the int64 range */
-    FSDPSHARD_ERR_CAPACITY = 3,     /* segment array too small; the layout reports the count */
+    FSDPSHARD_ERR_CAPACITY = 3,     /* a caller array (segments, pieces) or workspace too small */
     FSDPSHARD_ERR_ALIGNMENT = 4,    /* an fp32 or gradient pointer is not 16-byte aligned, ... */
     FSDPSHARD_ERR_UNSUPPORTED = 5,  /* fan_in above FSDPSHARD_MAX_FAN_IN */
     FSDPSHARD_ERR_HIP = 6           /* the HIP runtime refused a query or the kernel launch */
@@ -234,6 +234,29 @@ int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in, const floa
 int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs,
                    int32_t n_segments, uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
                    void* stream);
+
+/*
+ * reduce_shard_sumsq -- reduce_shard (accumulate == 0) or reduce_shard_accumulate
+ * (accumulate == 1) into the fp32 shard `out`, fused with the sum of squares of the result:
+ *   *sumsq = sum over real elements i of (double)out[i]^2   (float64, fixed order)
+ *
+ * [FSDP], gradient clipping passage (each rank contributes its part of the squared global norm;
+ * see grad_sumsq_shard) and mixed-precision passage (float32 gradient shards).  With a large
+ * fan-in this reads the contributions once: the reduction plus the fp32-gradient step move
+ * 2F + 4 + 30 bytes per parameter against 2F + 26 + 2F for grad_sumsq_shard plus the fused step.
+ * After the last micro-batch (accumulate == 1) it yields the norm of the accumulated gradient.
+ *   contribs, fan_in, n, scale, out   as reduce_shard; out also receives padding positions
+ *                                      (their values are whatever the reduction gives)
+ *   segs, n_segments   device segment table of the slice (padding does not count), or NULL/0
+ *   workspace          device, >= grad_sumsq_workspace_bytes(n) bytes, 8-byte aligned
+ *   sumsq              device, one double, receives this rank's part (+0 when n == 0)
+ * Errors: INVALID_ARG (nulls, overlaps, accumulate not 0 or 1), ALIGNMENT, UNSUPPORTED,
+ *         CAPACITY (workspace too small), OVERFLOW, HIP.
+ */
+int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_in, int64_t n, float scale,
+                       float* out, int32_t accumulate, const fsdpshard_segment* segs,
+                       int32_t n_segments, void* workspace, int64_t workspace_bytes, double* sumsq,
+                       void* stream);
 
 /*
  * One piece of a reshard plan: `length` elements that land at `dst_offset` of the destination

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert F.abi_version() == 1
-    assert F.strerror(CAPACITY) == "segment array too small"
+    assert F.strerror(CAPACITY) == "output array or workspace too small"
 
 
 def _oracle_segments(sizes, pad, wd, N, k):
@@ -274,6 +274,29 @@ def test_sumsq_validation_and_workspace():
     assert f(None, 0, g + 8, 100, None, 0, 1.0, ws, 8, res, None) == ALIGN
     assert f(arr, 2, None, -1, None, 0, 1.0, ws, 8, res, None) == INVALID
     assert f(arr, 2, None, 100, None, 0, 1.0, ws, 8, ws, None) == INVALID          # overlap
+
+
+def test_reduce_sumsq_validation():
+    # Every error is reported before anything is launched (fake device addresses are never
+    # dereferenced).
+    lib = F.lib()
+    arr = (ctypes.c_void_p * 2)(_Fake.at(3), _Fake.at(4))
+    out, ws, res = _Fake.at(10), _Fake.at(7), _Fake.at(8)
+    f = lib.reduce_shard_sumsq
+    assert f(arr, 2, 100, 1.0, out, 0, None, 0, ws, 0, res, None) == CAPACITY
+    assert f(arr, 2, 100, 1.0, out, 0, None, 0, None, 8, res, None) == CAPACITY
+    assert f(arr, 2, 100, 1.0, None, 0, None, 0, ws, 8, res, None) == INVALID
+    assert f(arr, 2, 100, 1.0, out, 2, None, 0, ws, 8, res, None) == INVALID   # accumulate 0/1
+    assert f(arr, 2, 100, 1.0, out, 0, None, 3, ws, 8, res, None) == INVALID   # segs missing
+    assert f(arr, 2, 100, 1.0, out, 0, None, 0, ws, 8, None, None) == INVALID
+    assert f(arr, 2, 100, 1.0, out + 8, 0, None, 0, ws, 8, res, None) == ALIGN
+    assert f(arr, 2, 100, 1.0, out, 0, None, 0, ws, 8, res + 4, None) == ALIGN
+    assert f(arr, 2, 100, 1.0, out, 0, None, 0, ws + 4, 8, res, None) == ALIGN
+    assert f(arr, 0, 100, 1.0, out, 0, None, 0, ws, 8, res, None) == INVALID
+    assert f(arr, 65, 100, 1.0, out, 0, None, 0, ws, 8, res, None) == UNSUP
+    assert f(arr, 2, -1, 1.0, out, 0, None, 0, ws, 8, res, None) == INVALID
+    assert f(arr, 2, 100, 1.0, out, 0, None, 0, ws, 8, out, None) == INVALID       # overlap
+    assert f(arr, 2, 100, 1.0, out, 0, None, 0, out, 8, res, None) == INVALID      # overlap
 
 
 # ---------------------------------------------------------------------------------- reshard plan

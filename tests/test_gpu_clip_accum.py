@@ -278,3 +278,84 @@ def test_sumsq_full_slice_parts_add_up(name):
     assert math.isfinite(whole) and whole > 0
     del grads
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n,F_in,acc", [(1, 1, False), (7, 3, True), (32768, 8, False),
+                                        (32769, 8, True), (65539, 2, True), (300_017, 5, False),
+                                        (1_000_003, 1, True), (2_500_001, 4, False)])
+def test_reduce_sumsq_matches_oracle(n, F_in, acc):
+    # The fp32 shard equals the plain reduction (or accumulation) bit for bit; the sum of squares
+    # of that shard matches the oracle's exact sum; the sum is bit-identical when repeated.
+    say(f"reduce+sumsq n={n} F={F_in} accumulate={acc}")
+    contribs = [W.np_bf16_normal([70, r], n, 1e-2) for r in range(F_in)]
+    dev = [to_dev16(c) for c in contribs]
+    acc0 = W.np_f32_normal([71, n], n, 1e-3) if acc else np.full(n, np.nan, np.float32)
+    out = Guarded(acc0)
+    res = torch.full((2,), float("nan"), dtype=torch.float64, device="cuda")
+    F.reduce_shard_sumsq(dev, out.data(), res[:1], accumulate=acc, scale=0.5)
+    torch.cuda.synchronize()
+    want = OS.accumulate_fp32(acc0, contribs, 0.5) if acc else OS.reduce_contributions(contribs, 0.5)
+    assert bit_equal(out.data_host(), want)
+    out.assert_guards("out")
+    h = res.cpu().numpy()
+    assert np.isnan(h[1])
+    osum = OC.sumsq_exact(want)
+    assert abs(h[0] - osum) <= SUMSQ_RTOL * osum, (h[0], osum)
+    if not acc:
+        F.reduce_shard_sumsq(dev, out.data(), res[:1], scale=0.5)
+        torch.cuda.synchronize()
+        assert res.cpu().numpy()[0] == h[0]
+        # The fused sum agrees with grad_sumsq_shard over the same fp32 shard.
+        assert abs(_gpu_sumsq(grad=out.data(), n=n) - h[0]) <= SUMSQ_RTOL * osum
+
+
+@pytest.mark.parametrize("F_in", [1, 4, 8, 3])
+def test_microbatches_with_fused_norm_then_clipped_step(F_in):
+    # Three micro-batches: reduce, accumulate, then accumulate fused with the sum of squares; the
+    # clipped fp32-gradient step uses that norm.  Padding (NaN contributions) never counts.
+    sizes = [(i * 7919) % 3001 + 1 for i in range(300)]
+    L, segs, flags = _layout(sizes, 16, [i % 3 != 0 for i in range(300)], 2, 1)
+    n = L.n
+    real = (flags & OL.PADDING) == 0
+    sd = F.segments_to_device(segs)
+    say(f"micro-batches + fused norm F={F_in} n={n} segments={L.n_segments}")
+    mbs = []
+    for mb in range(3):
+        cs = [W.np_bf16_normal([72, mb, r], n, 1e-2) for r in range(F_in)]
+        for c in cs:
+            c[~real] = 0x7FC0
+        mbs.append(cs)
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    res = torch.zeros(1, dtype=torch.float64, device="cuda")
+    F.reduce_shard([to_dev16(c) for c in mbs[0]], acc)
+    F.reduce_shard_accumulate([to_dev16(c) for c in mbs[1]], acc)
+    F.reduce_shard_sumsq([to_dev16(c) for c in mbs[2]], acc, res, accumulate=True, segs=sd,
+                         n_segments=L.n_segments)
+    oacc = OS.reduce_contributions(mbs[0])
+    oacc = OS.accumulate_fp32(oacc, mbs[1])
+    oacc = OS.accumulate_fp32(oacc, mbs[2])
+    torch.cuda.synchronize()
+    got_acc = acc.cpu().numpy()
+    assert bit_equal(got_acc[real], oacc[real])
+    osum = OC.sumsq_exact(oacc, real)
+    total = float(res.cpu().numpy()[0])
+    assert abs(total - osum) <= SUMSQ_RTOL * osum
+    master = W.np_f32_normal([73, 1], n, 0.02)
+    st = [Guarded(master), Guarded(np.zeros(n, np.float32)), Guarded(np.zeros(n, np.float32))]
+    flat = Guarded(np.zeros(n, np.uint16))
+    max_norm = 0.05
+    F.adamw_shard_step_f32grad(st[0].data(), st[1].data(), st[2].data(), acc, step=1, segs=sd,
+                               n_segments=L.n_segments, flat=flat.window(), flat_index0=L.lo,
+                               lo=L.lo, max_grad_norm=max_norm, grad_sumsq=res, **HP)
+    torch.cuda.synchronize()
+    scale = OC.clipped_scale(osum, max_norm)
+    assert scale < 1.0                                   # the clip is active in this case
+    om, omm, ov, oout = OS.shard_step_f32grad(master, np.zeros(n, np.float32),
+                                              np.zeros(n, np.float32), oacc, flags,
+                                              dict(HP, grad_scale=float(scale)), 1)
+    assert_f32(st[0].data_host(), om, "master")
+    assert_f32(st[1].data_host(), omm, "m")
+    assert_f32(st[2].data_host(), ov, "v")
+    assert_bf16(flat.data_host(), oout, "flat")
+    for g, what in zip(st + [flat], ("master", "m", "v", "flat")):
+        g.assert_guards(what)
