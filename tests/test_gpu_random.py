@@ -3,8 +3,9 @@
 Each trial draws a whole case from a seeded generator: tensor sizes and padding multiple, world
 size and rank, per-tensor weight-decay mask, fan-in (compile-time and run-time fan-ins up to 64)
 or an fp32 gradient shard, AdamW hyperparameters, gradient scale, clipping by the global norm
-(the squared norm taken on the GPU, as a caller would), the bf16 window's phase and the groups
-per wave.  Two steps per trial; fp32 state within relative 1e-5, bf16 within 1 ulp, NaN padding
+(the squared norm taken on the GPU, as a caller would; with bf16 contributions either from the
+contributions or from the fp32 shard that reduce_shard_sumsq writes), the bf16 window's phase and
+the groups per wave.  Two steps per trial; fp32 state within relative 1e-5, bf16 within 1 ulp, NaN padding
 gradients ignored, guard bands intact.
 """
 
@@ -93,6 +94,23 @@ def test_random_fused_steps(trial):
                 for cb in contribs:
                     cb[~real] = 0x7FC0
                 dev = [to_dev16(cb) for cb in contribs]
+                if clip and trial % 2:
+                    # Reduce once into an fp32 shard with its norm, then the fp32-gradient step.
+                    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+                    F.reduce_shard_sumsq(dev, acc, sumsq, scale=hp["grad_scale"], segs=sd,
+                                         n_segments=L.n_segments)
+                    ograd = OS.reduce_contributions(contribs, hp["grad_scale"])
+                    osum = OC.sumsq_exact(ograd, real)
+                    ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, 1.0))
+                    kw.update(max_grad_norm=clip, grad_sumsq=sumsq, grad_scale=1.0)
+                    F.adamw_shard_step_f32grad(gm.data(), gmm.data(), gv.data(), acc, **kw)
+                    om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, ograd, flags, ohp, t)
+                    torch.cuda.synchronize()
+                    assert_f32(gm.data_host(), om, f"master step {t}")
+                    assert_f32(gmm.data_host(), omm, f"m step {t}")
+                    assert_f32(gv.data_host(), ov, f"v step {t}")
+                    assert_bf16(flat.data_host(), oout, f"bf16 step {t}")
+                    continue
                 if clip:
                     F.grad_sumsq_shard(sumsq, contribs=dev, n=n, scale=hp["grad_scale"],
                                        segs=sd, n_segments=L.n_segments)
