@@ -22,6 +22,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfsdpshard.so")
 MAX_FAN_IN = 64
+STATE_BLOCK = 512          # elements per block of the blocked state layout
 SEG_WEIGHT_DECAY = 1
 SEG_PADDING = 2
 
@@ -88,6 +89,15 @@ def lib():
     h.unflatten_bf16.argtypes = [c_vp, c_i64, c_vp, c_i32, c_vp, c_i64, c_i64, c_vp]
     h.adamw_shard_step_f32grad.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32,
                                            ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64, c_vp]
+    h.state_blocked_elems.argtypes = [c_i64]
+    h.state_blocked_elems.restype = c_i64
+    h.adamw_shard_step_blocked.argtypes = [c_vp, ctypes.POINTER(c_vp), c_i32, c_i64, c_vp, c_i32,
+                                           ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64, c_vp]
+    h.adamw_shard_step_f32grad_blocked.argtypes = [c_vp, c_vp, c_i64, c_vp, c_i32,
+                                                   ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64,
+                                                   c_vp]
+    h.state_to_blocked.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp]
+    h.state_from_blocked.argtypes = [c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]
     h.reduce_shard_accumulate.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float,
                                           c_vp, c_vp]
     h.grad_sumsq_workspace_bytes.argtypes = [c_i64]
@@ -295,6 +305,69 @@ def adamw_shard_step_f32grad(master, m, v, grad, step, lr, beta1=0.9, beta2=0.99
         _ptr(master, "master", f32, n), _ptr(m, "m", f32, n), _ptr(v, "v", f32, n),
         _ptr(grad, "grad", f32, n), n, _segs(segs, n_segments), int(n_segments), ctypes.byref(hp),
         _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, master)))
+
+
+def state_blocked_elems(n):
+    """Floats in the blocked state array of an n-element slice (STATE_BLOCK-element blocks of
+    master, then m, then v)."""
+    v = int(lib().state_blocked_elems(int(n)))
+    if v < 0:
+        raise ValueError(f"slice length {n} out of range")
+    return v
+
+
+def adamw_shard_step_blocked(state, contribs, step, lr, n, beta1=0.9, beta2=0.999, eps=1e-8,
+                             weight_decay=0.0, grad_scale=1.0, segs=None, n_segments=0, flat=None,
+                             flat_index0=0, lo=0, max_grad_norm=0.0, grad_sumsq=None,
+                             stream=None):
+    """adamw_shard_step with the state of the n-element slice in the blocked layout."""
+    import torch
+    n = int(n)
+    arr = _contrib_array(contribs, n)
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay, grad_scale, max_grad_norm, grad_sumsq)
+    if flat is not None and not isinstance(flat, int):
+        _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
+    _check("adamw_shard_step_blocked", lib().adamw_shard_step_blocked(
+        _ptr(state, "state", {torch.float32}, state_blocked_elems(n)),
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n,
+        _segs(segs, n_segments), int(n_segments), ctypes.byref(hp),
+        _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, state)))
+
+
+def adamw_shard_step_f32grad_blocked(state, grad, step, lr, n, beta1=0.9, beta2=0.999, eps=1e-8,
+                                     weight_decay=0.0, grad_scale=1.0, segs=None, n_segments=0,
+                                     flat=None, flat_index0=0, lo=0, max_grad_norm=0.0,
+                                     grad_sumsq=None, stream=None):
+    """adamw_shard_step_f32grad with the state of the n-element slice in the blocked layout."""
+    import torch
+    n = int(n)
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay, grad_scale, max_grad_norm, grad_sumsq)
+    if flat is not None and not isinstance(flat, int):
+        _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
+    _check("adamw_shard_step_f32grad_blocked", lib().adamw_shard_step_f32grad_blocked(
+        _ptr(state, "state", {torch.float32}, state_blocked_elems(n)),
+        _ptr(grad, "grad", {torch.float32}, n), n, _segs(segs, n_segments), int(n_segments),
+        ctypes.byref(hp), _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, state)))
+
+
+def state_to_blocked(master, m, v, state, n=None, stream=None):
+    """Copy the separate master / m / v arrays of an n-element slice into the blocked array."""
+    import torch
+    n = master.numel() if n is None else int(n)
+    f32 = {torch.float32}
+    _check("state_to_blocked", lib().state_to_blocked(
+        _ptr(master, "master", f32, n), _ptr(m, "m", f32, n), _ptr(v, "v", f32, n), n,
+        _ptr(state, "state", f32, state_blocked_elems(n)), _stream(stream, state)))
+
+
+def state_from_blocked(state, master, m, v, n=None, stream=None):
+    """Copy the blocked array of an n-element slice back into separate master / m / v arrays."""
+    import torch
+    n = master.numel() if n is None else int(n)
+    f32 = {torch.float32}
+    _check("state_from_blocked", lib().state_from_blocked(
+        _ptr(state, "state", f32, state_blocked_elems(n)), n, _ptr(master, "master", f32, n),
+        _ptr(m, "m", f32, n), _ptr(v, "v", f32, n), _stream(stream, state)))
 
 
 def reduce_shard_accumulate(contribs, acc, scale=1.0, n=None, stream=None):

@@ -418,7 +418,22 @@ __device__ __forceinline__ void pack_out(const uint32_t (&fl)[kVec], const float
 
 // One 512-element group with per-lane bounds: the slice's last, partial group, and every group
 // of the run-time fan-in kernel.  TAIL = false drops the bounds for complete groups.
-template <int F, bool OUT, bool TAIL>
+// Where element e0 (a multiple of 8) of state array k (0 master, 1 m, 2 v) lives.  Separate
+// layout: three arrays.  Blocked layout: one array in which each block of kStateBlock slice
+// elements holds that block's masters, then its m, then its v (an 8-element vector never
+// straddles a block).
+constexpr int64_t kStateBlock = FSDPSHARD_STATE_BLOCK;
+
+template <bool BLK>
+__device__ __forceinline__ float* state_ptr(const StepParams& p, int k, int64_t e0) {
+    if constexpr (BLK) {
+        return p.master + ((e0 / kStateBlock) * 3 + k) * kStateBlock + e0 % kStateBlock;
+    } else {
+        return k == 0 ? p.master + e0 : (k == 1 ? p.m + e0 : p.v + e0);
+    }
+}
+
+template <int F, bool OUT, bool TAIL, bool BLK>
 __device__ __forceinline__ void step_group(const StepParams& p, float scale, const SegCursor& cur,
                                            int64_t vec, int64_t group_end_vec, int lane) {
     const int64_t n = p.n;
@@ -432,9 +447,9 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
     uint4 raw[F > 0 ? F : 1];
     if (valid) {
         load_grad<F>(p, e0, full, cnt, raw, gf);
-        load8(p.master + e0, full, cnt, th);
-        load8(p.m + e0, full, cnt, mm);
-        load8(p.v + e0, full, cnt, vv);
+        load8(state_ptr<BLK>(p, 0, e0), full, cnt, th);
+        load8(state_ptr<BLK>(p, 1, e0), full, cnt, mm);
+        load8(state_ptr<BLK>(p, 2, e0), full, cnt, vv);
         sum_grad<F>(p, e0, full, cnt, raw, gf, g);
     } else {
 #pragma unroll
@@ -448,9 +463,9 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
     adam8(p, scale, fl, g, th, mm, vv);
 
     if (valid) {
-        store8(p.master + e0, full, cnt, th);
-        store8(p.m + e0, full, cnt, mm);
-        store8(p.v + e0, full, cnt, vv);
+        store8(state_ptr<BLK>(p, 0, e0), full, cnt, th);
+        store8(state_ptr<BLK>(p, 1, e0), full, cnt, mm);
+        store8(state_ptr<BLK>(p, 2, e0), full, cnt, vv);
     }
     if constexpr (OUT) {
         uint32_t w[4];
@@ -466,7 +481,7 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
 // A wave's whole tile of U complete groups (compile-time gradient source F >= 1 or F == -1):
 // every HBM load of the tile is issued first (gradients non-temporal), then the segment cursor is
 // placed, then each group is reduced, updated and stored.
-template <int F, bool OUT, int U>
+template <int F, bool OUT, int U, bool BLK>
 __device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, int lane) {
     uint4 raw[U][F > 0 ? F : 1];
     float gf[U][kVec], th[U][kVec], mm[U][kVec], vv[U][kVec];
@@ -477,18 +492,18 @@ __device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, in
     for (int u = 0; u < U; ++u) {
         const int64_t e0 = (base0 + u * kWave + lane) * kVec;
         if constexpr (F == 1 || F == -1) {
-            load8(p.master + e0, true, kVec, th[u]);
-            load8(p.m + e0, true, kVec, mm[u]);
-            load8(p.v + e0, true, kVec, vv[u]);
+            load8(state_ptr<BLK>(p, 0, e0), true, kVec, th[u]);
+            load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm[u]);
+            load8(state_ptr<BLK>(p, 2, e0), true, kVec, vv[u]);
             __builtin_amdgcn_sched_barrier(0);
             load_grad<F>(p, e0, true, kVec, raw[u], gf[u]);
         } else {
-            load8(p.master + e0, true, kVec, th[u]);
-            load8(p.m + e0, true, kVec, mm[u]);
+            load8(state_ptr<BLK>(p, 0, e0), true, kVec, th[u]);
+            load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm[u]);
             __builtin_amdgcn_sched_barrier(0);
             load_grad<F>(p, e0, true, kVec, raw[u], gf[u]);
             __builtin_amdgcn_sched_barrier(0);
-            load8(p.v + e0, true, kVec, vv[u]);
+            load8(state_ptr<BLK>(p, 2, e0), true, kVec, vv[u]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -505,9 +520,9 @@ __device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, in
         float g[kVec];
         sum_grad<F>(p, e0, true, kVec, raw[u], gf[u], g);
         adam8(p, scale, fl, g, th[u], mm[u], vv[u]);
-        store8(p.master + e0, true, kVec, th[u]);
-        store8(p.m + e0, true, kVec, mm[u]);
-        store8(p.v + e0, true, kVec, vv[u]);
+        store8(state_ptr<BLK>(p, 0, e0), true, kVec, th[u]);
+        store8(state_ptr<BLK>(p, 1, e0), true, kVec, mm[u]);
+        store8(state_ptr<BLK>(p, 2, e0), true, kVec, vv[u]);
         if constexpr (OUT) {
             uint32_t w[4];
             pack_out(fl, th[u], w);
@@ -549,7 +564,7 @@ __device__ __forceinline__ int64_t tile_base(int wave, int groups) {
     return (tile_index<Run>() * kWavesPerBlock + wave) * (kWave * groups);
 }
 
-template <int F, bool OUT, int U>
+template <int F, bool OUT, int U, bool BLK>
 __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
@@ -558,7 +573,7 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     if (base0 >= nvec) return;
     if constexpr (F != 0) {
         if (base0 + kWave * U <= p.n / kVec) {
-            step_tile<F, OUT, U>(p, base0, lane);
+            step_tile<F, OUT, U, BLK>(p, base0, lane);
             return;
         }
     }
@@ -572,9 +587,9 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
         if (gend > nvec) gend = nvec;
         cur.seek(gb * kVec);
         if (gend == gb + kWave && gend * kVec <= p.n)
-            step_group<F, OUT, false>(p, scale, cur, gb + lane, gend, lane);
+            step_group<F, OUT, false, BLK>(p, scale, cur, gb + lane, gend, lane);
         else
-            step_group<F, OUT, true>(p, scale, cur, gb + lane, gend, lane);
+            step_group<F, OUT, true, BLK>(p, scale, cur, gb + lane, gend, lane);
     }
 }
 
@@ -1021,6 +1036,37 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
                                     __float_as_uint(st[2][1]), x));
 }
 
+// Conversion between the separate state arrays and the blocked state array (plain copies).
+struct StatePackParams {
+    float* sep[3];           // master, m, v
+    float* blocked;
+    int64_t n;
+};
+
+template <bool TO_BLOCKED>
+__global__ __launch_bounds__(kBlock) void state_pack_kernel(StatePackParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int64_t vec = tile_base(wave, 1) + lane;
+    const int64_t e0 = vec * kVec;
+    if (e0 >= p.n) return;
+    const int cnt = static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec);
+    const bool full = cnt == kVec;
+    const int64_t b0 = ((e0 / kStateBlock) * 3) * kStateBlock + e0 % kStateBlock;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        float x[kVec];
+        float* bp = p.blocked + b0 + k * kStateBlock;
+        if constexpr (TO_BLOCKED) {
+            load8(p.sep[k] + e0, full, cnt, x);
+            store8(bp, full, cnt, x);
+        } else {
+            load8(bp, full, cnt, x);
+            store8(p.sep[k] + e0, full, cnt, x);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // Host-side launch helpers.
 
@@ -1094,18 +1140,20 @@ int launch(const void* kernel, unsigned blocks, void* params, void* stream, int 
     return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
 }
 
-template <int F, int U>
+template <int F, int U, bool BLK>
 const void* step_kernel_u(bool out) {
-    return out ? reinterpret_cast<const void*>(&fused_step_kernel<F, true, U>)
-               : reinterpret_cast<const void*>(&fused_step_kernel<F, false, U>);
+    return out ? reinterpret_cast<const void*>(&fused_step_kernel<F, true, U, BLK>)
+               : reinterpret_cast<const void*>(&fused_step_kernel<F, false, U, BLK>);
 }
 
+// The blocked state layout is compiled with one group per wave only.
 template <int F>
-const void* step_kernel(bool out, int groups) {
+const void* step_kernel(bool out, int groups, bool blocked) {
+    if (blocked) return step_kernel_u<F, 1, true>(out);
     switch (groups) {
-        case 1: return step_kernel_u<F, 1>(out);
-        case 4: return step_kernel_u<F, 4>(out);
-        default: return step_kernel_u<F, 2>(out);
+        case 1: return step_kernel_u<F, 1, false>(out);
+        case 4: return step_kernel_u<F, 4, false>(out);
+        default: return step_kernel_u<F, 2, false>(out);
     }
 }
 
@@ -1118,14 +1166,14 @@ int groups_for(int fan_in) {
 }
 
 // fan_in -1 selects the fp32-gradient kernels.
-const void* pick_step_kernel(int fan_in, bool out, int groups) {
+const void* pick_step_kernel(int fan_in, bool out, int groups, bool blocked) {
     switch (fan_in) {
-        case -1: return step_kernel<-1>(out, groups);
-        case 1: return step_kernel<1>(out, groups);
-        case 2: return step_kernel<2>(out, groups);
-        case 4: return step_kernel<4>(out, groups);
-        case 8: return step_kernel<8>(out, groups);
-        default: return step_kernel<0>(out, groups);
+        case -1: return step_kernel<-1>(out, groups, blocked);
+        case 1: return step_kernel<1>(out, groups, blocked);
+        case 2: return step_kernel<2>(out, groups, blocked);
+        case 4: return step_kernel<4>(out, groups, blocked);
+        case 8: return step_kernel<8>(out, groups, blocked);
+        default: return step_kernel<0>(out, groups, blocked);
     }
 }
 
@@ -1150,12 +1198,19 @@ bool is_finite(double x) { return std::isfinite(x); }
 
 // Shared by the two step entry points: exactly one of (contribs, fan_in >= 1) and
 // (grad32, fan_in == -1) is the gradient source.
+// Elements of a blocked state array for an n-element slice (-1 when it does not fit int64).
+int64_t blocked_elems(int64_t n) {
+    if (n < 0 || n > INT64_MAX / 16) return -1;
+    return 3 * ((n + kStateBlock - 1) / kStateBlock) * kStateBlock;
+}
+
+// With `blocked`, `master` is the blocked state array and m, v are null.
 int launch_step(float* master, float* m, float* v, const uint16_t* const* contribs, int32_t fan_in,
                 const float* grad32, int64_t n, const fsdpshard_segment* segs, int32_t n_segments,
                 const fsdpshard_adamw* hp, uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
-                void* stream) {
-    if (master == nullptr || m == nullptr || v == nullptr || hp == nullptr || n < 0 ||
-        n_segments < 0 || (n_segments > 0 && segs == nullptr) || lo < 0)
+                void* stream, bool blocked = false) {
+    if (master == nullptr || (!blocked && (m == nullptr || v == nullptr)) || hp == nullptr ||
+        n < 0 || n_segments < 0 || (n_segments > 0 && segs == nullptr) || lo < 0)
         return FSDPSHARD_ERR_INVALID_ARG;
     int rc = FSDPSHARD_OK;
     if (fan_in == -1) {
@@ -1171,7 +1226,8 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
         !is_finite(hp->max_grad_norm) || hp->max_grad_norm < 0.0 ||
         (hp->max_grad_norm > 0.0 && hp->grad_sumsq == nullptr))
         return FSDPSHARD_ERR_INVALID_ARG;
-    if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return FSDPSHARD_ERR_ALIGNMENT;
+    if (!aligned16(master) || (!blocked && (!aligned16(m) || !aligned16(v))))
+        return FSDPSHARD_ERR_ALIGNMENT;
     if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
         return FSDPSHARD_ERR_ALIGNMENT;
     if (hp->max_grad_norm > 0.0 && (reinterpret_cast<uintptr_t>(hp->grad_sumsq) & 7u) != 0)
@@ -1182,11 +1238,11 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
         if ((reinterpret_cast<uintptr_t>(flat_bf16) & 1u) != 0) return FSDPSHARD_ERR_ALIGNMENT;
         out = flat_bf16 + (lo - flat_index0);
     }
-    if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
+    if (n > INT64_MAX / 16) return FSDPSHARD_ERR_OVERFLOW;
     // Written buffers must not overlap each other or the inputs.
     const int64_t fb = n * 4, hb = n * 2;
-    const void* wr[4] = {master, m, v, out};
-    const int64_t wb[4] = {fb, fb, fb, hb};
+    const void* wr[4] = {master, blocked ? nullptr : m, blocked ? nullptr : v, out};
+    const int64_t wb[4] = {blocked ? blocked_elems(n) * 4 : fb, fb, fb, hb};
     for (int i = 0; i < 4; ++i) {
         if (wr[i] == nullptr || n == 0) continue;
         for (int j = i + 1; j < 4; ++j)
@@ -1205,8 +1261,8 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
 
     StepParams p;
     p.master = master;
-    p.m = m;
-    p.v = v;
+    p.m = blocked ? nullptr : m;
+    p.v = blocked ? nullptr : v;
     for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
         p.contrib[r] = (fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
     p.segs = segs;
@@ -1231,11 +1287,11 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     p.dec = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
     p.scale = static_cast<float>(hp->grad_scale);
 
-    const int groups = groups_for(fan_in);
+    const int groups = blocked ? 1 : groups_for(fan_in);   // the blocked kernels take one
     unsigned blocks = 0;
     rc = tile_grid(n, groups, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(pick_step_kernel(fan_in, out != nullptr, groups), blocks, &p, stream,
+    return launch(pick_step_kernel(fan_in, out != nullptr, groups, blocked), blocks, &p, stream,
                   step_groups_per_cu(fan_in));
 }
 
@@ -1309,6 +1365,68 @@ extern "C" int adamw_shard_step_f32grad(float* master, float* m, float* v, const
                                         void* stream) {
     return launch_step(master, m, v, nullptr, -1, grad, n, segs, n_segments, hp, flat_bf16,
                        flat_index0, lo, stream);
+}
+
+extern "C" int64_t state_blocked_elems(int64_t n) { return blocked_elems(n); }
+
+extern "C" int adamw_shard_step_blocked(float* state, const uint16_t* const* contribs,
+                                        int32_t fan_in, int64_t n, const fsdpshard_segment* segs,
+                                        int32_t n_segments, const fsdpshard_adamw* hp,
+                                        uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
+                                        void* stream) {
+    if (fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
+    return launch_step(state, nullptr, nullptr, contribs, fan_in, nullptr, n, segs, n_segments, hp,
+                       flat_bf16, flat_index0, lo, stream, true);
+}
+
+extern "C" int adamw_shard_step_f32grad_blocked(float* state, const float* grad, int64_t n,
+                                                const fsdpshard_segment* segs, int32_t n_segments,
+                                                const fsdpshard_adamw* hp, uint16_t* flat_bf16,
+                                                int64_t flat_index0, int64_t lo, void* stream) {
+    return launch_step(state, nullptr, nullptr, nullptr, -1, grad, n, segs, n_segments, hp,
+                       flat_bf16, flat_index0, lo, stream, true);
+}
+
+namespace {
+int launch_state_pack(float* master, float* m, float* v, int64_t n, float* state, bool to_blocked,
+                      void* stream) {
+    if (master == nullptr || m == nullptr || v == nullptr || state == nullptr || n < 0)
+        return FSDPSHARD_ERR_INVALID_ARG;
+    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(state))
+        return FSDPSHARD_ERR_ALIGNMENT;
+    const int64_t sb = blocked_elems(n);
+    if (sb < 0) return FSDPSHARD_ERR_OVERFLOW;
+    const void* sep[3] = {master, m, v};
+    for (int i = 0; i < 3 && n > 0; ++i) {
+        if (overlaps(sep[i], n * 4, state, sb * 4)) return FSDPSHARD_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(sep[i], n * 4, sep[j], n * 4)) return FSDPSHARD_ERR_INVALID_ARG;
+    }
+    if (n == 0) return FSDPSHARD_OK;
+    StatePackParams p;
+    p.sep[0] = master;
+    p.sep[1] = m;
+    p.sep[2] = v;
+    p.blocked = state;
+    p.n = n;
+    unsigned blocks = 0;
+    const int rc = tile_grid(n, 1, &blocks);
+    if (rc != FSDPSHARD_OK) return rc;
+    return launch(to_blocked ? reinterpret_cast<const void*>(&state_pack_kernel<true>)
+                             : reinterpret_cast<const void*>(&state_pack_kernel<false>),
+                  blocks, &p, stream);
+}
+}  // namespace
+
+extern "C" int state_to_blocked(const float* master, const float* m, const float* v, int64_t n,
+                                float* state, void* stream) {
+    return launch_state_pack(const_cast<float*>(master), const_cast<float*>(m),
+                             const_cast<float*>(v), n, state, true, stream);
+}
+
+extern "C" int state_from_blocked(const float* state, int64_t n, float* master, float* m, float* v,
+                                  void* stream) {
+    return launch_state_pack(master, m, v, n, const_cast<float*>(state), false, stream);
 }
 
 extern "C" int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
