@@ -397,6 +397,10 @@ def main():
     ap.add_argument("--reshard-rank", type=int, default=1,
                     help="reshard path: destination rank")
     ap.add_argument("--micro-batches", type=int, default=4)
+    ap.add_argument("--state", choices=["blocked", "separate"], default="blocked",
+                    help="optimizer-state layout: one array of 512-element blocks of master, m "
+                         "and v (default), or three separate arrays (the split path always uses "
+                         "separate arrays)")
     ap.add_argument("--max-grad-norm", type=float, default=1.0)
     ap.add_argument("--evict-mb", type=int, default=-1,
                     help="MiB written between timed steps to flush the 256 MB last-level cache "
@@ -458,6 +462,24 @@ def main():
     phase = lo % 8
     flat = torch.empty(n + phase, dtype=torch.int16, device=dev)
     segs_dev = F.segments_to_device(segs, dev)
+    blocked = args.state == "blocked" and args.path != "split"
+    if blocked:
+        state = torch.empty(F.state_blocked_elems(n), dtype=torch.float32, device=dev)
+        F.state_to_blocked(master, m, v, state)
+        torch.cuda.synchronize()
+        del master, m, v
+
+        def step_bf16(t, **kw):
+            F.adamw_shard_step_blocked(state, grads, step=t, n=n, **kw)
+
+        def step_f32(acc, t, **kw):
+            F.adamw_shard_step_f32grad_blocked(state, acc, step=t, n=n, **kw)
+    else:
+        def step_bf16(t, **kw):
+            F.adamw_shard_step(master, m, v, grads, step=t, **kw)
+
+        def step_f32(acc, t, **kw):
+            F.adamw_shard_step_f32grad(master, m, v, acc, step=t, **kw)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -469,8 +491,8 @@ def main():
     # default; the clipped and accumulate paths measure the clipping and micro-batch rows.
     stages = []
     if args.path == "fused":
-        stages.append(("adamw_shard_step", lambda t: F.adamw_shard_step(
-            master, m, v, grads, step=t, **common), L.n_real * bpp))
+        stages.append(("adamw_shard_step" + ("_blocked" if blocked else ""),
+                       lambda t: step_bf16(t, **common), L.n_real * bpp))
     elif args.path == "split":
         no_out = {k: v for k, v in common.items() if k not in ("flat", "flat_index0", "lo")}
         stages.append(("adamw_shard_step (no bf16 output)", lambda t: F.adamw_shard_step(
@@ -485,17 +507,16 @@ def main():
             stages.append(("grad_sumsq_shard", lambda t: F.grad_sumsq_shard(
                 sumsq, contribs=grads, n=n, segs=segs_dev, n_segments=L.n_segments,
                 workspace=ws, stream=stream), n * 2 * Fi))
-            stages.append(("adamw_shard_step (clipped)", lambda t: F.adamw_shard_step(
-                master, m, v, grads, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
-                **common), L.n_real * bpp))
+            stages.append(("adamw_shard_step (clipped)", lambda t: step_bf16(
+                t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq, **common), L.n_real * bpp))
         elif args.path == "clipped32":
             acc = torch.empty(n, dtype=torch.float32, device=dev)
             stages.append(("reduce_shard_sumsq", lambda t: F.reduce_shard_sumsq(
                 grads, acc, sumsq, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
                 stream=stream), n * (2 * Fi + 4)))
-            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: F.adamw_shard_step_f32grad(
-                master, m, v, acc, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
-                **common), L.n_real * algorithmic_bytes_per_param_f32grad()))
+            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: step_f32(
+                acc, t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq, **common),
+                L.n_real * algorithmic_bytes_per_param_f32grad()))
         else:
             acc = torch.empty(n, dtype=torch.float32, device=dev)
             stages.append(("reduce_shard", lambda t: F.reduce_shard(grads, acc, stream=stream),
@@ -513,9 +534,9 @@ def main():
                 stages.append(("grad_sumsq_shard (fp32)", lambda t: F.grad_sumsq_shard(
                     sumsq, grad=acc, n=n, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
                     stream=stream), n * 4))
-            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: F.adamw_shard_step_f32grad(
-                master, m, v, acc, step=t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq,
-                **common), L.n_real * algorithmic_bytes_per_param_f32grad()))
+            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: step_f32(
+                acc, t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq, **common),
+                L.n_real * algorithmic_bytes_per_param_f32grad()))
 
     step_bytes = sum(b for _, _, b in stages)
     evict_mb = args.evict_mb if args.evict_mb >= 0 else (1024 if step_bytes < 2e9 else 0)
@@ -582,13 +603,18 @@ def main():
     if not args.no_copy_reference and n8 > 0 and args.path == "fused":
         out16 = flat[phase:phase + n8] if phase == 0 else torch.empty(n8, dtype=torch.int16,
                                                                         device=dev)
+        def mix():
+            if blocked:
+                F.stream_mix_blocked(grads, state, out16, n8, stream=stream)
+            else:
+                F.stream_mix(grads, master, m, v, out16, n=n8, stream=stream)
         for _ in range(2):
-            F.stream_mix(grads, master, m, v, out16, n=n8, stream=stream)
+            mix()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 5
         a.record(stream)
         for _ in range(reps):
-            F.stream_mix(grads, master, m, v, out16, n=n8, stream=stream)
+            mix()
         b.record(stream)
         torch.cuda.synchronize()
         mix_ms = a.elapsed_time(b) / reps
@@ -645,6 +671,8 @@ def main():
             "step_ms_min": round(min(step_ms), 4),
             "timing": timing,
             "path": args.path,
+            "state_layout": ("blocked: one array, 512-element blocks of master, m, v" if blocked
+                             else "separate master, m, v arrays"),
             "stages": stage_info,
             "groups_per_wave": args.groups_per_wave or "default",
         },

@@ -117,11 +117,15 @@ def lib():
     h.fsdpshard_stream_copy.argtypes = [c_vp, c_vp, c_i64, c_vp]
     h.fsdpshard_stream_mix.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_vp, c_vp, c_i64,
                                        c_vp]
+    h.fsdpshard_stream_mix_blocked.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_i64,
+                                               c_vp]
     for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
                  "adamw_shard_step_f32grad", "reduce_shard_accumulate", "grad_sumsq_shard",
                  "reshard_plan", "reshard_copy",
                  "fsdpshard_abi_version", "fsdpshard_set_groups_per_wave", "fsdpshard_stream_copy",
-                 "fsdpshard_stream_mix"):
+                 "fsdpshard_stream_mix", "fsdpshard_stream_mix_blocked", "reduce_shard_sumsq",
+                 "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
+                 "state_to_blocked", "state_from_blocked"):
         getattr(h, name).restype = ctypes.c_int
     _lib_handle = h
     return h
@@ -461,6 +465,17 @@ def stream_mix(contribs, s0, s1, s2, out, n=None, stream=None):
     _check("fsdpshard_stream_mix", lib().fsdpshard_stream_mix(
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(s0, "s0"), _ptr(s1, "s1"),
         _ptr(s2, "s2"), _ptr(out, "out"), n, _stream(stream, s0)))
+
+
+def stream_mix_blocked(contribs, state, out, n, stream=None):
+    """Measurement aid: stream_mix for the blocked state layout."""
+    n = int(n)
+    arr = _contrib_array(contribs, n)
+    _need_bytes(state, "state", 4 * state_blocked_elems(n))
+    _need_bytes(out, "out", 2 * n)
+    _check("fsdpshard_stream_mix_blocked", lib().fsdpshard_stream_mix_blocked(
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(state, "state"),
+        _ptr(out, "out"), n, _stream(stream, state)))
 
 
 # ------------------------------------------------------------------------------ reshard

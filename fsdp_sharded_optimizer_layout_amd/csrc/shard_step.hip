@@ -1001,7 +1001,7 @@ struct MixParams {
     int32_t fan_in;
 };
 
-template <int F>
+template <int F, bool BLK>
 __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
@@ -1016,8 +1016,14 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
 #pragma unroll
         for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
     }
+    // Separate layout: three arrays.  Blocked layout: s[0] is the blocked state array.
+    float* sp[3];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) load8(p.s[k] + e0, true, kVec, st[k]);
+    for (int k = 0; k < 3; ++k)
+        sp[k] = BLK ? p.s[0] + ((e0 / kStateBlock) * 3 + k) * kStateBlock + e0 % kStateBlock
+                    : p.s[k] + e0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) load8(sp[k], true, kVec, st[k]);
     if constexpr (F > 0) {
 #pragma unroll
         for (int r = 0; r < F; ++r) x ^= raw[r].x ^ raw[r].y ^ raw[r].z ^ raw[r].w;
@@ -1030,7 +1036,7 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         st[k][0] = __uint_as_float(__float_as_uint(st[k][0]) ^ x);
-        store8(p.s[k] + e0, true, kVec, st[k]);
+        store8(sp[k], true, kVec, st[k]);
     }
     st_u4_nt(p.out + e0, make_uint4(__float_as_uint(st[0][1]), __float_as_uint(st[1][1]),
                                     __float_as_uint(st[2][1]), x));
@@ -1623,21 +1629,26 @@ extern "C" int fsdpshard_set_groups_per_wave(int groups) {
     return g_groups_per_wave.exchange(groups);
 }
 
-extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0,
-                                    float* s1, float* s2, uint16_t* out, int64_t n, void* stream) {
-    if (s0 == nullptr || s1 == nullptr || s2 == nullptr || out == nullptr || n < 0 || n % kVec)
+namespace {
+// With `blocked`, s0 is the blocked state array and s1, s2 are null.
+int stream_mix_impl(const uint16_t* const* contribs, int32_t fan_in, float* s0, float* s1,
+                    float* s2, uint16_t* out, int64_t n, bool blocked, void* stream) {
+    if (s0 == nullptr || (!blocked && (s1 == nullptr || s2 == nullptr)) || out == nullptr ||
+        n < 0 || n % kVec)
         return FSDPSHARD_ERR_INVALID_ARG;
     int rc = check_contribs(contribs, fan_in, n);
     if (rc != FSDPSHARD_OK) return rc;
-    if (!aligned16(s0) || !aligned16(s1) || !aligned16(s2) || !aligned16(out))
+    if (!aligned16(s0) || (!blocked && (!aligned16(s1) || !aligned16(s2))) || !aligned16(out))
         return FSDPSHARD_ERR_ALIGNMENT;
-    if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
+    if (n > INT64_MAX / 16) return FSDPSHARD_ERR_OVERFLOW;
     if (n == 0) return FSDPSHARD_OK;
-    const void* wr[4] = {s0, s1, s2, out};
-    const int64_t wb[4] = {n * 4, n * 4, n * 4, n * 2};
+    const void* wr[4] = {s0, blocked ? nullptr : s1, blocked ? nullptr : s2, out};
+    const int64_t wb[4] = {blocked ? blocked_elems(n) * 4 : n * 4, n * 4, n * 4, n * 2};
     for (int i = 0; i < 4; ++i) {
+        if (wr[i] == nullptr) continue;
         for (int j = i + 1; j < 4; ++j)
-            if (overlaps(wr[i], wb[i], wr[j], wb[j])) return FSDPSHARD_ERR_INVALID_ARG;
+            if (wr[j] != nullptr && overlaps(wr[i], wb[i], wr[j], wb[j]))
+                return FSDPSHARD_ERR_INVALID_ARG;
         for (int r = 0; r < fan_in; ++r)
             if (overlaps(wr[i], wb[i], contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
     }
@@ -1652,8 +1663,23 @@ extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan
     unsigned blocks = 0;
     rc = tile_grid(n, 1, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    const void* k = fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1>)
-                    : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8>)
-                                  : reinterpret_cast<const void*>(&stream_mix_kernel<0>);
+    const void* k =
+        blocked ? (fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1, true>)
+                   : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8, true>)
+                                 : reinterpret_cast<const void*>(&stream_mix_kernel<0, true>))
+                : (fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1, false>)
+                   : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8, false>)
+                                 : reinterpret_cast<const void*>(&stream_mix_kernel<0, false>));
     return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in));   // as the step
+}
+}  // namespace
+
+extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0,
+                                    float* s1, float* s2, uint16_t* out, int64_t n, void* stream) {
+    return stream_mix_impl(contribs, fan_in, s0, s1, s2, out, n, false, stream);
+}
+
+extern "C" int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in,
+                                            float* state, uint16_t* out, int64_t n, void* stream) {
+    return stream_mix_impl(contribs, fan_in, state, nullptr, nullptr, out, n, true, stream);
 }

@@ -40,6 +40,13 @@ int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* strea
 int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0, float* s1,
                          float* s2, uint16_t* out, int64_t n, void* stream);
 
+/*
+ * fsdpshard_stream_mix_blocked -- the same replay for the blocked state layout (see
+ * adamw_shard_step_blocked): `state` holds state_blocked_elems(n) floats, 16-byte aligned.
+ */
+int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in, float* state,
+                                 uint16_t* out, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
