@@ -1014,18 +1014,27 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
     uint4 raw[F > 0 ? F : 1];
     float st[3][kVec];
     uint32_t x = 0;
-    if constexpr (F > 0) {
-#pragma unroll
-        for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
-    }
     // Separate layout: three arrays.  Blocked layout: s[0] is the blocked state array.
     float* sp[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k)
         sp[k] = BLK ? p.s[0] + ((e0 / kStateBlock) * 3 + k) * kStateBlock + e0 % kStateBlock
                     : p.s[k] + e0;
+    // The step's issue order: all state first (blocked state, or one gradient stream), else
+    // master and m, then the gradients, then v.
+    constexpr bool kStateFirst = BLK || F == 1;
+    load8(sp[0], true, kVec, st[0]);
+    load8(sp[1], true, kVec, st[1]);
+    if constexpr (kStateFirst) load8(sp[2], true, kVec, st[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (F > 0) {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) load8(sp[k], true, kVec, st[k]);
+        for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
+    }
+    if constexpr (!kStateFirst) {
+        __builtin_amdgcn_sched_barrier(0);
+        load8(sp[2], true, kVec, st[2]);
+    }
     if constexpr (F > 0) {
 #pragma unroll
         for (int r = 0; r < F; ++r) x ^= raw[r].x ^ raw[r].y ^ raw[r].z ^ raw[r].w;
