@@ -775,6 +775,19 @@ __global__ __launch_bounds__(kBlock) void sumsq_finish_kernel(SumsqParams p) {
 // sumsq_kernel (each work-group covers kSumsqGroups groups per wave, so the partials fill the
 // same workspace).  Whole tiles take a straight-line path; the slice's last tile and run-time
 // fan-ins take the bounds-checked path.
+//
+// Where many bytes per element arrive (eight contribution streams, or four plus the accumulator),
+// the straight-line path is software-pipelined: the next group's loads are issued before the
+// current group is reduced and stored, which the kernel cannot otherwise do because the
+// compiler must assume the stores may alias the next loads (the entry point rejects overlaps).
+// Those instances run one work-group per CU.  Measured on MI355X at the 7B-shaped slice against
+// one group at a time with 2 work-groups per CU: fan-in 8 9 % faster, fan-in 8 accumulating 2.5 %,
+// fan-in 4 accumulating 5.5 %; at fan-in 1, 2 and 4 without accumulation the pipeline is 4-10 %
+// slower, so they keep the plain loop.
+template <int F, bool ACC>
+constexpr bool reduce_sq_pipelined() { return F >= 8 || (F >= 4 && ACC); }
+static_assert(kSumsqGroups % 2 == 0, "the pipelined path takes groups in pairs");
+
 struct ReduceSqParams {
     const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
     float* out;
@@ -799,7 +812,46 @@ __global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) 
         SegCursor cur;
         cur.init(p.segs, p.n_segs, base0 * kVec);
         bool done = false;
-        if constexpr (F > 0) {
+        if constexpr (reduce_sq_pipelined<F, ACC>()) {
+            if (base0 + kSumsqGroups * kWave <= p.n / kVec) {
+                // Two register slots: slot (g0 & 1) holds group g0's loads.
+                uint4 raw[2][F];
+                float acc[2][kVec];
+                auto issue = [&](int slot, int g0) {
+                    const int64_t e0 = (base0 + g0 * kWave + lane) * kVec;
+#pragma unroll
+                    for (int r = 0; r < F; ++r) raw[slot][r] = ld_u4_nt(p.contrib[r] + e0);
+                    if constexpr (ACC) load8(p.out + e0, true, kVec, acc[slot]);
+                };
+                auto finish = [&](int slot, int g0) {
+                    const int64_t gb = base0 + g0 * kWave;
+                    const int64_t e0 = (gb + lane) * kVec;
+                    float g[kVec];
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < F; ++r) accumulate(g, raw[slot][r]);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        g[e] = g[e] * p.scale;
+                        if constexpr (ACC) g[e] = acc[slot][e] + g[e];
+                    }
+                    store8(p.out + e0, true, kVec, g);
+                    add_squares(cur, p.n, gb, nvec, lane, g, kVec, sq);
+                };
+                issue(0, 0);
+#pragma unroll 1
+                for (int g0 = 0; g0 < kSumsqGroups; g0 += 2) {
+                    issue(1, g0 + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    finish(0, g0);
+                    if (g0 + 2 < kSumsqGroups) issue(0, g0 + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    finish(1, g0 + 1);
+                }
+                done = true;
+            }
+        } else if constexpr (F > 0) {
             if (base0 + kSumsqGroups * kWave <= p.n / kVec) {
                 for (int g0 = 0; g0 < kSumsqGroups; ++g0) {
                     const int64_t gb = base0 + g0 * kWave;
@@ -1115,8 +1167,9 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 // from an fp32 gradient; at fan-in 4 the 2,000-tensor slice is 5 % faster with 3 per CU (2 gains
 // nothing there), and at fan-in 2 and 16 both are within 1 %, so other fan-ins take 3.  The fp32
 // accumulation is 4-10 % faster with 2 per CU; the plain reduction of a single contribution wants
-// 4 per CU (2 cost it a quarter); the sum of squares, unflatten and plain copies are fastest
-// uncapped.
+// 4 per CU (2 cost it a quarter); the reduction fused with the sum of squares wants 2 per CU, 3
+// for a single contribution and 1 where its loads are software-pipelined (reduce_sq_pipelined);
+// the sum of squares, unflatten and plain copies are fastest uncapped.
 constexpr int step_groups_per_cu(int fan_in) {
     return fan_in == 1 || fan_in == 8 || fan_in == -1 ? 2 : 3;
 }
@@ -1124,6 +1177,7 @@ constexpr int kReduceGroupsPerCU = 2;
 constexpr int kReduceOneStreamGroupsPerCU = 4;
 constexpr int kReduceSqGroupsPerCU = 2;
 constexpr int kReduceOneStreamSqGroupsPerCU = 3;
+constexpr int kReduceSqPipelinedGroupsPerCU = 1;
 constexpr int kMaxDevices = 64;
 std::atomic<int64_t> g_lds_per_cu[kMaxDevices];   // 0: not queried yet; -1: unknown
 
@@ -1551,11 +1605,13 @@ extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_i
     if (parts > 0) {
         const bool acc = accumulate != 0;
         const void* k = nullptr;
+        bool pipelined = false;
         switch (fan_in) {
 #define FSDPSHARD_REDUCE_SQ_CASE(FI)                                                            \
     case FI:                                                                                    \
         k = acc ? reinterpret_cast<const void*>(&reduce_sumsq_kernel<FI, true>)                \
                 : reinterpret_cast<const void*>(&reduce_sumsq_kernel<FI, false>);              \
+        pipelined = acc ? reduce_sq_pipelined<FI, true>() : reduce_sq_pipelined<FI, false>();   \
         break;
             FSDPSHARD_REDUCE_SQ_CASE(1)
             FSDPSHARD_REDUCE_SQ_CASE(2)
@@ -1567,7 +1623,9 @@ extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_i
                         : reinterpret_cast<const void*>(&reduce_sumsq_kernel<0, false>);
         }
         rc = launch(k, static_cast<unsigned>(parts), &p, stream,
-                    fan_in == 1 && !acc ? kReduceOneStreamSqGroupsPerCU : kReduceSqGroupsPerCU);
+                    pipelined                ? kReduceSqPipelinedGroupsPerCU
+                    : fan_in == 1 && !acc    ? kReduceOneStreamSqGroupsPerCU
+                                             : kReduceSqGroupsPerCU);
         if (rc != FSDPSHARD_OK) return rc;
     }
     SumsqParams f;

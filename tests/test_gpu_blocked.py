@@ -130,11 +130,12 @@ def test_blocked_step_matches_oracle_and_separate_layout(case):
 
 
 @pytest.mark.slow
-def test_full_size_dense7b_blocked_equals_separate():
-    w = W.WORKLOADS["dense7b_n8_rank0"]
+@pytest.mark.parametrize("name", ["dense7b_n8_rank0", "dense70b_n64_rank0"])
+def test_full_size_blocked_equals_separate(name):
+    w = W.WORKLOADS[name]
     L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
     n, lo = L.n, L.lo
-    say(f"blocked 7B full size n={n}")
+    say(f"blocked full size {name} n={n}")
     dev = torch.device("cuda")
     sd = F.segments_to_device(segs, dev)
     master, m, v = W.torch_state(w, n, 0, dev)

@@ -282,7 +282,9 @@ def test_sumsq_full_slice_parts_add_up(name):
 
 @pytest.mark.parametrize("n,F_in,acc", [(1, 1, False), (7, 3, True), (32768, 8, False),
                                         (32769, 8, True), (65539, 2, True), (300_017, 5, False),
-                                        (1_000_003, 1, True), (2_500_001, 4, False)])
+                                        (1_000_003, 1, True), (2_500_001, 4, False),
+                                        (1_000_003, 4, True), (300_017, 8, True),
+                                        (2_500_001, 8, False), (98_304, 4, True)])
 def test_reduce_sumsq_matches_oracle(n, F_in, acc):
     # The fp32 shard equals the plain reduction (or accumulation) bit for bit; the sum of squares
     # of that shard matches the oracle's exact sum; the sum is bit-identical when repeated.
@@ -307,6 +309,35 @@ def test_reduce_sumsq_matches_oracle(n, F_in, acc):
         assert res.cpu().numpy()[0] == h[0]
         # The fused sum agrees with grad_sumsq_shard over the same fp32 shard.
         assert abs(_gpu_sumsq(grad=out.data(), n=n) - h[0]) <= SUMSQ_RTOL * osum
+
+
+@pytest.mark.parametrize("F_in,acc", [(8, False), (8, True), (4, True), (4, False), (1, False),
+                                      (2, True)])
+def test_reduce_sumsq_padding_inside_whole_tiles(F_in, acc):
+    # A padded layout across several whole tiles (the straight-line paths, pipelined or not):
+    # the fp32 shard is the plain reduction bit for bit and the sum drops every padding element.
+    sizes = [(i * 7919) % 3001 + 1 for i in range(300)]
+    L, segs, flags = _layout(sizes, 16, None, 2, 1)
+    n = L.n
+    real = (flags & OL.PADDING) == 0
+    say(f"reduce+sumsq padded tiles F={F_in} accumulate={acc} n={n} segments={L.n_segments}")
+    contribs = [W.np_bf16_normal([74, r], n, 1e-2) for r in range(F_in)]
+    for c in contribs:
+        c[~real] = 0x7FC0
+    acc0 = W.np_f32_normal([75, n], n, 1e-3) if acc else np.zeros(n, np.float32)
+    out = Guarded(acc0)
+    res = torch.zeros(1, dtype=torch.float64, device="cuda")
+    F.reduce_shard_sumsq([to_dev16(c) for c in contribs], out.data(), res, accumulate=acc,
+                         scale=0.25, segs=F.segments_to_device(segs), n_segments=L.n_segments)
+    torch.cuda.synchronize()
+    want = (OS.accumulate_fp32(acc0, contribs, 0.25) if acc
+            else OS.reduce_contributions(contribs, 0.25))
+    assert n > 4 * 32768
+    assert bit_equal(out.data_host()[real], want[real])
+    out.assert_guards("out")
+    osum = OC.sumsq_exact(want, real)
+    got = float(res.cpu().numpy()[0])
+    assert abs(got - osum) <= SUMSQ_RTOL * osum, (got, osum)
 
 
 @pytest.mark.parametrize("F_in", [1, 4, 8, 3])
