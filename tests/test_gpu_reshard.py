@@ -152,3 +152,36 @@ def test_full_size_dense7b_sampled(dst_pad, dst_world, dst_rank):
     guard = torch.cat([dst[:4], dst[4 + n_dst:]]).cpu().numpy()
     assert (guard == 0x5A5A5A5A).all()
     say(f"  {j.size} sampled elements ok ({int(real.sum())} real)")
+
+
+@pytest.mark.slow
+def test_full_state_dict_from_2000_tensor_shards():
+    """16 ranks with padding 16 -> one rank without padding: the result must be every tensor's
+    values back to back, which is what a full (unsharded, unpadded) state dict holds.  Each real
+    element carries its running index + 1 and padding carries 0, so the expected vector is
+    1..P_real by definition, with no call to the oracle's reshard."""
+    w = W.WORKLOADS["many_small_n16_rank3"]
+    sizes, pa, na = w.sizes, w.pad_multiple, w.world_size
+    offs, Pa = OL.flatten_offsets(sizes, pa)
+    real_total = int(np.sum(sizes))
+    flat = np.zeros(Pa, dtype=np.int32)
+    start = 1
+    for o, s in zip(offs, sizes):
+        flat[o:o + s] = np.arange(start, start + s, dtype=np.int32)
+        start += s
+    src = []
+    for k in range(na):
+        lo, hi = OL.shard_bounds(Pa, na, k)
+        src.append(torch.from_numpy(flat[lo:hi].copy()).cuda())
+    del flat
+    pieces = F.reshard_plan(sizes, pa, na, 1, 1, 0)
+    say(f"full state dict: {na}/{pa} -> 1/1, {real_total} elements, {len(pieces)} pieces")
+    dst = torch.full((real_total + 8,), -7, dtype=torch.int32, device="cuda")
+    F.reshard_copy(src, dst[4:4 + real_total], pieces)
+    want = torch.arange(1, real_total + 1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    assert torch.equal(dst[4:4 + real_total], want)
+    h = dst.cpu().numpy()
+    assert (h[:4] == -7).all() and (h[4 + real_total:] == -7).all()
+    del src, dst, want
+    torch.cuda.empty_cache()
