@@ -10,12 +10,16 @@
  *   - Counts and indices are int64_t.  bf16 values travel as uint16_t bit patterns.
  *   - "device" pointers are HIP device allocations on the current HIP device; "host" pointers are
  *     ordinary process memory.  The caller owns every buffer; the library never allocates device
- *     memory and keeps no state besides the process-wide tuning setting below.
+ *     memory and keeps no state besides the process-wide tuning setting below and, per device,
+ *     the cached LDS size of one compute unit (queried once, used to size launches).
  *   - `stream` is a hipStream_t passed as void* (NULL = the device's null stream).  GPU calls are
- *     asynchronous and stream-ordered: they validate their arguments on the host, enqueue one
- *     kernel and return.  A fault inside a kernel surfaces at the caller's next synchronisation.
- *   - Every call returns 0 (FSDPSHARD_OK) or a positive fsdpshard_status.  Nothing is enqueued
- *     when a call returns an error; nothing is thrown and nothing aborts.
+ *     asynchronous and stream-ordered: they validate their arguments on the host, enqueue their
+ *     kernels (one for most calls; two for the sums of squares; reshard_copy one per 96 pieces)
+ *     and return.  A fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - Every call returns 0 (FSDPSHARD_OK) or a positive fsdpshard_status.  Argument errors are
+ *     found before anything is enqueued; a launch the HIP runtime refuses (FSDPSHARD_ERR_HIP)
+ *     may leave a multi-kernel call's earlier kernels enqueued.  Nothing is thrown and nothing
+ *     aborts.
  *   - n == 0 is a successful no-op.
  */
 #ifndef FSDPSHARD_H
