@@ -239,6 +239,18 @@ def _stream(stream, like=None):
     return stream.cuda_stream
 
 
+def _call_workspace(nbytes, device, stream):
+    """Workspace for one call, allocated through PyTorch's caching allocator.  The block is tied
+    to the current stream; when the call runs on another stream, that stream is recorded on the
+    tensor so the block is not handed out again before the call's kernels have run."""
+    import torch
+    ws = torch.empty(max(int(nbytes), 8), dtype=torch.uint8, device=device)
+    handle = _stream(stream, ws)
+    if handle != torch.cuda.current_stream(ws.device).cuda_stream:
+        ws.record_stream(torch.cuda.ExternalStream(handle, device=ws.device))
+    return ws
+
+
 def _contrib_array(contribs, n):
     if not 1 <= len(contribs) <= MAX_FAN_IN:
         raise ValueError(f"fan-in must be 1..{MAX_FAN_IN}")
@@ -393,7 +405,7 @@ def grad_sumsq_shard(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=No
     """Sum of squares of the slice's reduced gradient (float64, fixed order) into ``sumsq`` (a
     device float64 tensor).  Give either the bf16 ``contribs`` or one fp32 ``grad`` shard.
     ``workspace``: device tensor of at least grad_sumsq_workspace_bytes(n) bytes (allocated here
-    through PyTorch when omitted)."""
+    through PyTorch when omitted, and then safe to use with any ``stream``)."""
     import torch
     if (contribs is None) == (grad is None):
         raise ValueError("give exactly one of contribs and grad")
@@ -402,7 +414,7 @@ def grad_sumsq_shard(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=No
     n = int(n)
     need = grad_sumsq_workspace_bytes(n)
     if workspace is None:
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=sumsq.device)
+        workspace = _call_workspace(need, sumsq.device, stream)
     wbytes = workspace.numel() * workspace.element_size()
     if contribs is not None:
         arr = _contrib_array(contribs, n)
@@ -425,7 +437,7 @@ def reduce_shard_sumsq(contribs, out, sumsq, accumulate=False, scale=1.0, n=None
     n = out.numel() if n is None else int(n)
     need = grad_sumsq_workspace_bytes(n)
     if workspace is None:
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=sumsq.device)
+        workspace = _call_workspace(need, sumsq.device, stream)
     wbytes = workspace.numel() * workspace.element_size()
     arr = _contrib_array(contribs, n)
     _check("reduce_shard_sumsq", lib().reduce_shard_sumsq(
