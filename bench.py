@@ -664,6 +664,12 @@ def main():
             "segments": L.n_segments,
             "storage": "bf16 grads and params, fp32 master/m/v",
             "algorithmic_bytes_per_param": bpp if args.path == "fused" else None,
+            # A step that re-read the bf16 parameters would move 2 more bytes per parameter
+            # (28 + 2F); the fused kernel writes them from the updated fp32 master instead, so
+            # the roofline above does not credit those bytes.
+            "bytes_per_param_with_param_reread": bpp + 2 if args.path == "fused" else None,
+            "GBps_with_param_reread": (round(L.n_real * (bpp + 2) / avg_kernel_s / 1e9, 1)
+                                       if args.path == "fused" else None),
             "achieved_GBps_wall": round(sum(x["algorithmic_bytes"] for x in stage_info)
                                         / (ms_per_step / 1e3) / 1e9, 1),
             "kernel_avg_ms": round(avg_kernel_s * 1e3, 4),
