@@ -128,3 +128,73 @@ def test_random_fused_steps(trial):
             g.assert_guards(what)
     finally:
         F.set_groups_per_wave(prev)
+
+
+@pytest.mark.parametrize("trial", range(24))
+def test_random_blocked_steps(trial):
+    """The same randomized cases through the blocked-state entry points (the layout the
+    benchmark times): bf16 contributions or an fp32 gradient shard, with or without clipping,
+    against the oracle; slots past n in the last block and every guard band stay untouched."""
+    c = _draw(random.Random(3000 + trial))
+    L, segs = F.shard_layout(c["sizes"], c["N"], c["k"], c["pad"], c["wd"])
+    lo, hi, osegs = OL.segments(c["sizes"], c["pad"], c["wd"], c["N"], c["k"])
+    assert (L.lo, L.hi) == (lo, hi)
+    n = hi - lo
+    flags = np.zeros(n, dtype=np.int64)
+    for s in osegs:
+        flags[s["shard_begin"]: s["shard_begin"] + s["length"]] = s["flags"]
+    real = (flags & OL.PADDING) == 0
+    F_in, hp, clip, d = c["F_in"], c["hp"], c["clip"], c["d"]
+    say(f"random blocked trial {trial}: n={n} lo={lo} segs={L.n_segments} F={F_in} clip={clip} "
+        f"d={d} hp={hp}")
+    sd = F.segments_to_device(segs)
+    seed = 7000 + trial
+    master0 = W.np_f32_normal([seed, 1], n, 0.02)
+    m0 = W.np_f32_normal([seed, 2], n, 1e-3)
+    v0 = (np.abs(W.np_f32_normal([seed, 3], n, 1e-3)) ** 2).astype(np.float32)
+    unused = 0x7FB0B0B0
+    blk = Guarded(OL.to_blocked(master0, m0, v0, fill=np.uint32(unused).view(np.float32)))
+    flat = Guarded(np.zeros(n, np.uint16), pre=d)
+    om, omm, ov = master0.copy(), m0.copy(), v0.copy()
+    sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for t in (1, 2):
+        ohp = dict(hp)
+        kw = dict(step=t, segs=sd, n_segments=L.n_segments, flat=flat.window(),
+                  flat_index0=lo - d, lo=lo, **hp)
+        if F_in == -1:
+            grad = W.np_f32_normal([seed, 10 + t], n, 1e-2)
+            grad[~real] = np.nan
+            gdev = torch.from_numpy(grad).cuda()
+            if clip:
+                F.grad_sumsq_shard(sumsq, grad=gdev, n=n, scale=hp["grad_scale"], segs=sd,
+                                   n_segments=L.n_segments)
+                osum = OC.sumsq_exact(grad * np.float32(hp["grad_scale"]), real)
+                ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
+            F.adamw_shard_step_f32grad_blocked(blk.data(), gdev, n=n, **kw)
+            om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, grad, flags, ohp, t)
+        else:
+            contribs = [W.np_bf16_normal([seed, 20 + t, r], n, 1e-2) for r in range(F_in)]
+            for cb in contribs:
+                cb[~real] = 0x7FC0
+            dev = [to_dev16(cb) for cb in contribs]
+            if clip:
+                F.grad_sumsq_shard(sumsq, contribs=dev, n=n, scale=hp["grad_scale"], segs=sd,
+                                   n_segments=L.n_segments)
+                osum = OC.grad_sumsq(contribs, real, hp["grad_scale"])
+                ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
+            F.adamw_shard_step_blocked(blk.data(), dev, n=n, **kw)
+            om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, ohp, t)
+        torch.cuda.synchronize()
+        gm, gmm, gv = OL.from_blocked(blk.data_host(), n)
+        assert_f32(gm, om, f"master step {t}")
+        assert_f32(gmm, omm, f"m step {t}")
+        assert_f32(gv, ov, f"v step {t}")
+        assert_bf16(flat.data_host(), oout, f"bf16 step {t}")
+    st = blk.data_host().view(np.uint32)
+    used = OL.to_blocked(np.ones(n, np.float32), np.ones(n, np.float32), np.ones(n, np.float32),
+                         fill=0.0) != 0.0
+    assert (st[~used] == np.uint32(unused)).all(), "unused slots of the last block written"
+    blk.assert_guards("blocked state")
+    flat.assert_guards("flat window")
