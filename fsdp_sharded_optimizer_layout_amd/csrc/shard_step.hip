@@ -752,10 +752,23 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
     }
 }
 
+// Finish: thread t adds partials t, t + 256, t + 512, ... in that order, then the fixed wave and
+// work-group trees.  The loads go out 16 at a time ahead of their adds (the addition order is
+// unchanged), so a thread waits for memory once per 16 partials instead of once per partial.
+constexpr int kFinishBatch = 16;
+
 __global__ __launch_bounds__(kBlock) void sumsq_finish_kernel(SumsqParams p) {
     __shared__ double wave_part[kWavesPerBlock];
     double acc = 0.0;
-    for (int i = threadIdx.x; i < p.n_partials; i += kBlock) acc += p.partials[i];
+    int i = threadIdx.x;
+    for (; i + (kFinishBatch - 1) * kBlock < p.n_partials; i += kFinishBatch * kBlock) {
+        double x[kFinishBatch];
+#pragma unroll
+        for (int k = 0; k < kFinishBatch; ++k) x[k] = p.partials[i + k * kBlock];
+#pragma unroll
+        for (int k = 0; k < kFinishBatch; ++k) acc += x[k];
+    }
+    for (; i < p.n_partials; i += kBlock) acc += p.partials[i];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
     acc = wave_sum(acc);
