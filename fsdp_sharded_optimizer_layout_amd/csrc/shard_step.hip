@@ -760,7 +760,7 @@ constexpr int kFinishBatch = 16;
 __global__ __launch_bounds__(kBlock) void sumsq_finish_kernel(SumsqParams p) {
     __shared__ double wave_part[kWavesPerBlock];
     double acc = 0.0;
-    int i = threadIdx.x;
+    int64_t i = threadIdx.x;   // 64-bit: i + 15 * 256 stays exact for any partial count
     for (; i + (kFinishBatch - 1) * kBlock < p.n_partials; i += kFinishBatch * kBlock) {
         double x[kFinishBatch];
 #pragma unroll
