@@ -19,6 +19,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 COMMON = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", f"-I{os.path.join(ROOT, 'include')}"]
 # $ORIGIN-relative, so the binaries find the library wherever the repository is copied.
 LINK = [f"-L{PKG}", "-lfsdpshard", "-Wl,-rpath,$ORIGIN/../../../fsdp_sharded_optimizer_layout_amd"]
+# A plain C compiler must name the platform for the HIP runtime header (hipcc does it itself).
 HIP = ["-D__HIP_PLATFORM_AMD__", f"-isystem{os.path.join(ROCM, 'include')}"]
 HIP_LINK = [f"-L{os.path.join(ROCM, 'lib')}", "-lamdhip64", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"]
 
