@@ -137,6 +137,27 @@ def test_sumsq_fp32_grad_sizes(n):
     assert abs(got - want) <= SUMSQ_RTOL * want, (got, want)
 
 
+@pytest.mark.parametrize("blocks,tail", [(3840, 0), (3841, 1), (5000, 12345), (8192, 32767)])
+def test_sumsq_finish_over_many_partials(blocks, tail):
+    """Thousands of float64 partials, so the finish kernel's batched loads and its tail loop both
+    run.  Element i holds 2^-4 * (1 + (i // 32768) % 3): every square is a power-of-two multiple
+    of 2^-8, so the float64 sum is exact in any order and must equal sum(k^2) * 2^-8 bit for bit;
+    a partial dropped or added twice changes it."""
+    tile = 32768                               # elements per float64 partial
+    n = blocks * tile + tail
+    say(f"sumsq finish: n={n} partials={blocks + (tail > 0)}")
+    idx = torch.arange(n, device="cuda", dtype=torch.int64)
+    grad = ((idx // tile) % 3 + 1).to(torch.float32) * 0.0625
+    del idx
+    got = _gpu_sumsq(grad=grad, n=n)
+    k = np.arange(blocks + 1, dtype=np.int64) % 3 + 1
+    units = int((k[:blocks] ** 2).sum()) * tile + int(k[blocks] ** 2) * tail
+    want = math.ldexp(units, -8)
+    assert got == want, (got, want)
+    del grad
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("F_in", [-1, 1, 4, 8])
 def test_sumsq_padding_inside_whole_tiles(F_in):
     # 300 small tensors padded to 16 (padding every few hundred elements, NaN-filled) across
