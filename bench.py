@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of one rank's sharded AdamW step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path PATH]
+                    [--state blocked|separate] [--no-extra-workloads] [--no-copy-reference]
+                    [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over the rank's slice: the host layout call
 (shard_layout: flatten, floor-rule slice, segment table) and the fused GPU step
@@ -12,12 +14,17 @@ step.  The timed region is K steps bracketed by device synchronisation; each ker
 bracketed by HIP events on the stream it runs on, which gives the kernel's own average duration
 for the roofline figure.
 
+The default run times the 7B-shaped slice (the headline `value`), then, under "workloads", the
+70B-shaped, one-layer and 2,000-tensor slices and the separate-array entry point on the 7B-shaped
+slice, then the memory-system references under "ceiling", then the CPU oracle.
+
 Prints one JSON line (the last line of stdout).
 """
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -29,10 +36,14 @@ METRIC = "params updated/sec per GPU (sharded AdamW step); achieved HBM GB/s vs 
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 DEFAULT_WORKLOAD = "dense7b_n8_rank0"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc", "shard_step.hip")
-RESHARD_SOURCE = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc", "reshard.hip")
+CSRC = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc")
+KERNEL_SOURCE = [os.path.join(CSRC, "shard_step.hip"), os.path.join(CSRC, "stream_common.h")]
+RESHARD_SOURCE = os.path.join(CSRC, "reshard.hip")
 STEP_KERNEL = "void (anonymous namespace)::fused_step_kernel"
 RESHARD_KERNEL = "(anonymous namespace)::reshard_kernel"
+# Workloads measured after the headline in the default run: (name, blocked state layout).
+EXTRA_WORKLOADS = [("dense70b_n64_rank0", True), ("llama_layer_n8_rank0", True),
+                   ("many_small_n16_rank3", True), ("dense7b_n8_rank0", False)]
 
 
 def log(msg):
@@ -51,15 +62,22 @@ def algorithmic_bytes_per_param_f32grad():
 
 
 def source_digest(source=KERNEL_SOURCE):
-    """Digest of a kernel source with comments and whitespace removed: the counter figures stay
-    valid across comment edits and lapse with any change to the code."""
+    """Digest of kernel sources (a path or a list of paths) with comments and whitespace removed:
+    the counter figures stay valid across comment edits and lapse with any change to the code."""
     import re
-    with open(source) as f:
-        text = f.read()
+    paths = [source] if isinstance(source, str) else list(source)
+    text = ""
+    for path in paths:
+        with open(path) as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
     return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
+def traffic_key(workload, blocked=True):
+    return workload if blocked else f"{workload}:separate"
 
 
 def counter_traffic(key, source=KERNEL_SOURCE):
@@ -127,63 +145,23 @@ def summarize_counters(key, fetch_dir, write_dir, kernel_prefix=STEP_KERNEL, sou
     print(json.dumps(rec[key]))
 
 
-def cpu_baseline(workload, seconds=12.0, sample=1 << 21):
-    """The oracle as it is, single-threaded NumPy on the host, on the first `sample` elements of
-    the same workload's slice; repeated steps until about `seconds` of work."""
-    import numpy as np
-    import workloads as W
-    from oracle import layout as OL
-    from oracle import step as OS
+# ----------------------------------------------------------------------------- CPU oracle baseline
 
-    w = W.WORKLOADS[workload]
-    lo, hi, osegs = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
-    n = min(sample, hi - lo)
-    flags = np.zeros(n, dtype=np.int64)
-    for s in osegs:
-        a, b = s["shard_begin"], min(n, s["shard_begin"] + s["length"])
-        if a < n:
-            flags[a:b] = s["flags"]
-    master, m, v = W.np_state(w, n, 0)
-    grads = W.np_grads(w, n, 1, 0)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        steps += 1
-        master, m, v, out = OS.shard_step(master, m, v, grads, flags, w.hp, steps)
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    n_real = int(np.count_nonzero((flags & OL.PADDING) == 0))
-    return {"value": n_real * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} elements of the {workload} slice, fan-in {w.fan_in}, "
-                      f"{steps} oracle steps in {el:.1f} s (NumPy float32, one thread)"}
-
-
-def _oracle_chunk(args):
-    """Worker of the parallel baseline: the oracle on elements [a, b) of the sampled slice."""
-    workload, a, b, seconds = args
-    import numpy as np
-    import workloads as W
-    from oracle import layout as OL
-    from oracle import step as OS
-
-    w = W.WORKLOADS[workload]
-    lo, hi, osegs = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
-    flags = np.zeros(b - a, dtype=np.int64)
-    for s in osegs:
-        x, y = max(a, s["shard_begin"]), min(b, s["shard_begin"] + s["length"])
-        if x < y:
-            flags[x - a:y - a] = s["flags"]
-    master, m, v = W.np_state(w, b - a, a)
-    grads = W.np_grads(w, b - a, 1, a)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        steps += 1
-        master, m, v, _ = OS.shard_step(master, m, v, grads, flags, w.hp, steps)
-        if time.perf_counter() - t0 >= seconds:
-            break
-    return int(np.count_nonzero((flags & OL.PADDING) == 0)) * steps
+def host_cores():
+    """What the host offers this process: os.cpu_count(), the CPUs in its affinity mask, and the
+    cgroup CPU quota (cpu.max) if one is set.  `usable` is the smaller of the last two."""
+    n_os = os.cpu_count()
+    aff = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+        if q != "max":
+            quota = max(1, math.ceil(int(q) / int(period)))
+    except (OSError, ValueError):
+        pass
+    return {"os_cpu_count": n_os, "affinity": aff, "cgroup_quota": quota,
+            "usable": min(aff, quota) if quota else aff}
 
 
 def cpu_model():
@@ -197,10 +175,68 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline_parallel(workload, procs, seconds=12.0, chunk=1 << 20):
-    """The same oracle in `procs` processes, each stepping its own contiguous chunk of the slice
-    (valid because the step is elementwise once the layout is fixed).  Rate = all processes'
-    real parameters x steps / the wall time of the whole pool."""
+def _oracle_inputs(workload, a, b):
+    """Flags, initial state and one step's contributions for elements [a, b) of the slice."""
+    import numpy as np
+    import workloads as W
+    from oracle import layout as OL
+
+    w = W.WORKLOADS[workload]
+    lo, hi, osegs = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
+    flags = np.zeros(b - a, dtype=np.int64)
+    for s in osegs:
+        x, y = max(a, s["shard_begin"]), min(b, s["shard_begin"] + s["length"])
+        if x < y:
+            flags[x - a:y - a] = s["flags"]
+    master, m, v = W.np_state(w, b - a, a)
+    grads = W.np_grads(w, b - a, 1, a)
+    n_real = int(np.count_nonzero((flags & OL.PADDING) == 0))
+    return w, flags, master, m, v, grads, n_real
+
+
+def _oracle_steps(w, flags, master, m, v, grads, seconds):
+    """Oracle steps on one chunk until `seconds` have passed; returns (steps, elapsed)."""
+    from oracle import step as OS
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        steps += 1
+        master, m, v, _ = OS.shard_step(master, m, v, grads, flags, w.hp, steps)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return steps, el
+
+
+def cpu_baseline_single(workload, seconds=12.0, sample=1 << 26):
+    """The oracle as it is, single-threaded NumPy, on the first `sample` elements of the same
+    workload's slice (64 Mi elements: a working set far beyond the host's caches)."""
+    from oracle import layout as OL
+    import workloads as W
+
+    w0 = W.WORKLOADS[workload]
+    lo, hi, _ = OL.segments(w0.sizes, w0.pad_multiple, w0.wd_mask, w0.world_size, w0.rank)
+    n = min(sample, hi - lo)
+    w, flags, master, m, v, grads, n_real = _oracle_inputs(workload, 0, n)
+    steps, el = _oracle_steps(w, flags, master, m, v, grads, seconds)
+    return {"value": n_real * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"first {n} elements of the {workload} slice, fan-in {w.fan_in}, "
+                      f"{steps} oracle steps in {el:.1f} s (NumPy float32, one thread)"}
+
+
+def _oracle_worker(args):
+    workload, a, b, seconds, barrier, results = args
+    w, flags, master, m, v, grads, n_real = _oracle_inputs(workload, a, b)
+    barrier.wait()                     # every worker starts stepping at the same moment
+    steps, el = _oracle_steps(w, flags, master, m, v, grads, seconds)
+    results.put((n_real * steps, el))
+
+
+def cpu_baseline(workload, procs, seconds=12.0, chunk=1 << 22):
+    """The same oracle in `procs` processes, each stepping its own contiguous 4 Mi-element chunk
+    of the slice (valid because the step is elementwise once the layout is fixed).  The workers
+    draw their inputs, meet at a barrier, then step for `seconds`; rate = all workers' real
+    parameters x steps / the longest worker's stepping time."""
     import multiprocessing as mp
 
     import workloads as W
@@ -210,35 +246,510 @@ def cpu_baseline_parallel(workload, procs, seconds=12.0, chunk=1 << 20):
     lo, hi, _ = OL.segments(w.sizes, w.pad_multiple, w.wd_mask, w.world_size, w.rank)
     n = hi - lo
     procs = max(1, min(procs, n // chunk if n >= chunk else 1))
-    jobs = [(workload, i * chunk, min(n, (i + 1) * chunk), seconds) for i in range(procs)]
     ctx = mp.get_context("spawn")
-    t0 = time.perf_counter()
-    with ctx.Pool(procs) as pool:
-        done = sum(pool.map(_oracle_chunk, jobs))
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "params/s", "cores": procs, "kind": "oracle",
-            "cpu": cpu_model(),
-            "sample": f"{procs} processes, each stepping the oracle on its own "
-                      f"{chunk}-element chunk of the {workload} slice for about {seconds:.0f} s "
-                      f"(NumPy float32); rate over the pool's wall time including start-up"}
+    barrier, results = ctx.Barrier(procs), ctx.Queue()
+    workers = [ctx.Process(target=_oracle_worker,
+                           args=((workload, i * chunk, min(n, (i + 1) * chunk), seconds, barrier,
+                                  results),))
+               for i in range(procs)]
+    for p in workers:
+        p.start()
+    done = [results.get() for _ in workers]
+    for p in workers:
+        p.join()
+    total = sum(d[0] for d in done)
+    el = max(d[1] for d in done)
+    cores = host_cores()
+    return {"value": total / el, "unit": "params/s", "cores": procs, "kind": "oracle",
+            "cpu": cpu_model(), "host": cores,
+            "sample": f"{procs} processes (one per usable host core: {cores['affinity']} CPUs in "
+                      f"the affinity mask, cgroup quota {cores['cgroup_quota']}, os.cpu_count() "
+                      f"{cores['os_cpu_count']}), each stepping the oracle on its own "
+                      f"{chunk}-element chunk of the {workload} slice for {seconds:.0f} s "
+                      f"(NumPy float32, one thread each)"}
 
+
+# ----------------------------------------------------------------------------- GPU measurement
+
+class Slice:
+    """Device buffers of one workload's slice: state (blocked or separate), F contributions,
+    the bf16 flat window and the segment table."""
+
+    def __init__(self, F, W, torch, name, blocked, dev):
+        w = W.WORKLOADS[name]
+        self.w, self.blocked, self.dev = w, blocked, dev
+        self.L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
+        n, lo = self.L.n, self.L.lo
+        master, m, v = W.torch_state(w, n, 0, dev)
+        self.grads = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(w.fan_in)]
+        W.torch_grads_into(w, self.grads, 1, 0)
+        if w.nan_padding_grads:
+            for s in segs:
+                if s["flags"] & F.SEG_PADDING:
+                    for g in self.grads:
+                        g[int(s["shard_begin"]): int(s["shard_begin"] + s["length"])] = 0x7FC0
+        self.phase = lo % 8
+        self.flat = torch.empty(n + self.phase, dtype=torch.int16, device=dev)
+        self.segs_dev = F.segments_to_device(segs, dev)
+        if blocked:
+            self.state = torch.empty(F.state_blocked_elems(n), dtype=torch.float32, device=dev)
+            F.state_to_blocked(master, m, v, self.state)
+            torch.cuda.synchronize()
+            del master, m, v
+            self.master = self.m = self.v = None
+        else:
+            self.state = None
+            self.master, self.m, self.v = master, m, v
+        torch.cuda.synchronize()
+
+    def common(self, stream):
+        L = self.L
+        return dict(segs=self.segs_dev, n_segments=L.n_segments, flat=self.flat,
+                    flat_index0=L.lo - self.phase, lo=L.lo, stream=stream, **self.w.hp)
+
+    def step_bf16(self, F, t, **kw):
+        if self.blocked:
+            F.adamw_shard_step_blocked(self.state, self.grads, step=t, n=self.L.n, **kw)
+        else:
+            F.adamw_shard_step(self.master, self.m, self.v, self.grads, step=t, **kw)
+
+    def step_f32(self, F, acc, t, **kw):
+        if self.blocked:
+            F.adamw_shard_step_f32grad_blocked(self.state, acc, step=t, n=self.L.n, **kw)
+        else:
+            F.adamw_shard_step_f32grad(self.master, self.m, self.v, acc, step=t, **kw)
+
+
+def build_stages(F, torch, S, path, stream, args):
+    """Stages of one step: (name, launch(t), algorithmic bytes per launch)."""
+    L, n, Fi, dev = S.L, S.L.n, S.w.fan_in, S.dev
+    bpp = algorithmic_bytes_per_param(Fi)
+    common = S.common(stream)
+    stages = []
+    suffix = "_blocked" if S.blocked else ""
+    if path == "fused":
+        stages.append(("adamw_shard_step" + suffix, lambda t: S.step_bf16(F, t, **common),
+                       L.n_real * bpp))
+    elif path == "split":
+        no_out = {k: v for k, v in common.items() if k not in ("flat", "flat_index0", "lo")}
+        stages.append(("adamw_shard_step (no bf16 output)", lambda t: F.adamw_shard_step(
+            S.master, S.m, S.v, S.grads, step=t, **no_out), L.n_real * (bpp - 2)))
+        stages.append(("unflatten_bf16", lambda t: F.unflatten_bf16(
+            S.master, S.flat, flat_index0=L.lo - S.phase, lo=L.lo, segs=S.segs_dev,
+            n_segments=L.n_segments, stream=stream), L.n_real * 4 + n * 2))
+    else:
+        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        ws = torch.empty(max(8, F.grad_sumsq_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+        segkw = dict(segs=S.segs_dev, n_segments=L.n_segments, workspace=ws, stream=stream)
+        clip = dict(max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq)
+        f32_bytes = L.n_real * algorithmic_bytes_per_param_f32grad()
+        if path == "clipped":
+            stages.append(("grad_sumsq_shard", lambda t: F.grad_sumsq_shard(
+                sumsq, contribs=S.grads, n=n, **segkw), n * 2 * Fi))
+            stages.append(("adamw_shard_step" + suffix + " (clipped)", lambda t: S.step_bf16(
+                F, t, **clip, **common), L.n_real * bpp))
+        elif path == "clipped32":
+            acc = torch.empty(n, dtype=torch.float32, device=dev)
+            stages.append(("reduce_shard_sumsq", lambda t: F.reduce_shard_sumsq(
+                S.grads, acc, sumsq, **segkw), n * (2 * Fi + 4)))
+            stages.append(("adamw_shard_step_f32grad" + suffix + " (clipped)", lambda t: S.step_f32(
+                F, acc, t, **clip, **common), f32_bytes))
+        else:   # accumulate
+            acc = torch.empty(n, dtype=torch.float32, device=dev)
+            stages.append(("reduce_shard", lambda t: F.reduce_shard(S.grads, acc, stream=stream),
+                           n * (2 * Fi + 4)))
+            for mb in range(1, args.micro_batches - 1):
+                stages.append((f"reduce_shard_accumulate[{mb}]", lambda t: F.reduce_shard_accumulate(
+                    S.grads, acc, stream=stream), n * (2 * Fi + 8)))
+            if args.micro_batches > 1:
+                stages.append((f"reduce_shard_sumsq (accumulate)[{args.micro_batches - 1}]",
+                               lambda t: F.reduce_shard_sumsq(S.grads, acc, sumsq, accumulate=True,
+                                                              **segkw), n * (2 * Fi + 8)))
+            else:
+                stages.append(("grad_sumsq_shard (fp32)", lambda t: F.grad_sumsq_shard(
+                    sumsq, grad=acc, n=n, **segkw), n * 4))
+            stages.append(("adamw_shard_step_f32grad" + suffix + " (clipped)", lambda t: S.step_f32(
+                F, acc, t, **clip, **common), f32_bytes))
+    return stages
+
+
+def make_evict(torch, dev, step_bytes, evict_mb):
+    """A 1 GiB buffer written between timed steps of workloads that move under 2 GB per step, so
+    the 256 MB last-level cache holds none of the step's data when the next one starts."""
+    mb = evict_mb if evict_mb >= 0 else (1024 if step_bytes < 2e9 else 0)
+    return mb, (torch.zeros(mb << 18, dtype=torch.float32, device=dev) if mb else None)
+
+
+def time_stages(F, torch, S, stages, stream, steps, warmup, evict):
+    """W warm-up steps, then `steps` timed steps (host layout call + every stage), each stage
+    bracketed by HIP events on `stream`."""
+    w = S.w
+
+    def one_step(t, ev=None):
+        if evict is not None:
+            evict.add_(1.0)   # outside the kernel events: flushes the last-level cache
+        F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
+        for i, (_, launch, _) in enumerate(stages):
+            if ev is not None:
+                ev[i][0].record(stream)
+            launch(t)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    for t in range(1, warmup + 1):
+        one_step(t)
+    torch.cuda.synchronize()
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in stages] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(warmup + 1 + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [sum(events[i][j][0].elapsed_time(events[i][j][1]) for j in range(len(stages)))
+               for i in range(steps)]
+    if evict is None:
+        ms_per_step = wall / steps * 1e3
+        timing = "wall clock over the timed steps"
+    else:
+        ms_per_step = sum(step_ms) / len(step_ms)
+        timing = (f"sum of each step's HIP-event kernel times; {evict.numel() >> 18} MiB written "
+                  "between steps to flush the last-level cache")
+    info = []
+    for j, (name, _, nbytes) in enumerate(stages):
+        ms = [events[i][j][0].elapsed_time(events[i][j][1]) for i in range(steps)]
+        avg = sum(ms) / len(ms)
+        info.append({"call": name, "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4),
+                     "median_ms": round(sorted(ms)[len(ms) // 2], 4),
+                     "algorithmic_bytes": nbytes, "GBps": round(nbytes / (avg / 1e3) / 1e9, 1)})
+    return {"ms_per_step": ms_per_step, "step_ms": step_ms, "stages": info, "timing": timing}
+
+
+def time_launches(torch, launch, stream, reps=5, warm=2, evict=None):
+    """Average HIP-event time of `launch` (per launch when a flush runs between launches)."""
+    for _ in range(warm):
+        launch()
+    torch.cuda.synchronize()
+    if evict is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    total = 0.0
+    for _ in range(reps):
+        evict.add_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+    return total / reps
+
+
+def mix_references(F, torch, S, stream, evict, phased=False):
+    """The step's loads and stores with trivial arithmetic on this slice's own buffers: in the
+    step's order (same grid, tile map and work-groups per CU), and, with `phased`, each
+    work-group's reads and writes in separate phases (blocked state only)."""
+    n8 = S.L.n - S.L.n % 8
+    if n8 == 0:
+        return None
+    bpp = algorithmic_bytes_per_param(S.w.fan_in)
+    out16 = (S.flat[S.phase:S.phase + n8] if S.phase == 0
+             else torch.empty(n8, dtype=torch.int16, device=S.dev))
+    if S.blocked:
+        mix = lambda: F.stream_mix_blocked(S.grads, S.state, out16, n8, stream=stream)
+    else:
+        mix = lambda: F.stream_mix(S.grads, S.master, S.m, S.v, out16, n=n8, stream=stream)
+    ms = time_launches(torch, mix, stream, evict=evict)
+    ref = {"step_order": {"GBps": round(n8 * bpp / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4),
+                          "kernel": "fsdpshard_stream_mix" + ("_blocked" if S.blocked else "")},
+           "flushed": evict is not None}
+    if phased and S.blocked and S.w.fan_in in (1, 4, 8):
+        for G, per_cu in ((1, 2), (2, 1), (2, 2), (4, 1)):
+            ms = time_launches(torch, lambda: F.stream_mix_phased(
+                S.grads, S.state, out16, n8, G, per_cu, stream=stream), stream, evict=evict)
+            ref[f"phased_g{G}_cu{per_cu}"] = {
+                "GBps": round(n8 * bpp / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4),
+                "kernel": f"fsdpshard_stream_mix_phased ({G} groups per wave, {per_cu} "
+                          "work-groups per CU)"}
+    del out16
+    return ref
+
+
+def measure_workload(F, W, torch, name, blocked, args, dev, stream, mix=True):
+    """The fused step of one workload: its stage timing, roofline figures and (like for like,
+    flushed when the step is) the traffic replica."""
+    S = Slice(F, W, torch, name, blocked, dev)
+    stages = build_stages(F, torch, S, "fused", stream, args)
+    evict_mb, evict = make_evict(torch, dev, stages[0][2], args.evict_mb)
+    r = time_stages(F, torch, S, stages, stream, args.steps, args.warmup, evict)
+    st = r["stages"][0]
+    bpp = algorithmic_bytes_per_param(S.w.fan_in)
+    gbps = st["algorithmic_bytes"] / (st["avg_ms"] / 1e3) / 1e9
+    out = {"workload": name,
+           "state_layout": "blocked" if blocked else "separate master, m, v arrays",
+           "call": st["call"], "fan_in": S.w.fan_in, "slice_elems": S.L.n,
+           "real_params": S.L.n_real, "segments": S.L.n_segments, "dest_phase": S.phase,
+           "algorithmic_bytes_per_param": bpp,
+           "kernel_avg_ms": st["avg_ms"], "kernel_min_ms": st["min_ms"],
+           "ms_per_step": round(r["ms_per_step"], 4),
+           "params_per_s": round(S.L.n_real / (r["ms_per_step"] / 1e3), 1),
+           "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "traffic": counter_traffic(traffic_key(name, blocked)),
+           "timing": r["timing"]}
+    if mix and not args.no_copy_reference:
+        out["mix_reference"] = mix_references(F, torch, S, stream, evict)
+    del S, evict
+    torch.cuda.empty_cache()
+    return out
+
+
+def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=4 << 30):
+    """What the memory system does for plain streams on this GPU: pure reads, pure writes, a
+    copy, and the step's 2 : 1 read : write byte ratio, each with and without a cap of 2
+    work-groups per CU (best reported), plus the time bound they imply for the step's bytes."""
+    bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for b in bufs:
+        b.fill_(1.0)
+    A, B, C = bufs
+    cases = {"read": ([A, B], [], 2 * nbytes), "write": ([], [A, B], 2 * nbytes),
+             "copy": ([A], [B], 2 * nbytes), "read2_write1": ([A, B], [C], 3 * nbytes)}
+    out = {}
+    for name, (srcs, dsts, moved) in cases.items():
+        best = None
+        for per_cu in (0, 2):
+            ms = time_launches(torch, lambda: F.stream_rw(srcs, dsts, nbytes, per_cu=per_cu,
+                                                          sink=sink, stream=stream),
+                               stream, reps=10)
+            gbps = moved / (ms / 1e3) / 1e9
+            if best is None or gbps > best["GBps"]:
+                best = {"GBps": round(gbps, 1), "per_cu": per_cu}
+        out[name] = best
+        log(f"  {name}: {best['GBps']} GB/s (work-groups per CU {best['per_cu'] or 'uncapped'})")
+    ms = time_launches(torch, lambda: F.stream_copy(A, B, stream=stream), stream, reps=10)
+    out["copy_plain"] = {"GBps": round(2 * nbytes / (ms / 1e3) / 1e9, 1),
+                         "kernel": "fsdpshard_stream_copy (the counters' calibration kernel)"}
+    # If a channel could only read at the pure-read rate and write at the pure-write rate, one
+    # after the other, the step's bytes would need at least this long.
+    t = read_bytes / (out["read"]["GBps"] * 1e9) + write_bytes / (out["write"]["GBps"] * 1e9)
+    out["serial_rw_bound"] = {
+        "GBps": round((read_bytes + write_bytes) / t / 1e9, 1),
+        "read_bytes": read_bytes, "write_bytes": write_bytes,
+        "meaning": "the step's read and write bytes at the pure-read and pure-write rates, one "
+                   "after the other"}
+    del bufs, A, B, C, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--path", choices=["fused", "clipped", "clipped32", "accumulate", "split",
+                                       "reshard"],
+                    default="fused",
+                    help="fused: the fused step (default); clipped: sum of squares + clipped "
+                         "step; clipped32: reduction fused with the sum of squares into an fp32 "
+                         "shard + clipped fp32-gradient step; accumulate: fp32 micro-batch "
+                         "accumulation (the last fused with the sum of squares) + clipped fp32 "
+                         "step; split: the step without its bf16 output, then unflatten_bf16; "
+                         "reshard: move one destination rank's fp32 master/m/v to another "
+                         "world size and padding multiple")
+    ap.add_argument("--reshard-world", type=int, default=6,
+                    help="reshard path: destination world size")
+    ap.add_argument("--reshard-pad", type=int, default=0,
+                    help="reshard path: destination padding multiple (0 = the workload's)")
+    ap.add_argument("--reshard-rank", type=int, default=1,
+                    help="reshard path: destination rank")
+    ap.add_argument("--micro-batches", type=int, default=4)
+    ap.add_argument("--state", choices=["blocked", "separate"], default="blocked",
+                    help="optimizer-state layout: one array of 512-element blocks of master, m "
+                         "and v (default), or three separate arrays (the split path always uses "
+                         "separate arrays)")
+    ap.add_argument("--max-grad-norm", type=float, default=1.0)
+    ap.add_argument("--evict-mb", type=int, default=-1,
+                    help="MiB written between timed steps to flush the 256 MB last-level cache "
+                         "(-1: 1024 when one step moves under 2 GB, else 0); with eviction the "
+                         "per-step time is the sum of the step's HIP-event kernel times")
+    ap.add_argument("--cpu-procs", type=int, default=0,
+                    help="processes for the parallel oracle baseline (0: one per usable host "
+                         "core; -1: skip it)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-reference", action="store_true",
+                    help="skip the traffic replicas and the memory-system references")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="time only the selected workload")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+    args = ap.parse_args()
+    if args.summarize_counters:
+        if args.path == "reshard":
+            import workloads as W
+            w = W.WORKLOADS[args.workload]
+            key = reshard_key(w.name, args.reshard_world, args.reshard_pad or w.pad_multiple,
+                              args.reshard_rank)
+            summarize_counters(key, *args.summarize_counters, kernel_prefix=RESHARD_KERNEL,
+                               source=RESHARD_SOURCE)
+        else:
+            summarize_counters(traffic_key(args.workload, args.state == "blocked"),
+                               *args.summarize_counters)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: it times one rank's slice on a single MI355X and "
+              "has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fsdp_sharded_optimizer_layout_amd as F
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    F.lib()  # fail loudly if the library is missing
+
+    w = W.WORKLOADS[args.workload]
+    if args.path == "reshard":
+        bench_reshard(args, w, F, W, torch)
+        return
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    blocked = args.state == "blocked" and args.path != "split"
+    S = Slice(F, W, torch, w.name, blocked, dev)
+    L, Fi = S.L, w.fan_in
+    log(f"workload {w.name}: P={L.P} slice [{L.lo}, {L.hi}) n={L.n} n_real={L.n_real} "
+        f"F={Fi} segments={L.n_segments}")
+    bpp = algorithmic_bytes_per_param(Fi)
+    stages = build_stages(F, torch, S, args.path, stream, args)
+    step_bytes = sum(b for _, _, b in stages)
+    evict_mb, evict = make_evict(torch, dev, step_bytes, args.evict_mb)
+    r = time_stages(F, torch, S, stages, stream, args.steps, args.warmup, evict)
+    ms_per_step, stage_info = r["ms_per_step"], r["stages"]
+    main_stage = max(stage_info, key=lambda x: x["avg_ms"])
+    avg_kernel_s = main_stage["avg_ms"] / 1e3
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; kernel avg "
+        f"{avg_kernel_s * 1e3:.3f} ms")
+    for x in stage_info:
+        log(f"  {x['call']}: {x['avg_ms']:.3f} ms, {x['GBps']} GB/s")
+    achieved = main_stage["algorithmic_bytes"] / avg_kernel_s / 1e9
+    traffic = counter_traffic(traffic_key(w.name, blocked)) if args.path == "fused" else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic}
+
+    mix_ref = None
+    if not args.no_copy_reference and args.path == "fused":
+        mix_ref = mix_references(F, torch, S, stream, evict, phased=True)
+        for k, x in (mix_ref or {}).items():
+            if isinstance(x, dict):
+                log(f"  traffic replica {k}: {x['GBps']} GB/s")
+    read_bytes = L.n_real * (2 * Fi + 12)
+    write_bytes = L.n_real * 14
+    del S, stages, evict
+    torch.cuda.empty_cache()
+
+    extra = None
+    if args.path == "fused" and not args.no_extra_workloads:
+        extra = []
+        for name, blk in EXTRA_WORKLOADS:
+            if name == w.name and blk == blocked:
+                continue
+            x = measure_workload(F, W, torch, name, blk, args, dev, stream)
+            log(f"workload {name} ({x['state_layout']}): {x['kernel_avg_ms']:.4f} ms, "
+                f"{x['GBps']} GB/s, frac {x['frac']}")
+            extra.append(x)
+
+    ceiling = None
+    if not args.no_copy_reference:
+        log("memory-system references:")
+        ceiling = ceiling_references(F, torch, dev, stream, read_bytes, write_bytes)
+
+    cpu = cpu_single = None
+    if not args.no_cpu_baseline:
+        cores = host_cores()
+        procs = args.cpu_procs if args.cpu_procs > 0 else cores["usable"]
+        log(f"timing the CPU oracle (host cores {cores}) ...")
+        cpu_single = cpu_baseline_single(w.name)
+        log(f"cpu oracle, one thread: {cpu_single['value']:.3e} params/s")
+        if args.cpu_procs >= 0:
+            cpu = cpu_baseline(w.name, procs)
+            log(f"cpu oracle, {cpu['cores']} processes: {cpu['value']:.3e} params/s")
+        else:
+            cpu = cpu_single
+
+    value = L.n_real / (ms_per_step / 1e3)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "flat_params": L.P,
+            "world_size": w.world_size,
+            "rank": w.rank,
+            "slice_elems": L.n,
+            "real_params": L.n_real,
+            "fan_in": Fi,
+            "segments": L.n_segments,
+            "storage": "bf16 grads and params, fp32 master/m/v",
+            "algorithmic_bytes_per_param": bpp if args.path == "fused" else None,
+            # A step that re-read the bf16 parameters would move 2 more bytes per parameter
+            # (28 + 2F); the fused kernel writes them from the updated fp32 master instead, so
+            # the roofline above does not credit those bytes.
+            "bytes_per_param_with_param_reread": bpp + 2 if args.path == "fused" else None,
+            "GBps_with_param_reread": (round(L.n_real * (bpp + 2) / avg_kernel_s / 1e9, 1)
+                                       if args.path == "fused" else None),
+            "achieved_GBps_wall": round(sum(x["algorithmic_bytes"] for x in stage_info)
+                                        / (ms_per_step / 1e3) / 1e9, 1),
+            "kernel_avg_ms": round(avg_kernel_s * 1e3, 4),
+            "step_ms_median": round(sorted(r["step_ms"])[len(r["step_ms"]) // 2], 4),
+            "step_ms_min": round(min(r["step_ms"]), 4),
+            "timing": r["timing"],
+            "path": args.path,
+            "state_layout": ("blocked: one array, 512-element blocks of master, m, v" if blocked
+                             else "separate master, m, v arrays"),
+            "stages": stage_info,
+        },
+        "roofline": roofline,
+        "workloads": extra,
+        "mix_reference": mix_ref,
+        "ceiling": ceiling,
+        "cpu_baseline": cpu,
+        "cpu_baseline_single_thread": cpu_single,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+# ----------------------------------------------------------------------------- reshard path
 
 def copy_reference(F, torch, dev, stream, nbytes=4 << 30):
     """Plain 16-byte copy of nbytes (non-temporal loads and stores): the bandwidth a pure
     read+write stream reaches, and the calibration kernel of the counter runs."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        F.stream_copy(src, dst, stream=stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    reps = 10
-    for _ in range(reps):
-        F.stream_copy(src, dst, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = a.elapsed_time(b) / reps
-    ref = {"GBps": round(2 * nbytes / (copy_ms / 1e3) / 1e9, 1), "bytes_moved": 2 * nbytes,
+    ms = time_launches(torch, lambda: F.stream_copy(src, dst, stream=stream), stream, reps=10,
+                       warm=3)
+    ref = {"GBps": round(2 * nbytes / (ms / 1e3) / 1e9, 1), "bytes_moved": 2 * nbytes,
            "kernel": "fsdpshard_stream_copy (16-byte loads and stores)"}
     log(f"copy reference: {ref['GBps']} GB/s")
     del src, dst
@@ -370,325 +881,6 @@ def bench_reshard(args, w, F, W, torch):
     }
     print(json.dumps(rec), flush=True)
 
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--groups-per-wave", type=int, default=0,
-                    help="512-element groups per wavefront (1, 2, 4; 0 = library default)")
-    ap.add_argument("--path", choices=["fused", "clipped", "clipped32", "accumulate", "split",
-                                       "reshard"],
-                    default="fused",
-                    help="fused: the fused step (default); clipped: sum of squares + clipped "
-                         "step; clipped32: reduction fused with the sum of squares into an fp32 "
-                         "shard + clipped fp32-gradient step; accumulate: fp32 micro-batch "
-                         "accumulation (the last fused with the sum of squares) + clipped fp32 "
-                         "step; "
-                         "split: the step without its bf16 output, then unflatten_bf16; "
-                         "reshard: move one destination rank's fp32 master/m/v to another "
-                         "world size and padding multiple")
-    ap.add_argument("--reshard-world", type=int, default=6,
-                    help="reshard path: destination world size")
-    ap.add_argument("--reshard-pad", type=int, default=0,
-                    help="reshard path: destination padding multiple (0 = the workload's)")
-    ap.add_argument("--reshard-rank", type=int, default=1,
-                    help="reshard path: destination rank")
-    ap.add_argument("--micro-batches", type=int, default=4)
-    ap.add_argument("--state", choices=["blocked", "separate"], default="blocked",
-                    help="optimizer-state layout: one array of 512-element blocks of master, m "
-                         "and v (default), or three separate arrays (the split path always uses "
-                         "separate arrays)")
-    ap.add_argument("--max-grad-norm", type=float, default=1.0)
-    ap.add_argument("--evict-mb", type=int, default=-1,
-                    help="MiB written between timed steps to flush the 256 MB last-level cache "
-                         "(-1: 1024 when one step moves under 2 GB, else 0); with eviction the "
-                         "per-step time is the sum of the step's HIP-event kernel times")
-    ap.add_argument("--cpu-procs", type=int, default=16,
-                    help="processes for the parallel oracle baseline (0: skip it)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-copy-reference", action="store_true")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
-    args = ap.parse_args()
-    if args.summarize_counters:
-        if args.path == "reshard":
-            import workloads as W
-            w = W.WORKLOADS[args.workload]
-            key = reshard_key(w.name, args.reshard_world, args.reshard_pad or w.pad_multiple,
-                              args.reshard_rank)
-            summarize_counters(key, *args.summarize_counters, kernel_prefix=RESHARD_KERNEL,
-                               source=RESHARD_SOURCE)
-        else:
-            summarize_counters(args.workload, *args.summarize_counters)
-        return
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: it times one rank's slice on a single MI355X and "
-              "has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import fsdp_sharded_optimizer_layout_amd as F
-    import workloads as W
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    F.lib()  # fail loudly if the library is missing
-    if args.groups_per_wave:
-        F.set_groups_per_wave(args.groups_per_wave)
-
-    w = W.WORKLOADS[args.workload]
-    if args.path == "reshard":
-        bench_reshard(args, w, F, W, torch)
-        return
-    L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
-    n, lo, Fi = L.n, L.lo, w.fan_in
-    log(f"workload {w.name}: P={L.P} slice [{L.lo}, {L.hi}) n={n} n_real={L.n_real} "
-        f"F={Fi} segments={L.n_segments}")
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    master, m, v = W.torch_state(w, n, 0, dev)
-    grads = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(Fi)]
-    W.torch_grads_into(w, grads, 1, 0)
-    if w.nan_padding_grads:
-        for s in segs:
-            if s["flags"] & F.SEG_PADDING:
-                for g in grads:
-                    g[int(s["shard_begin"]): int(s["shard_begin"] + s["length"])] = 0x7FC0
-    phase = lo % 8
-    flat = torch.empty(n + phase, dtype=torch.int16, device=dev)
-    segs_dev = F.segments_to_device(segs, dev)
-    blocked = args.state == "blocked" and args.path != "split"
-    if blocked:
-        state = torch.empty(F.state_blocked_elems(n), dtype=torch.float32, device=dev)
-        F.state_to_blocked(master, m, v, state)
-        torch.cuda.synchronize()
-        del master, m, v
-
-        def step_bf16(t, **kw):
-            F.adamw_shard_step_blocked(state, grads, step=t, n=n, **kw)
-
-        def step_f32(acc, t, **kw):
-            F.adamw_shard_step_f32grad_blocked(state, acc, step=t, n=n, **kw)
-    else:
-        def step_bf16(t, **kw):
-            F.adamw_shard_step(master, m, v, grads, step=t, **kw)
-
-        def step_f32(acc, t, **kw):
-            F.adamw_shard_step_f32grad(master, m, v, acc, step=t, **kw)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    bpp = algorithmic_bytes_per_param(Fi)
-    common = dict(segs=segs_dev, n_segments=L.n_segments, flat=flat, flat_index0=lo - phase,
-                  lo=lo, stream=stream, **w.hp)
-
-    # Stages of one step: (name, launch(t), algorithmic bytes per launch).  The fused path is the
-    # default; the clipped and accumulate paths measure the clipping and micro-batch rows.
-    stages = []
-    if args.path == "fused":
-        stages.append(("adamw_shard_step" + ("_blocked" if blocked else ""),
-                       lambda t: step_bf16(t, **common), L.n_real * bpp))
-    elif args.path == "split":
-        no_out = {k: v for k, v in common.items() if k not in ("flat", "flat_index0", "lo")}
-        stages.append(("adamw_shard_step (no bf16 output)", lambda t: F.adamw_shard_step(
-            master, m, v, grads, step=t, **no_out), L.n_real * (bpp - 2)))
-        stages.append(("unflatten_bf16", lambda t: F.unflatten_bf16(
-            master, flat, flat_index0=lo - phase, lo=lo, segs=segs_dev,
-            n_segments=L.n_segments, stream=stream), L.n_real * 4 + n * 2))
-    else:
-        sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
-        ws = torch.empty(max(8, F.grad_sumsq_workspace_bytes(n)), dtype=torch.uint8, device=dev)
-        if args.path == "clipped":
-            stages.append(("grad_sumsq_shard", lambda t: F.grad_sumsq_shard(
-                sumsq, contribs=grads, n=n, segs=segs_dev, n_segments=L.n_segments,
-                workspace=ws, stream=stream), n * 2 * Fi))
-            stages.append(("adamw_shard_step (clipped)", lambda t: step_bf16(
-                t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq, **common), L.n_real * bpp))
-        elif args.path == "clipped32":
-            acc = torch.empty(n, dtype=torch.float32, device=dev)
-            stages.append(("reduce_shard_sumsq", lambda t: F.reduce_shard_sumsq(
-                grads, acc, sumsq, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
-                stream=stream), n * (2 * Fi + 4)))
-            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: step_f32(
-                acc, t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq, **common),
-                L.n_real * algorithmic_bytes_per_param_f32grad()))
-        else:
-            acc = torch.empty(n, dtype=torch.float32, device=dev)
-            stages.append(("reduce_shard", lambda t: F.reduce_shard(grads, acc, stream=stream),
-                           n * (2 * Fi + 4)))
-            for mb in range(1, args.micro_batches - 1):
-                stages.append((f"reduce_shard_accumulate[{mb}]", lambda t: F.reduce_shard_accumulate(
-                    grads, acc, stream=stream), n * (2 * Fi + 8)))
-            if args.micro_batches > 1:
-                stages.append((f"reduce_shard_sumsq (accumulate)[{args.micro_batches - 1}]",
-                               lambda t: F.reduce_shard_sumsq(
-                                   grads, acc, sumsq, accumulate=True, segs=segs_dev,
-                                   n_segments=L.n_segments, workspace=ws, stream=stream),
-                               n * (2 * Fi + 8)))
-            else:
-                stages.append(("grad_sumsq_shard (fp32)", lambda t: F.grad_sumsq_shard(
-                    sumsq, grad=acc, n=n, segs=segs_dev, n_segments=L.n_segments, workspace=ws,
-                    stream=stream), n * 4))
-            stages.append(("adamw_shard_step_f32grad (clipped)", lambda t: step_f32(
-                acc, t, max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq, **common),
-                L.n_real * algorithmic_bytes_per_param_f32grad()))
-
-    step_bytes = sum(b for _, _, b in stages)
-    evict_mb = args.evict_mb if args.evict_mb >= 0 else (1024 if step_bytes < 2e9 else 0)
-    evict = (torch.zeros(evict_mb << 18, dtype=torch.float32, device=dev) if evict_mb
-             else None)
-
-    def one_step(t, ev=None):
-        if evict is not None:
-            evict.add_(1.0)   # outside the kernel events: flushes the last-level cache
-        F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
-        for i, (_, launch, _) in enumerate(stages):
-            if ev is not None:
-                ev[i][0].record(stream)
-            launch(t)
-            if ev is not None:
-                ev[i][1].record(stream)
-
-    for t in range(1, args.warmup + 1):
-        one_step(t)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-
-    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in stages] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(args.warmup + 1 + i, events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = [sum(events[i][j][0].elapsed_time(events[i][j][1]) for j in range(len(stages)))
-               for i in range(args.steps)]
-    if evict is None:
-        ms_per_step = wall / args.steps * 1e3
-        timing = "wall clock over the timed steps"
-    else:
-        ms_per_step = sum(step_ms) / len(step_ms)
-        timing = (f"sum of each step's HIP-event kernel times; {evict_mb} MiB written between "
-                  "steps to flush the last-level cache")
-    stage_info = []
-    for j, (name, _, nbytes) in enumerate(stages):
-        ms = [events[i][j][0].elapsed_time(events[i][j][1]) for i in range(args.steps)]
-        avg = sum(ms) / len(ms)
-        stage_info.append({"call": name, "avg_ms": round(avg, 4), "min_ms": round(min(ms), 4),
-                           "median_ms": round(sorted(ms)[len(ms) // 2], 4),
-                           "algorithmic_bytes": nbytes,
-                           "GBps": round(nbytes / (avg / 1e3) / 1e9, 1)})
-    main_stage = max(stage_info, key=lambda x: x["avg_ms"])
-    avg_kernel_s = main_stage["avg_ms"] / 1e3
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; kernel avg {avg_kernel_s*1e3:.3f} ms")
-    for x in stage_info:
-        log(f"  {x['call']}: {x['avg_ms']:.3f} ms, {x['GBps']} GB/s")
-
-    alg_bytes = main_stage["algorithmic_bytes"]
-    achieved = alg_bytes / avg_kernel_s / 1e9
-    traffic = counter_traffic(w.name) if args.path == "fused" else None
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                "traffic": traffic}
-
-    # Same streams, same grid, trivial arithmetic: the ceiling of this access pattern.
-    n8 = n - n % 8
-    mix_ref = None
-    if not args.no_copy_reference and n8 > 0 and args.path == "fused":
-        out16 = flat[phase:phase + n8] if phase == 0 else torch.empty(n8, dtype=torch.int16,
-                                                                        device=dev)
-        def mix():
-            if blocked:
-                F.stream_mix_blocked(grads, state, out16, n8, stream=stream)
-            else:
-                F.stream_mix(grads, master, m, v, out16, n=n8, stream=stream)
-        for _ in range(2):
-            mix()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 5
-        a.record(stream)
-        for _ in range(reps):
-            mix()
-        b.record(stream)
-        torch.cuda.synchronize()
-        mix_ms = a.elapsed_time(b) / reps
-        mix_ref = {"GBps": round(n8 * bpp / (mix_ms / 1e3) / 1e9, 1), "ms": round(mix_ms, 4),
-                   "kernel": "fsdpshard_stream_mix (the step's loads and stores, no arithmetic)"}
-        log(f"stream-mix reference: {mix_ref['GBps']} GB/s")
-        del out16
-
-    copy_ref = None
-    if not args.no_copy_reference:
-        del grads
-        torch.cuda.empty_cache()
-        copy_ref = copy_reference(F, torch, dev, stream)
-
-    cpu = cpu_par = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle ...")
-        cpu = cpu_baseline(w.name)
-        log(f"cpu oracle: {cpu['value']:.3e} params/s")
-        if args.cpu_procs > 0:
-            cpu_par = cpu_baseline_parallel(w.name, args.cpu_procs)
-            log(f"cpu oracle, {cpu_par['cores']} processes: {cpu_par['value']:.3e} params/s")
-
-    value = L.n_real / (ms_per_step / 1e3)
-    rec = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "params/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "description": w.description,
-            "flat_params": L.P,
-            "world_size": w.world_size,
-            "rank": w.rank,
-            "slice_elems": n,
-            "real_params": L.n_real,
-            "fan_in": Fi,
-            "segments": L.n_segments,
-            "storage": "bf16 grads and params, fp32 master/m/v",
-            "algorithmic_bytes_per_param": bpp if args.path == "fused" else None,
-            # A step that re-read the bf16 parameters would move 2 more bytes per parameter
-            # (28 + 2F); the fused kernel writes them from the updated fp32 master instead, so
-            # the roofline above does not credit those bytes.
-            "bytes_per_param_with_param_reread": bpp + 2 if args.path == "fused" else None,
-            "GBps_with_param_reread": (round(L.n_real * (bpp + 2) / avg_kernel_s / 1e9, 1)
-                                       if args.path == "fused" else None),
-            "achieved_GBps_wall": round(sum(x["algorithmic_bytes"] for x in stage_info)
-                                        / (ms_per_step / 1e3) / 1e9, 1),
-            "kernel_avg_ms": round(avg_kernel_s * 1e3, 4),
-            "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
-            "step_ms_min": round(min(step_ms), 4),
-            "timing": timing,
-            "path": args.path,
-            "state_layout": ("blocked: one array, 512-element blocks of master, m, v" if blocked
-                             else "separate master, m, v arrays"),
-            "stages": stage_info,
-            "groups_per_wave": args.groups_per_wave or "default",
-        },
-        "roofline": roofline,
-        "mix_reference": mix_ref,
-        "copy_reference": copy_ref,
-        "cpu_baseline": cpu,
-        "cpu_baseline_parallel": cpu_par,
-    }
-    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

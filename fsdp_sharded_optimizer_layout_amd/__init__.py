@@ -113,17 +113,21 @@ def lib():
     h.fsdpshard_strerror.argtypes = [ctypes.c_int]
     h.fsdpshard_strerror.restype = ctypes.c_char_p
     h.fsdpshard_abi_version.argtypes = []
-    h.fsdpshard_set_groups_per_wave.argtypes = [ctypes.c_int]
     h.fsdpshard_stream_copy.argtypes = [c_vp, c_vp, c_i64, c_vp]
     h.fsdpshard_stream_mix.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_vp, c_vp, c_i64,
                                        c_vp]
     h.fsdpshard_stream_mix_blocked.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_i64,
                                                c_vp]
+    h.fsdpshard_stream_rw.argtypes = [ctypes.POINTER(c_vp), c_i32, ctypes.POINTER(c_vp), c_i32,
+                                      c_i64, c_i32, c_vp, c_vp]
+    h.fsdpshard_stream_mix_phased.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_i64,
+                                              c_i32, c_i32, c_vp]
     for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
                  "adamw_shard_step_f32grad", "reduce_shard_accumulate", "grad_sumsq_shard",
                  "reshard_plan", "reshard_copy",
-                 "fsdpshard_abi_version", "fsdpshard_set_groups_per_wave", "fsdpshard_stream_copy",
-                 "fsdpshard_stream_mix", "fsdpshard_stream_mix_blocked", "reduce_shard_sumsq",
+                 "fsdpshard_abi_version", "fsdpshard_stream_copy", "fsdpshard_stream_rw",
+                 "fsdpshard_stream_mix", "fsdpshard_stream_mix_blocked",
+                 "fsdpshard_stream_mix_phased", "reduce_shard_sumsq",
                  "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
                  "state_to_blocked", "state_from_blocked"):
         getattr(h, name).restype = ctypes.c_int
@@ -137,15 +141,6 @@ def strerror(code):
 
 def abi_version():
     return lib().fsdpshard_abi_version()
-
-
-def set_groups_per_wave(groups):
-    """512-element groups per wavefront in adamw_shard_step (1, 2 or 4; 0 = built-in choice).
-    Returns the previous setting."""
-    prev = lib().fsdpshard_set_groups_per_wave(int(groups))
-    if prev < 0:
-        raise ValueError("groups per wave must be 0, 1, 2 or 4")
-    return prev
 
 
 def _check(call, code):
@@ -468,6 +463,22 @@ def stream_copy(src, dst, nbytes=None, stream=None):
         _ptr(src, "src"), _ptr(dst, "dst"), nbytes, _stream(stream, src)))
 
 
+def stream_rw(srcs, dsts, nbytes, per_cu=0, sink=None, stream=None):
+    """Measurement aid: len(srcs) read streams and len(dsts) write streams of ``nbytes`` each
+    (pure reads when ``dsts`` is empty; then ``sink`` is a device tensor of at least 4 bytes)."""
+    nbytes = int(nbytes)
+    for i, t in enumerate(list(srcs) + list(dsts)):
+        _need_bytes(t, f"stream {i}", nbytes)
+    _need_bytes(sink, "sink", 4)
+    like = next(iter(list(srcs) + list(dsts)), None)
+    src_arr = (c_vp * max(1, len(srcs)))(*[_ptr(t, "source") for t in srcs])
+    dst_arr = (c_vp * max(1, len(dsts)))(*[_ptr(t, "destination") for t in dsts])
+    _check("fsdpshard_stream_rw", lib().fsdpshard_stream_rw(
+        ctypes.cast(src_arr, ctypes.POINTER(c_vp)), len(srcs),
+        ctypes.cast(dst_arr, ctypes.POINTER(c_vp)), len(dsts), nbytes, int(per_cu),
+        _ptr(sink, "sink"), _stream(stream, like)))
+
+
 def stream_mix(contribs, s0, s1, s2, out, n=None, stream=None):
     """Measurement aid: the fused step's traffic with trivial arithmetic (n a multiple of 8)."""
     n = s0.numel() if n is None else int(n)
@@ -488,6 +499,18 @@ def stream_mix_blocked(contribs, state, out, n, stream=None):
     _check("fsdpshard_stream_mix_blocked", lib().fsdpshard_stream_mix_blocked(
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(state, "state"),
         _ptr(out, "out"), n, _stream(stream, state)))
+
+
+def stream_mix_phased(contribs, state, out, n, groups_per_wave, per_cu, stream=None):
+    """Measurement aid: stream_mix_blocked's bytes with each work-group's loads and stores in
+    separate phases (see fsdpshard_stream_mix_phased)."""
+    n = int(n)
+    arr = _contrib_array(contribs, n)
+    _need_bytes(state, "state", 4 * state_blocked_elems(n))
+    _need_bytes(out, "out", 2 * n)
+    _check("fsdpshard_stream_mix_phased", lib().fsdpshard_stream_mix_phased(
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(state, "state"),
+        _ptr(out, "out"), n, int(groups_per_wave), int(per_cu), _stream(stream, state)))
 
 
 # ------------------------------------------------------------------------------ reshard

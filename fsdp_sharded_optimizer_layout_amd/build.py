@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfsdpshard.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = [os.path.join(CSRC, "shard_step.hip"), os.path.join(CSRC, "reshard.hip")]
+HIP_SOURCES = [os.path.join(CSRC, "shard_step.hip"), os.path.join(CSRC, "reshard.hip"),
+               os.path.join(CSRC, "calib.hip")]
 HOST_SOURCES = [os.path.join(CSRC, "layout.cpp")]
 
 

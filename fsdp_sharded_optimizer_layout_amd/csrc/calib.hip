@@ -1,0 +1,369 @@
+// Measurement aids of libfsdpshard.so (declared in include/fsdpshard_calib.h).  None of these is
+// part of the sharded step; they bound what the memory system allows for the step's traffic.
+//
+//   * stream_copy_kernel   one read and one write stream (the classic copy).
+//   * stream_rw_kernel     R read streams and W write streams of equal length: pure reads
+//                          (W = 0), pure writes (R = 0), a copy (1, 1), or the 2 : 1 read : write
+//                          byte ratio of the fused step at fan-in 8 (2, 1).
+//   * stream_mix_kernel    the fused step's exact loads and stores (same vector width, cache
+//                          hints, tile map, load issue order and work-groups per CU) with
+//                          trivial integer arithmetic in place of the reduction and the update.
+//   * stream_mix_phased_kernel
+//                          the same bytes as the blocked-state step, ordered in phases: each
+//                          wave loads G consecutive groups, the work-group meets at a barrier,
+//                          and only then does any wave of it store.  With one work-group per CU
+//                          a CU alternates between a pure-read and a pure-write phase.
+//
+// Every kernel checks each vector index against the stream length, so any grid is safe.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fsdpshard.h"
+#include "fsdpshard_calib.h"
+#include "stream_common.h"
+
+namespace {
+
+using namespace fsdpshard_detail;
+
+__global__ __launch_bounds__(kBlock) void stream_copy_kernel(const uint4* __restrict__ src,
+                                                             uint4* __restrict__ dst,
+                                                             int64_t nvec) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= nvec) return;
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + i));
+}
+
+// ------------------------------------------------------------------------------------------------
+// R read streams, W write streams.
+
+constexpr int kRwMaxStreams = FSDPSHARD_CALIB_MAX_STREAMS;
+constexpr int kRwVecs = 4;   // 16-byte vectors per thread per stream (a work-group: 16 KiB each)
+constexpr uint32_t kSinkMagic = 0x9E3779B9u;
+
+struct RwParams {
+    const u32x4_t* src[kRwMaxStreams];
+    u32x4_t* dst[kRwMaxStreams];
+    uint32_t* sink;
+    int64_t nvec;
+    int32_t n_src, n_dst;
+};
+
+// Thread t of work-group b handles vectors b * 1024 + u * 256 + t, u = 0..3, of every stream:
+// all loads first, then the XOR of the loaded words (mixed with the index) to every write stream.
+// With no write stream, a lane whose XOR equals a fixed constant stores it to `sink`, so the
+// loads cannot be dropped and almost no bytes are written.
+__global__ __launch_bounds__(kBlock) void stream_rw_kernel(RwParams p) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kBlock * kRwVecs) + threadIdx.x;
+    u32x4_t x[kRwVecs];
+#pragma unroll
+    for (int u = 0; u < kRwVecs; ++u) {
+        const uint32_t i32 = static_cast<uint32_t>(base + u * kBlock);
+        x[u] = u32x4_t{i32, i32 ^ 0x55555555u, i32 ^ 0x33333333u, i32 ^ 0x0F0F0F0Fu};
+    }
+#pragma unroll
+    for (int r = 0; r < kRwMaxStreams; ++r) {
+        if (r >= p.n_src) break;
+#pragma unroll
+        for (int u = 0; u < kRwVecs; ++u) {
+            const int64_t i = base + u * kBlock;
+            if (i < p.nvec) x[u] ^= __builtin_nontemporal_load(p.src[r] + i);
+        }
+    }
+    if (p.n_dst == 0) {
+#pragma unroll
+        for (int u = 0; u < kRwVecs; ++u)
+            if ((x[u].x ^ x[u].y ^ x[u].z ^ x[u].w) == kSinkMagic) *p.sink = x[u].x;
+        return;
+    }
+#pragma unroll
+    for (int w = 0; w < kRwMaxStreams; ++w) {
+        if (w >= p.n_dst) break;
+#pragma unroll
+        for (int u = 0; u < kRwVecs; ++u) {
+            const int64_t i = base + u * kBlock;
+            if (i < p.nvec) {
+                u32x4_t y = x[u];
+                y.x += static_cast<uint32_t>(w);
+                __builtin_nontemporal_store(y, p.dst[w] + i);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Replicas of the fused step's traffic.
+
+struct MixParams {
+    const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
+    float* s[3];
+    uint16_t* out;
+    int64_t nvec;
+    int32_t fan_in;
+};
+
+// One 512-element group per wave, exactly as the step: F non-temporal bf16 loads, three fp32
+// read-modify-write streams (separate, or the blocked array in s[0]), one bf16 store per
+// 8-element vector.
+template <int F, bool BLK>
+__global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int64_t vec = tile_base<kStepXcdRun>(wave, 1) + lane;
+    if (vec >= p.nvec) return;
+    const int64_t e0 = vec * kVec;
+    const int fan_in = F > 0 ? F : p.fan_in;
+    uint4 raw[F > 0 ? F : 1];
+    float st[3][kVec];
+    uint32_t x = 0;
+    float* sp[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) sp[k] = BLK ? p.s[0] + blocked_index(k, e0) : p.s[k] + e0;
+    // The step's issue order: all state first (blocked state, or one gradient stream), else
+    // master and m, then the gradients, then v.
+    constexpr bool kStateFirst = BLK || F == 1;
+    load8(sp[0], true, kVec, st[0]);
+    load8(sp[1], true, kVec, st[1]);
+    if constexpr (kStateFirst) load8(sp[2], true, kVec, st[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (F > 0) {
+#pragma unroll
+        for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
+    }
+    if constexpr (!kStateFirst) {
+        __builtin_amdgcn_sched_barrier(0);
+        load8(sp[2], true, kVec, st[2]);
+    }
+    if constexpr (F > 0) {
+#pragma unroll
+        for (int r = 0; r < F; ++r) x ^= raw[r].x ^ raw[r].y ^ raw[r].z ^ raw[r].w;
+    } else {
+        for (int r = 0; r < fan_in; ++r) {
+            const uint4 q = ld_u4_nt(p.contrib[r] + e0);
+            x ^= q.x ^ q.y ^ q.z ^ q.w;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        st[k][0] = __uint_as_float(__float_as_uint(st[k][0]) ^ x);
+        store8(sp[k], true, kVec, st[k]);
+    }
+    st_u4_nt(p.out + e0, make_uint4(__float_as_uint(st[0][1]), __float_as_uint(st[1][1]),
+                                    __float_as_uint(st[2][1]), x));
+}
+
+// Blocked-state replica in phases: wave w owns G consecutive groups; it issues every load of
+// its G groups (state first, then the contributions) and folds all loaded words into one XOR,
+// so it holds all its data before the work-group barrier; no wave of the work-group stores
+// before every wave has loaded.  Same bytes per element as stream_mix_kernel.
+template <int F, int G>
+__global__ __launch_bounds__(kBlock) void stream_mix_phased_kernel(MixParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int64_t base = tile_base<kStepXcdRun>(wave, G);
+    float st[G][3][kVec];
+    uint4 raw[G][F];
+    uint32_t x[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int64_t vec = base + g * kWave + lane;
+        x[g] = 0u;
+        if (vec < p.nvec) {
+            const int64_t e0 = vec * kVec;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) load8(p.s[0] + blocked_index(k, e0), true, kVec, st[g][k]);
+#pragma unroll
+            for (int r = 0; r < F; ++r) raw[g][r] = ld_u4_nt(p.contrib[r] + e0);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (base + g * kWave + lane < p.nvec) {
+#pragma unroll
+            for (int r = 0; r < F; ++r) x[g] ^= raw[g][r].x ^ raw[g][r].y ^ raw[g][r].z ^ raw[g][r].w;
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int e = 1; e < kVec; ++e) x[g] ^= __float_as_uint(st[g][k][e]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int64_t vec = base + g * kWave + lane;
+        if (vec < p.nvec) {
+            const int64_t e0 = vec * kVec;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                st[g][k][0] = __uint_as_float(__float_as_uint(st[g][k][0]) ^ x[g]);
+                store8(p.s[0] + blocked_index(k, e0), true, kVec, st[g][k]);
+            }
+            st_u4_nt(p.out + e0, make_uint4(__float_as_uint(st[g][0][1]),
+                                            __float_as_uint(st[g][1][1]),
+                                            __float_as_uint(st[g][2][1]), x[g]));
+        }
+    }
+}
+
+template <int G>
+const void* phased_kernel(int fan_in) {
+    switch (fan_in) {
+        case 1: return reinterpret_cast<const void*>(&stream_mix_phased_kernel<1, G>);
+        case 4: return reinterpret_cast<const void*>(&stream_mix_phased_kernel<4, G>);
+        case 8: return reinterpret_cast<const void*>(&stream_mix_phased_kernel<8, G>);
+        default: return nullptr;
+    }
+}
+
+// Checks shared by the mix replicas.  With `blocked`, s0 is the blocked state array and s1, s2
+// are null.
+int check_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0, float* s1, float* s2,
+              uint16_t* out, int64_t n, bool blocked) {
+    if (s0 == nullptr || (!blocked && (s1 == nullptr || s2 == nullptr)) || out == nullptr ||
+        n < 0 || n % kVec)
+        return FSDPSHARD_ERR_INVALID_ARG;
+    const int rc = check_contribs(contribs, fan_in);
+    if (rc != FSDPSHARD_OK) return rc;
+    if (!aligned16(s0) || (!blocked && (!aligned16(s1) || !aligned16(s2))) || !aligned16(out))
+        return FSDPSHARD_ERR_ALIGNMENT;
+    if (n > INT64_MAX / 16) return FSDPSHARD_ERR_OVERFLOW;
+    const void* wr[4] = {s0, blocked ? nullptr : s1, blocked ? nullptr : s2, out};
+    const int64_t wb[4] = {blocked ? blocked_elems(n) * 4 : n * 4, n * 4, n * 4, n * 2};
+    for (int i = 0; i < 4 && n > 0; ++i) {
+        if (wr[i] == nullptr) continue;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(wr[i], wb[i], wr[j], wb[j])) return FSDPSHARD_ERR_INVALID_ARG;
+        for (int r = 0; r < fan_in; ++r)
+            if (overlaps(wr[i], wb[i], contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+    }
+    return FSDPSHARD_OK;
+}
+
+void fill_mix(MixParams& p, const uint16_t* const* contribs, int32_t fan_in, float* s0, float* s1,
+              float* s2, uint16_t* out, int64_t n) {
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
+    p.s[0] = s0;
+    p.s[1] = s1;
+    p.s[2] = s2;
+    p.out = out;
+    p.nvec = n / kVec;
+    p.fan_in = fan_in;
+}
+
+int stream_mix_impl(const uint16_t* const* contribs, int32_t fan_in, float* s0, float* s1,
+                    float* s2, uint16_t* out, int64_t n, bool blocked, void* stream) {
+    int rc = check_mix(contribs, fan_in, s0, s1, s2, out, n, blocked);
+    if (rc != FSDPSHARD_OK || n == 0) return rc;
+    MixParams p;
+    fill_mix(p, contribs, fan_in, s0, s1, s2, out, n);
+    unsigned blocks = 0;
+    rc = tile_grid(n, 1, &blocks);
+    if (rc != FSDPSHARD_OK) return rc;
+    const void* k =
+        blocked ? (fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1, true>)
+                   : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8, true>)
+                                 : reinterpret_cast<const void*>(&stream_mix_kernel<0, true>))
+                : (fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1, false>)
+                   : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8, false>)
+                                 : reinterpret_cast<const void*>(&stream_mix_kernel<0, false>));
+    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in));   // as the step
+}
+
+}  // namespace
+
+extern "C" int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (src == nullptr || dst == nullptr || bytes < 0 || (bytes & 15) != 0)
+        return FSDPSHARD_ERR_INVALID_ARG;
+    if (!aligned16(src) || !aligned16(dst)) return FSDPSHARD_ERR_ALIGNMENT;
+    if (overlaps(src, bytes, dst, bytes)) return FSDPSHARD_ERR_INVALID_ARG;
+    if (bytes == 0) return FSDPSHARD_OK;
+    const int64_t nvec = bytes / 16;
+    const int64_t blocks = (nvec + kBlock - 1) / kBlock;
+    if (blocks > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
+    void* args[3];
+    const uint4* s = static_cast<const uint4*>(src);
+    uint4* d = static_cast<uint4*>(dst);
+    int64_t nv = nvec;
+    args[0] = &s;
+    args[1] = &d;
+    args[2] = &nv;
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel),
+                                         dim3(static_cast<unsigned>(blocks)), dim3(kBlock), args,
+                                         0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
+}
+
+extern "C" int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* const* dst,
+                                   int32_t n_dst, int64_t bytes, int32_t per_cu, uint32_t* sink,
+                                   void* stream) {
+    if (n_src < 0 || n_dst < 0 || n_src > kRwMaxStreams || n_dst > kRwMaxStreams ||
+        n_src + n_dst == 0 || bytes < 0 || (bytes & 15) != 0 || per_cu < 0 ||
+        (n_src > 0 && src == nullptr) || (n_dst > 0 && dst == nullptr) ||
+        (n_dst == 0 && sink == nullptr))
+        return FSDPSHARD_ERR_INVALID_ARG;
+    for (int r = 0; r < n_src; ++r) {
+        if (src[r] == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
+        if (!aligned16(src[r])) return FSDPSHARD_ERR_ALIGNMENT;
+    }
+    for (int w = 0; w < n_dst; ++w) {
+        if (dst[w] == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
+        if (!aligned16(dst[w])) return FSDPSHARD_ERR_ALIGNMENT;
+        for (int j = w + 1; j < n_dst; ++j)
+            if (overlaps(dst[w], bytes, dst[j], bytes)) return FSDPSHARD_ERR_INVALID_ARG;
+        for (int r = 0; r < n_src; ++r)
+            if (overlaps(dst[w], bytes, src[r], bytes)) return FSDPSHARD_ERR_INVALID_ARG;
+    }
+    if (sink != nullptr && (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return FSDPSHARD_ERR_ALIGNMENT;
+    if (bytes == 0) return FSDPSHARD_OK;
+    RwParams p;
+    for (int r = 0; r < kRwMaxStreams; ++r) {
+        p.src[r] = r < n_src ? static_cast<const u32x4_t*>(src[r]) : nullptr;
+        p.dst[r] = r < n_dst ? static_cast<u32x4_t*>(dst[r]) : nullptr;
+    }
+    p.sink = sink;
+    p.nvec = bytes / 16;
+    p.n_src = n_src;
+    p.n_dst = n_dst;
+    const int64_t per_block = static_cast<int64_t>(kBlock) * kRwVecs;
+    const int64_t blocks = (p.nvec + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
+    return launch(reinterpret_cast<const void*>(&stream_rw_kernel), static_cast<unsigned>(blocks),
+                  &p, stream, per_cu);
+}
+
+extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0,
+                                    float* s1, float* s2, uint16_t* out, int64_t n, void* stream) {
+    return stream_mix_impl(contribs, fan_in, s0, s1, s2, out, n, false, stream);
+}
+
+extern "C" int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in,
+                                            float* state, uint16_t* out, int64_t n, void* stream) {
+    return stream_mix_impl(contribs, fan_in, state, nullptr, nullptr, out, n, true, stream);
+}
+
+extern "C" int fsdpshard_stream_mix_phased(const uint16_t* const* contribs, int32_t fan_in,
+                                           float* state, uint16_t* out, int64_t n,
+                                           int32_t groups_per_wave, int32_t per_cu,
+                                           void* stream) {
+    int rc = check_mix(contribs, fan_in, state, nullptr, nullptr, out, n, true);
+    if (rc != FSDPSHARD_OK) return rc;
+    if (per_cu < 0) return FSDPSHARD_ERR_INVALID_ARG;
+    const void* k = groups_per_wave == 1   ? phased_kernel<1>(fan_in)
+                    : groups_per_wave == 2 ? phased_kernel<2>(fan_in)
+                    : groups_per_wave == 4 ? phased_kernel<4>(fan_in)
+                                           : nullptr;
+    if (k == nullptr) return FSDPSHARD_ERR_UNSUPPORTED;
+    if (n == 0) return FSDPSHARD_OK;
+    MixParams p;
+    fill_mix(p, contribs, fan_in, state, nullptr, nullptr, out, n);
+    unsigned blocks = 0;
+    rc = tile_grid(n, groups_per_wave, &blocks);
+    if (rc != FSDPSHARD_OK) return rc;
+    return launch(k, blocks, &p, stream, per_cu);
+}

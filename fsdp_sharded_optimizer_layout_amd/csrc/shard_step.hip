@@ -15,13 +15,12 @@
 //   * Every lane owns a vector of 8 consecutive elements: one 16-byte load per gradient stream,
 //     two 16-byte loads / stores per fp32 stream, one 16-byte bf16 store.  A wave covers 512
 //     elements (1 KiB per bf16 stream, 2 KiB per fp32 stream, all fully coalesced).
-//   * One tile per wave: each wave owns U consecutive 512-element groups (U = 1 by default; 2
-//     and 4 selectable) and issues every HBM load of its tile before the first arithmetic
-//     instruction; the grid has one work-group of 4 waves per 4U groups (hundreds of thousands
-//     for a 7B-model slice), enough to keep all 256 CUs fed.  Work-groups map to tiles so that
-//     each of the 8 XCDs streams runs of 64 consecutive tiles (tile_index).  Gradient loads and
-//     all full-vector stores carry the non-temporal hint (single-use streams); the state loads
-//     do not.
+//   * One 512-element group per wave: each wave issues every HBM load of its group before the
+//     first arithmetic instruction; the grid has one work-group of 4 waves per 4 groups
+//     (hundreds of thousands for a 7B-model slice), enough to keep all 256 CUs fed.  Work-groups
+//     map to tiles so that each of the 8 XCDs streams runs of consecutive tiles (tile_index).
+//     Gradient loads and all full-vector stores carry the non-temporal hint (single-use
+//     streams); the state loads do not.
 //   * Contributions are reduced in registers in rank order 0..F-1 from +0 (fixed order, so the
 //     result is deterministic and matches a sequential float32 sum bit for bit).
 //   * Segment flags (padding, weight decay) come from a per-wave cursor over the segment table:
@@ -37,19 +36,15 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 
 #include "fsdpshard.h"
-#include "fsdpshard_calib.h"
+#include "stream_common.h"
 
 namespace {
 
-constexpr int kVec = 8;            // elements per lane
-constexpr int kWave = 64;          // lanes per wavefront
-constexpr int kBlock = 256;        // threads per work-group
-constexpr int kWavesPerBlock = kBlock / kWave;
+using namespace fsdpshard_detail;
 
 // ------------------------------------------------------------------------------------------------
 // Kernel parameter blocks (passed by value in the kernel-argument segment).
@@ -106,8 +101,6 @@ struct UnflattenParams {
 // ------------------------------------------------------------------------------------------------
 // Small helpers.
 
-__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -131,63 +124,11 @@ __device__ __forceinline__ void accumulate(float (&g)[kVec], const uint4 raw) {
     g[7] = g[7] + bf16_hi(raw.w);
 }
 
-__device__ __forceinline__ uint4 ld_u4(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-__device__ __forceinline__ float4 ld_f4(const float* p) {
-    return *reinterpret_cast<const float4*>(p);
-}
-__device__ __forceinline__ void st_f4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
-
-// Non-temporal forms for single-use streams (global_load / global_store with the nt bit).
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 ld_u4_nt(const uint16_t* p) {
-    const u32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(r.x, r.y, r.z, r.w);
-}
-__device__ __forceinline__ void ld8_f32_nt(const float* p, float (&x)[8]) {
-    const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-    const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void st_f4_nt(float* p, float a, float b, float c, float d) {
-    const f32x4_t v = {a, b, c, d};
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
-}
-__device__ __forceinline__ void st_u4_nt(uint16_t* p, uint4 x) {
-    const u32x4_t v = {x.x, x.y, x.z, x.w};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
-}
-
 // Partial vector (slice tail): element-wise loads of the first `cnt` elements, zeros after.
 __device__ __forceinline__ uint4 ld_u4_partial(const uint16_t* p, int cnt) {
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     for (int e = 0; e < cnt; ++e) w[e >> 1] |= static_cast<uint32_t>(p[e]) << (16 * (e & 1));
     return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-__device__ __forceinline__ void load8(const float* p, bool full, int cnt, float (&x)[kVec]) {
-    if (full) {
-        const float4 a = ld_f4(p), b = ld_f4(p + 4);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) x[e] = (e < cnt) ? p[e] : 0.0f;
-    }
-}
-
-__device__ __forceinline__ void store8(float* p, bool full, int cnt, const float (&x)[kVec]) {
-    if (full) {
-        st_f4_nt(p, x[0], x[1], x[2], x[3]);
-        st_f4_nt(p + 4, x[4], x[5], x[6], x[7]);
-    } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e)
-            if (e < cnt) p[e] = x[e];
-    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -416,23 +357,19 @@ __device__ __forceinline__ void pack_out(const uint32_t (&fl)[kVec], const float
     }
 }
 
-// One 512-element group with per-lane bounds: the slice's last, partial group, and every group
-// of the run-time fan-in kernel.  TAIL = false drops the bounds for complete groups.
-// Where element e0 (a multiple of 8) of state array k (0 master, 1 m, 2 v) lives.  Separate
-// layout: three arrays.  Blocked layout: one array in which each block of kStateBlock slice
-// elements holds that block's masters, then its m, then its v (an 8-element vector never
-// straddles a block).
-constexpr int64_t kStateBlock = FSDPSHARD_STATE_BLOCK;
-
+// Where element e0 (a multiple of 8) of state array k (0 master, 1 m, 2 v) lives: three separate
+// arrays, or the blocked array (blocked_index).
 template <bool BLK>
 __device__ __forceinline__ float* state_ptr(const StepParams& p, int k, int64_t e0) {
     if constexpr (BLK) {
-        return p.master + ((e0 / kStateBlock) * 3 + k) * kStateBlock + e0 % kStateBlock;
+        return p.master + blocked_index(k, e0);
     } else {
         return k == 0 ? p.master + e0 : (k == 1 ? p.m + e0 : p.v + e0);
     }
 }
 
+// One 512-element group with per-lane bounds: the slice's last, partial group, and every group
+// of the run-time fan-in kernel.  TAIL = false drops the bounds for complete groups.
 template <int F, bool OUT, bool TAIL, bool BLK>
 __device__ __forceinline__ void step_group(const StepParams& p, float scale, const SegCursor& cur,
                                            int64_t vec, int64_t group_end_vec, int lane) {
@@ -478,121 +415,81 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
     }
 }
 
-// A wave's whole tile of U complete groups (compile-time gradient source F >= 1 or F == -1):
-// every HBM load of the tile is issued first (gradients non-temporal), then the segment cursor is
-// placed, then each group is reduced, updated and stored.
-template <int F, bool OUT, int U, bool BLK>
-__device__ __forceinline__ void step_tile(const StepParams& p, int64_t base0, int lane) {
-    uint4 raw[U][F > 0 ? F : 1];
-    float gf[U][kVec], th[U][kVec], mm[U][kVec], vv[U][kVec];
-    // Issue order of the tile's loads, pinned with scheduling barriers because it moves the
+// A wave's complete group (compile-time gradient source F >= 1 or F == -1): every HBM load of
+// the group is issued first (gradients non-temporal), then the segment cursor is placed, then
+// the group is reduced, updated and stored.
+template <int F, bool OUT, bool BLK>
+__device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb, int lane) {
+    uint4 raw[F > 0 ? F : 1];
+    float gf[kVec], th[kVec], mm[kVec], vv[kVec];
+    const int64_t e0 = (gb + lane) * kVec;
+    // Issue order of the group's loads, pinned with scheduling barriers because it moves the
     // kernel's bandwidth on MI355X (measured): with the blocked state, or with one gradient
     // stream, every state load goes first (blocked, fan-in 8: 5 % faster than the order below);
     // with separate state arrays and several gradient streams, master and m go first, then the
     // gradients, then v (about 2 % better than the alternatives).
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t e0 = (base0 + u * kWave + lane) * kVec;
-        if constexpr (BLK || F == 1 || F == -1) {
-            load8(state_ptr<BLK>(p, 0, e0), true, kVec, th[u]);
-            load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm[u]);
-            load8(state_ptr<BLK>(p, 2, e0), true, kVec, vv[u]);
-            __builtin_amdgcn_sched_barrier(0);
-            load_grad<F>(p, e0, true, kVec, raw[u], gf[u]);
-        } else {
-            load8(state_ptr<BLK>(p, 0, e0), true, kVec, th[u]);
-            load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm[u]);
-            __builtin_amdgcn_sched_barrier(0);
-            load_grad<F>(p, e0, true, kVec, raw[u], gf[u]);
-            __builtin_amdgcn_sched_barrier(0);
-            load8(state_ptr<BLK>(p, 2, e0), true, kVec, vv[u]);
-        }
+    if constexpr (BLK || F == 1 || F == -1) {
+        load8(state_ptr<BLK>(p, 0, e0), true, kVec, th);
+        load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
+        load8(state_ptr<BLK>(p, 2, e0), true, kVec, vv);
+        __builtin_amdgcn_sched_barrier(0);
+        load_grad<F>(p, e0, true, kVec, raw, gf);
+    } else {
+        load8(state_ptr<BLK>(p, 0, e0), true, kVec, th);
+        load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
+        __builtin_amdgcn_sched_barrier(0);
+        load_grad<F>(p, e0, true, kVec, raw, gf);
+        __builtin_amdgcn_sched_barrier(0);
+        load8(state_ptr<BLK>(p, 2, e0), true, kVec, vv);
     }
     __builtin_amdgcn_sched_barrier(0);
     const float scale = step_scale(p);     // after the loads: its own reads overlap them
     SegCursor cur;
-    cur.init(p.segs, p.n_segs, base0 * kVec);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t gb = base0 + u * kWave;
-        const int64_t e0 = (gb + lane) * kVec;
-        cur.seek(gb * kVec);
-        uint32_t fl[kVec];
-        element_flags(cur, (gb + kWave) * kVec, e0, fl);
-        float g[kVec];
-        sum_grad<F>(p, e0, true, kVec, raw[u], gf[u], g);
-        adam8(p, scale, fl, g, th[u], mm[u], vv[u]);
-        store8(state_ptr<BLK>(p, 0, e0), true, kVec, th[u]);
-        store8(state_ptr<BLK>(p, 1, e0), true, kVec, mm[u]);
-        store8(state_ptr<BLK>(p, 2, e0), true, kVec, vv[u]);
-        if constexpr (OUT) {
-            uint32_t w[4];
-            pack_out(fl, th[u], w);
-            const int s = p.out_shift;
-            const bool next_ok = (lane < kWave - 1) && ((gb + lane + 1) * kVec + s <= p.n);
-            const bool prev_ok = (lane > 0) && (e0 + s <= p.n);
-            store_bf16_vec(p.out, e0, s, w, true, kVec, next_ok, prev_ok);
-        }
+    cur.init(p.segs, p.n_segs, gb * kVec);
+    uint32_t fl[kVec];
+    element_flags(cur, (gb + kWave) * kVec, e0, fl);
+    float g[kVec];
+    sum_grad<F>(p, e0, true, kVec, raw, gf, g);
+    adam8(p, scale, fl, g, th, mm, vv);
+    store8(state_ptr<BLK>(p, 0, e0), true, kVec, th);
+    store8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
+    store8(state_ptr<BLK>(p, 2, e0), true, kVec, vv);
+    if constexpr (OUT) {
+        uint32_t w[4];
+        pack_out(fl, th, w);
+        const int s = p.out_shift;
+        const bool next_ok = (lane < kWave - 1) && ((gb + lane + 1) * kVec + s <= p.n);
+        const bool prev_ok = (lane > 0) && (e0 + s <= p.n);
+        store_bf16_vec(p.out, e0, s, w, true, kVec, next_ok, prev_ok);
     }
 }
 
-// Wave w of the grid owns vectors [w * 64U, (w + 1) * 64U) of the slice.
-// Work-group -> tile.  MI355X deals a launch's work-groups to its 8 XCDs in turn, so with the
-// identity map neighbouring tiles run on different XCDs at the same moment.  Here work-group b on
-// XCD x = b mod 8 takes the (b / 8 mod Run)-th tile of the x-th run of Run consecutive tiles in
-// each block of 8 * Run tiles: every XCD streams its own run of tiles.  Work-groups past the last
-// whole block keep the identity map, so the map is a permutation of [0, gridDim.x) for any grid.
-// Measured on one GPU against the identity map, with runs of 64 tiles (512 KiB of each fp32
-// stream): the fused step 3-4 % faster on the 7B-shaped slice and 0.4-1.4 % on the 70B-shaped
-// one, the fp32 accumulation 2-5 % faster; runs of 8 or 96 tiles were slower than 64 or 128.  With
-// the cap on work-groups per CU (launch), the fused step does 0.5-1 % better with runs of 32 tiles
-// on the large slices, while the reduction keeps 64 (2 % better than 32).  Results never depend
-// on the map: a tile's work is the same wherever it runs.
-constexpr int64_t kXcds = 8;
-constexpr int64_t kXcdRun = 64;       // reduction, unflatten
-constexpr int64_t kStepXcdRun = 32;   // fused step and its traffic replica
-
-template <int64_t Run = kXcdRun>
-__device__ __forceinline__ int64_t tile_index() {
-    const int64_t b = blockIdx.x;
-    const int64_t whole = static_cast<int64_t>(gridDim.x) / (kXcds * Run) * (kXcds * Run);
-    if (b >= whole) return b;
-    const int64_t x = b % kXcds, q = b / kXcds;
-    return (q / Run) * (kXcds * Run) + x * Run + q % Run;
-}
-
-template <int64_t Run = kXcdRun>
-__device__ __forceinline__ int64_t tile_base(int wave, int groups) {
-    return (tile_index<Run>() * kWavesPerBlock + wave) * (kWave * groups);
-}
-
-template <int F, bool OUT, int U, bool BLK>
+// Wave w of the grid owns vectors [64w, 64w + 64) of the slice (one group), placed by the
+// XCD-aware tile map.  One group per wave was measured fastest on MI355X for every fan-in and
+// state layout: waves owning 2 or 4 consecutive groups (all loads first) ran 7-15 % slower on
+// the 7B- and 70B-shaped slices.
+template <int F, bool OUT, bool BLK>
 __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
-    const int64_t base0 = tile_base<kStepXcdRun>(wave, U);
-    if (base0 >= nvec) return;
+    const int64_t gb = tile_base<kStepXcdRun>(wave, 1);
+    if (gb >= nvec) return;
     if constexpr (F != 0) {
-        if (base0 + kWave * U <= p.n / kVec) {
-            step_tile<F, OUT, U, BLK>(p, base0, lane);
+        if (gb + kWave <= p.n / kVec) {
+            step_whole_group<F, OUT, BLK>(p, gb, lane);
             return;
         }
     }
     const float scale = step_scale(p);
     SegCursor cur;
-    cur.init(p.segs, p.n_segs, base0 * kVec);
-    for (int u = 0; u < U; ++u) {
-        const int64_t gb = base0 + u * kWave;
-        if (gb >= nvec) break;
-        int64_t gend = gb + kWave;
-        if (gend > nvec) gend = nvec;
-        cur.seek(gb * kVec);
-        if (gend == gb + kWave && gend * kVec <= p.n)
-            step_group<F, OUT, false, BLK>(p, scale, cur, gb + lane, gend, lane);
-        else
-            step_group<F, OUT, true, BLK>(p, scale, cur, gb + lane, gend, lane);
-    }
+    cur.init(p.segs, p.n_segs, gb * kVec);
+    int64_t gend = gb + kWave;
+    if (gend > nvec) gend = nvec;
+    if (gend == gb + kWave && gend * kVec <= p.n)
+        step_group<F, OUT, false, BLK>(p, scale, cur, gb + lane, gend, lane);
+    else
+        step_group<F, OUT, true, BLK>(p, scale, cur, gb + lane, gend, lane);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1047,77 +944,6 @@ __global__ __launch_bounds__(kBlock) void unflatten_kernel(UnflattenParams p) {
     store_bf16_vec(p.out, e0, s, w, valid, cnt, next_ok, prev_ok);
 }
 
-__global__ __launch_bounds__(kBlock) void stream_copy_kernel(const uint4* __restrict__ src,
-                                                             uint4* __restrict__ dst,
-                                                             int64_t nvec) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (i >= nvec) return;
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i));
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + i));
-}
-
-// Measurement aid: the fused step's exact streams (F non-temporal bf16 loads, three fp32
-// read-modify-write streams, one bf16 store per 8-element vector, one 512-element group per wave)
-// with trivial integer arithmetic in place of the reduction and the optimizer, launched with the
-// same grid and the same work-groups per CU as the step.
-struct MixParams {
-    const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
-    float* s[3];
-    uint16_t* out;
-    int64_t nvec;
-    int32_t fan_in;
-};
-
-template <int F, bool BLK>
-__global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = wave_uniform(threadIdx.x >> 6);
-    const int64_t vec = tile_base<kStepXcdRun>(wave, 1) + lane;
-    if (vec >= p.nvec) return;
-    const int64_t e0 = vec * kVec;
-    const int fan_in = F > 0 ? F : p.fan_in;
-    uint4 raw[F > 0 ? F : 1];
-    float st[3][kVec];
-    uint32_t x = 0;
-    // Separate layout: three arrays.  Blocked layout: s[0] is the blocked state array.
-    float* sp[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-        sp[k] = BLK ? p.s[0] + ((e0 / kStateBlock) * 3 + k) * kStateBlock + e0 % kStateBlock
-                    : p.s[k] + e0;
-    // The step's issue order: all state first (blocked state, or one gradient stream), else
-    // master and m, then the gradients, then v.
-    constexpr bool kStateFirst = BLK || F == 1;
-    load8(sp[0], true, kVec, st[0]);
-    load8(sp[1], true, kVec, st[1]);
-    if constexpr (kStateFirst) load8(sp[2], true, kVec, st[2]);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (F > 0) {
-#pragma unroll
-        for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
-    }
-    if constexpr (!kStateFirst) {
-        __builtin_amdgcn_sched_barrier(0);
-        load8(sp[2], true, kVec, st[2]);
-    }
-    if constexpr (F > 0) {
-#pragma unroll
-        for (int r = 0; r < F; ++r) x ^= raw[r].x ^ raw[r].y ^ raw[r].z ^ raw[r].w;
-    } else {
-        for (int r = 0; r < fan_in; ++r) {
-            const uint4 q = ld_u4_nt(p.contrib[r] + e0);
-            x ^= q.x ^ q.y ^ q.z ^ q.w;
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        st[k][0] = __uint_as_float(__float_as_uint(st[k][0]) ^ x);
-        store8(sp[k], true, kVec, st[k]);
-    }
-    st_u4_nt(p.out + e0, make_uint4(__float_as_uint(st[0][1]), __float_as_uint(st[1][1]),
-                                    __float_as_uint(st[2][1]), x));
-}
-
 // Conversion between the separate state arrays and the blocked state array (plain copies).
 struct StatePackParams {
     float* sep[3];           // master, m, v
@@ -1152,112 +978,33 @@ __global__ __launch_bounds__(kBlock) void state_pack_kernel(StatePackParams p) {
 // ------------------------------------------------------------------------------------------------
 // Host-side launch helpers.
 
-std::atomic<int> g_groups_per_wave{0};   // 0: built-in choice per fan-in
-
-// One work-group of 4 waves per 4 * groups * 64 vectors of 8 elements.
-int tile_grid(int64_t n, int groups, unsigned* blocks) {
-    const int64_t nvec = (n + kVec - 1) / kVec;
-    const int64_t per_block = static_cast<int64_t>(kWavesPerBlock) * kWave * groups;
-    const int64_t b = (nvec + per_block - 1) / per_block;
-    if (b > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
-    *blocks = static_cast<unsigned>(b);
-    return FSDPSHARD_OK;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + static_cast<uintptr_t>(bbytes) && y < x + static_cast<uintptr_t>(abytes);
-}
-
-// Resident work-groups per CU.  The streaming kernels lose bandwidth when every CU holds as
-// many work-groups as its registers allow: with fewer waves in flight the HBM sees fewer
-// concurrent access streams.  The cap is set by reserving LDS that the kernels never touch (a
-// dynamic LDS size at launch), sized from the device's LDS per CU so that exactly `per_cu`
-// work-groups fit: halfway between lds/(per_cu+1) and lds/per_cu.  Measured on one GPU against the
-// register-limited occupancy: the fused step is 4-10 % faster with 2 per CU at fan-in 1 and 8 and
-// from an fp32 gradient; at fan-in 4 the 2,000-tensor slice is 5 % faster with 3 per CU (2 gains
-// nothing there), and at fan-in 2 and 16 both are within 1 %, so other fan-ins take 3.  The fp32
-// accumulation is 4-10 % faster with 2 per CU; the plain reduction of a single contribution wants
-// 4 per CU (2 cost it a quarter); the reduction fused with the sum of squares wants 2 per CU, 3
-// for a single contribution and 1 where its loads are software-pipelined (reduce_sq_pipelined);
-// the sum of squares, unflatten and plain copies are fastest uncapped.
-constexpr int step_groups_per_cu(int fan_in) {
-    return fan_in == 1 || fan_in == 8 || fan_in == -1 ? 2 : 3;
-}
+// Work-groups per CU of the reduction kernels (see occupancy_lds): the fp32 accumulation is 4-10 %
+// faster with 2 per CU; the plain reduction of a single contribution wants 4 per CU (2 cost it a
+// quarter); the reduction fused with the sum of squares wants 2 per CU, 3 for a single
+// contribution and 1 where its loads are software-pipelined (reduce_sq_pipelined); the sum of
+// squares and unflatten are fastest uncapped.
 constexpr int kReduceGroupsPerCU = 2;
 constexpr int kReduceOneStreamGroupsPerCU = 4;
 constexpr int kReduceSqGroupsPerCU = 2;
 constexpr int kReduceOneStreamSqGroupsPerCU = 3;
 constexpr int kReduceSqPipelinedGroupsPerCU = 1;
-constexpr int kMaxDevices = 64;
-std::atomic<int64_t> g_lds_per_cu[kMaxDevices];   // 0: not queried yet; -1: unknown
 
-int64_t lds_per_cu() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
-    int64_t v = g_lds_per_cu[dev].load(std::memory_order_relaxed);
-    if (v == 0) {
-        int bytes = 0;
-        const hipError_t e = hipDeviceGetAttribute(
-            &bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
-        v = (e == hipSuccess && bytes > 0) ? bytes : -1;
-        g_lds_per_cu[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
-}
-
-// Dynamic LDS bytes that leave room for exactly `per_cu` work-groups (0: no cap).
-size_t occupancy_lds(int per_cu) {
-    if (per_cu <= 0) return 0;
-    const int64_t lds = lds_per_cu();
-    if (lds <= 0) return 0;
-    const int64_t bytes = (lds / (per_cu + 1) + lds / per_cu) / 2;
-    return static_cast<size_t>(bytes & ~static_cast<int64_t>(1023));
-}
-
-int launch(const void* kernel, unsigned blocks, void* params, void* stream, int per_cu = 0) {
-    void* args[] = {params};
-    const hipError_t e = hipLaunchKernel(kernel, dim3(blocks), dim3(kBlock), args,
-                                         occupancy_lds(per_cu), static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
-}
-
-template <int F, int U, bool BLK>
-const void* step_kernel_u(bool out) {
-    return out ? reinterpret_cast<const void*>(&fused_step_kernel<F, true, U, BLK>)
-               : reinterpret_cast<const void*>(&fused_step_kernel<F, false, U, BLK>);
-}
-
-// The blocked state layout is compiled with one group per wave only.
-template <int F>
-const void* step_kernel(bool out, int groups, bool blocked) {
-    if (blocked) return step_kernel_u<F, 1, true>(out);
-    switch (groups) {
-        case 1: return step_kernel_u<F, 1, false>(out);
-        case 4: return step_kernel_u<F, 4, false>(out);
-        default: return step_kernel_u<F, 2, false>(out);
-    }
-}
-
-// Groups per wave: the process-wide setting if one was made, else the built-in choice.
-int groups_for(int fan_in) {
-    const int g = g_groups_per_wave.load(std::memory_order_relaxed);
-    if (g > 0) return g;
-    (void)fan_in;
-    return 1;  // measured fastest on MI355X for every fan-in (one 512-element group per wave)
+template <int F, bool BLK>
+const void* step_kernel(bool out) {
+    return out ? reinterpret_cast<const void*>(&fused_step_kernel<F, true, BLK>)
+               : reinterpret_cast<const void*>(&fused_step_kernel<F, false, BLK>);
 }
 
 // fan_in -1 selects the fp32-gradient kernels.
-const void* pick_step_kernel(int fan_in, bool out, int groups, bool blocked) {
+template <bool BLK>
+const void* pick_step_kernel(int fan_in, bool out) {
     switch (fan_in) {
-        case -1: return step_kernel<-1>(out, groups, blocked);
-        case 1: return step_kernel<1>(out, groups, blocked);
-        case 2: return step_kernel<2>(out, groups, blocked);
-        case 4: return step_kernel<4>(out, groups, blocked);
-        case 8: return step_kernel<8>(out, groups, blocked);
-        default: return step_kernel<0>(out, groups, blocked);
+        case -1: return step_kernel<-1, BLK>(out);
+        case 1: return step_kernel<1, BLK>(out);
+        case 2: return step_kernel<2, BLK>(out);
+        case 4: return step_kernel<4, BLK>(out);
+        case 8: return step_kernel<8, BLK>(out);
+        default: return step_kernel<0, BLK>(out);
     }
 }
 
@@ -1267,28 +1014,16 @@ int out_shift_of(const uint16_t* out) {
     return static_cast<int>((kVec - phase) % kVec);
 }
 
-int check_contribs(const uint16_t* const* contribs, int32_t fan_in, int64_t n) {
-    if (contribs == nullptr || fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
-    if (fan_in > FSDPSHARD_MAX_FAN_IN) return FSDPSHARD_ERR_UNSUPPORTED;
-    for (int r = 0; r < fan_in; ++r) {
-        if (contribs[r] == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
-        if (!aligned16(contribs[r])) return FSDPSHARD_ERR_ALIGNMENT;
-    }
-    (void)n;
-    return FSDPSHARD_OK;
-}
-
 bool is_finite(double x) { return std::isfinite(x); }
 
-// Shared by the two step entry points: exactly one of (contribs, fan_in >= 1) and
-// (grad32, fan_in == -1) is the gradient source.
-// Elements of a blocked state array for an n-element slice (-1 when it does not fit int64).
-int64_t blocked_elems(int64_t n) {
-    if (n < 0 || n > INT64_MAX / 16) return -1;
-    return 3 * ((n + kStateBlock - 1) / kStateBlock) * kStateBlock;
+// Bytes of a device segment table.
+int64_t seg_bytes(const fsdpshard_segment* segs, int32_t n_segments) {
+    return segs == nullptr ? 0 : static_cast<int64_t>(n_segments) * sizeof(fsdpshard_segment);
 }
 
-// With `blocked`, `master` is the blocked state array and m, v are null.
+// Shared by the step entry points: exactly one of (contribs, fan_in >= 1) and (grad32,
+// fan_in == -1) is the gradient source.  With `blocked`, `master` is the blocked state array and
+// m, v are null.
 int launch_step(float* master, float* m, float* v, const uint16_t* const* contribs, int32_t fan_in,
                 const float* grad32, int64_t n, const fsdpshard_segment* segs, int32_t n_segments,
                 const fsdpshard_adamw* hp, uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
@@ -1301,7 +1036,7 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
         if (grad32 == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
         if (!aligned16(grad32)) return FSDPSHARD_ERR_ALIGNMENT;
     } else {
-        rc = check_contribs(contribs, fan_in, n);
+        rc = check_contribs(contribs, fan_in);
         if (rc != FSDPSHARD_OK) return rc;
     }
     if (hp->step < 1 || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) ||
@@ -1312,10 +1047,8 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
         return FSDPSHARD_ERR_INVALID_ARG;
     if (!aligned16(master) || (!blocked && (!aligned16(m) || !aligned16(v))))
         return FSDPSHARD_ERR_ALIGNMENT;
-    if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
-        return FSDPSHARD_ERR_ALIGNMENT;
-    if (hp->max_grad_norm > 0.0 && (reinterpret_cast<uintptr_t>(hp->grad_sumsq) & 7u) != 0)
-        return FSDPSHARD_ERR_ALIGNMENT;
+    if (segs != nullptr && !aligned8(segs)) return FSDPSHARD_ERR_ALIGNMENT;
+    if (hp->max_grad_norm > 0.0 && !aligned8(hp->grad_sumsq)) return FSDPSHARD_ERR_ALIGNMENT;
     uint16_t* out = nullptr;
     if (flat_bf16 != nullptr) {
         if (flat_index0 > lo) return FSDPSHARD_ERR_INVALID_ARG;
@@ -1323,25 +1056,27 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
         out = flat_bf16 + (lo - flat_index0);
     }
     if (n > INT64_MAX / 16) return FSDPSHARD_ERR_OVERFLOW;
-    // Written buffers must not overlap each other or the inputs.
+    // Written buffers must not overlap each other or any input (gradients, segment table, the
+    // global sum of squares).
+    if (n == 0) return FSDPSHARD_OK;
     const int64_t fb = n * 4, hb = n * 2;
     const void* wr[4] = {master, blocked ? nullptr : m, blocked ? nullptr : v, out};
     const int64_t wb[4] = {blocked ? blocked_elems(n) * 4 : fb, fb, fb, hb};
+    const int64_t sb = seg_bytes(segs, n_segments);
     for (int i = 0; i < 4; ++i) {
-        if (wr[i] == nullptr || n == 0) continue;
+        if (wr[i] == nullptr) continue;
         for (int j = i + 1; j < 4; ++j)
-            if (wr[j] != nullptr && overlaps(wr[i], wb[i], wr[j], wb[j]))
-                return FSDPSHARD_ERR_INVALID_ARG;
+            if (overlaps(wr[i], wb[i], wr[j], wb[j])) return FSDPSHARD_ERR_INVALID_ARG;
         if (fan_in == -1) {
             if (overlaps(wr[i], wb[i], grad32, fb)) return FSDPSHARD_ERR_INVALID_ARG;
         } else {
             for (int r = 0; r < fan_in; ++r)
                 if (overlaps(wr[i], wb[i], contribs[r], hb)) return FSDPSHARD_ERR_INVALID_ARG;
         }
+        if (overlaps(wr[i], wb[i], segs, sb)) return FSDPSHARD_ERR_INVALID_ARG;
         if (hp->max_grad_norm > 0.0 && overlaps(wr[i], wb[i], hp->grad_sumsq, 8))
             return FSDPSHARD_ERR_INVALID_ARG;
     }
-    if (n == 0) return FSDPSHARD_OK;
 
     StepParams p;
     p.master = master;
@@ -1371,18 +1106,18 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     p.dec = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
     p.scale = static_cast<float>(hp->grad_scale);
 
-    const int groups = blocked ? 1 : groups_for(fan_in);   // the blocked kernels take one
     unsigned blocks = 0;
-    rc = tile_grid(n, groups, &blocks);
+    rc = tile_grid(n, 1, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(pick_step_kernel(fan_in, out != nullptr, groups, blocked), blocks, &p, stream,
-                  step_groups_per_cu(fan_in));
+    const void* k = blocked ? pick_step_kernel<true>(fan_in, out != nullptr)
+                            : pick_step_kernel<false>(fan_in, out != nullptr);
+    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in));
 }
 
 int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, float scale,
                   float* out, bool accumulate, void* stream) {
     if (out == nullptr || n < 0) return FSDPSHARD_ERR_INVALID_ARG;
-    int rc = check_contribs(contribs, fan_in, n);
+    int rc = check_contribs(contribs, fan_in);
     if (rc != FSDPSHARD_OK) return rc;
     if (!aligned16(out)) return FSDPSHARD_ERR_ALIGNMENT;
     if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
@@ -1538,21 +1273,32 @@ extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
         if (grad == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
         if (!aligned16(grad)) return FSDPSHARD_ERR_ALIGNMENT;
     } else {
-        const int rc = check_contribs(contribs, fan_in, n);
+        const int rc = check_contribs(contribs, fan_in);
         if (rc != FSDPSHARD_OK) return rc;
     }
-    if ((reinterpret_cast<uintptr_t>(sumsq) & 7u) != 0) return FSDPSHARD_ERR_ALIGNMENT;
-    if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
-        return FSDPSHARD_ERR_ALIGNMENT;
+    if (!aligned8(sumsq)) return FSDPSHARD_ERR_ALIGNMENT;
+    if (segs != nullptr && !aligned8(segs)) return FSDPSHARD_ERR_ALIGNMENT;
     if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
     const int64_t parts = sumsq_partials(n);
     if (parts > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
     const int64_t need = parts * static_cast<int64_t>(sizeof(double));
     if (parts > 0 && (workspace == nullptr || workspace_bytes < need))
         return FSDPSHARD_ERR_CAPACITY;
-    if (parts > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
-        return FSDPSHARD_ERR_ALIGNMENT;
-    if (parts > 0 && overlaps(workspace, need, sumsq, 8)) return FSDPSHARD_ERR_INVALID_ARG;
+    if (parts > 0 && !aligned8(workspace)) return FSDPSHARD_ERR_ALIGNMENT;
+    // The two written buffers (workspace, sumsq) must not overlap each other or an input.
+    const void* wr[2] = {parts > 0 ? workspace : nullptr, sumsq};
+    const int64_t wb[2] = {need, 8};
+    const int64_t sb = seg_bytes(segs, n_segments);
+    if (overlaps(wr[0], wb[0], wr[1], wb[1])) return FSDPSHARD_ERR_INVALID_ARG;
+    for (int i = 0; i < 2 && n > 0; ++i) {
+        if (fan_in == 0) {
+            if (overlaps(wr[i], wb[i], grad, n * 4)) return FSDPSHARD_ERR_INVALID_ARG;
+        } else {
+            for (int r = 0; r < fan_in; ++r)
+                if (overlaps(wr[i], wb[i], contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+        }
+        if (overlaps(wr[i], wb[i], segs, sb)) return FSDPSHARD_ERR_INVALID_ARG;
+    }
     SumsqParams p;
     for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
         p.contrib[r] = (fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
@@ -1588,24 +1334,28 @@ extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_i
     if (out == nullptr || n < 0 || sumsq == nullptr || n_segments < 0 ||
         (n_segments > 0 && segs == nullptr) || (accumulate != 0 && accumulate != 1))
         return FSDPSHARD_ERR_INVALID_ARG;
-    int rc = check_contribs(contribs, fan_in, n);
+    int rc = check_contribs(contribs, fan_in);
     if (rc != FSDPSHARD_OK) return rc;
     if (!aligned16(out)) return FSDPSHARD_ERR_ALIGNMENT;
-    if ((reinterpret_cast<uintptr_t>(sumsq) & 7u) != 0) return FSDPSHARD_ERR_ALIGNMENT;
-    if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
-        return FSDPSHARD_ERR_ALIGNMENT;
+    if (!aligned8(sumsq)) return FSDPSHARD_ERR_ALIGNMENT;
+    if (segs != nullptr && !aligned8(segs)) return FSDPSHARD_ERR_ALIGNMENT;
     if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
     const int64_t parts = sumsq_partials(n);
     if (parts > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
     const int64_t need = parts * static_cast<int64_t>(sizeof(double));
     if (parts > 0 && (workspace == nullptr || workspace_bytes < need)) return FSDPSHARD_ERR_CAPACITY;
-    if (parts > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
-        return FSDPSHARD_ERR_ALIGNMENT;
-    for (int r = 0; r < fan_in && n > 0; ++r)
-        if (overlaps(out, n * 4, contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
-    if (n > 0 && overlaps(out, n * 4, sumsq, 8)) return FSDPSHARD_ERR_INVALID_ARG;
-    if (parts > 0 && (overlaps(workspace, need, sumsq, 8) || overlaps(workspace, need, out, n * 4)))
-        return FSDPSHARD_ERR_INVALID_ARG;
+    if (parts > 0 && !aligned8(workspace)) return FSDPSHARD_ERR_ALIGNMENT;
+    // The three written buffers (out, workspace, sumsq) must not overlap each other or an input.
+    const void* wr[3] = {n > 0 ? out : nullptr, parts > 0 ? workspace : nullptr, sumsq};
+    const int64_t wb[3] = {n * 4, need, 8};
+    const int64_t sb = seg_bytes(segs, n_segments);
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(wr[i], wb[i], wr[j], wb[j])) return FSDPSHARD_ERR_INVALID_ARG;
+        for (int r = 0; r < fan_in && n > 0; ++r)
+            if (overlaps(wr[i], wb[i], contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+        if (overlaps(wr[i], wb[i], segs, sb)) return FSDPSHARD_ERR_INVALID_ARG;
+    }
     ReduceSqParams p;
     for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
     p.out = out;
@@ -1665,12 +1415,12 @@ extern "C" int unflatten_bf16(const float* master, int64_t n, const fsdpshard_se
         return FSDPSHARD_ERR_INVALID_ARG;
     if (!aligned16(master) || (reinterpret_cast<uintptr_t>(flat_bf16) & 1u) != 0)
         return FSDPSHARD_ERR_ALIGNMENT;
-    if (segs != nullptr && (reinterpret_cast<uintptr_t>(segs) & 7u) != 0)
-        return FSDPSHARD_ERR_ALIGNMENT;
+    if (segs != nullptr && !aligned8(segs)) return FSDPSHARD_ERR_ALIGNMENT;
     if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
     uint16_t* out = flat_bf16 + (lo - flat_index0);
-    if (n > 0 && overlaps(out, n * 2, master, n * 4)) return FSDPSHARD_ERR_INVALID_ARG;
     if (n == 0) return FSDPSHARD_OK;
+    if (overlaps(out, n * 2, master, n * 4) || overlaps(out, n * 2, segs, seg_bytes(segs, n_segments)))
+        return FSDPSHARD_ERR_INVALID_ARG;
     UnflattenParams p;
     p.master = master;
     p.segs = segs;
@@ -1682,86 +1432,4 @@ extern "C" int unflatten_bf16(const float* master, int64_t n, const fsdpshard_se
     int rc = tile_grid(n, 1, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
     return launch(reinterpret_cast<const void*>(&unflatten_kernel), blocks, &p, stream);
-}
-
-extern "C" int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
-    if (src == nullptr || dst == nullptr || bytes < 0 || (bytes & 15) != 0)
-        return FSDPSHARD_ERR_INVALID_ARG;
-    if (!aligned16(src) || !aligned16(dst)) return FSDPSHARD_ERR_ALIGNMENT;
-    if (bytes > 0 && overlaps(src, bytes, dst, bytes)) return FSDPSHARD_ERR_INVALID_ARG;
-    if (bytes == 0) return FSDPSHARD_OK;
-    const int64_t nvec = bytes / 16;
-    const int64_t blocks = (nvec + kBlock - 1) / kBlock;
-    if (blocks > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
-    void* args[3];
-    const uint4* s = static_cast<const uint4*>(src);
-    uint4* d = static_cast<uint4*>(dst);
-    int64_t nv = nvec;
-    args[0] = &s;
-    args[1] = &d;
-    args[2] = &nv;
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel),
-                                         dim3(static_cast<unsigned>(blocks)), dim3(kBlock), args,
-                                         0, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
-}
-
-extern "C" int fsdpshard_set_groups_per_wave(int groups) {
-    if (groups != 0 && groups != 1 && groups != 2 && groups != 4) return -1;
-    return g_groups_per_wave.exchange(groups);
-}
-
-namespace {
-// With `blocked`, s0 is the blocked state array and s1, s2 are null.
-int stream_mix_impl(const uint16_t* const* contribs, int32_t fan_in, float* s0, float* s1,
-                    float* s2, uint16_t* out, int64_t n, bool blocked, void* stream) {
-    if (s0 == nullptr || (!blocked && (s1 == nullptr || s2 == nullptr)) || out == nullptr ||
-        n < 0 || n % kVec)
-        return FSDPSHARD_ERR_INVALID_ARG;
-    int rc = check_contribs(contribs, fan_in, n);
-    if (rc != FSDPSHARD_OK) return rc;
-    if (!aligned16(s0) || (!blocked && (!aligned16(s1) || !aligned16(s2))) || !aligned16(out))
-        return FSDPSHARD_ERR_ALIGNMENT;
-    if (n > INT64_MAX / 16) return FSDPSHARD_ERR_OVERFLOW;
-    if (n == 0) return FSDPSHARD_OK;
-    const void* wr[4] = {s0, blocked ? nullptr : s1, blocked ? nullptr : s2, out};
-    const int64_t wb[4] = {blocked ? blocked_elems(n) * 4 : n * 4, n * 4, n * 4, n * 2};
-    for (int i = 0; i < 4; ++i) {
-        if (wr[i] == nullptr) continue;
-        for (int j = i + 1; j < 4; ++j)
-            if (wr[j] != nullptr && overlaps(wr[i], wb[i], wr[j], wb[j]))
-                return FSDPSHARD_ERR_INVALID_ARG;
-        for (int r = 0; r < fan_in; ++r)
-            if (overlaps(wr[i], wb[i], contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
-    }
-    MixParams p;
-    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
-    p.s[0] = s0;
-    p.s[1] = s1;
-    p.s[2] = s2;
-    p.out = out;
-    p.nvec = n / kVec;
-    p.fan_in = fan_in;
-    unsigned blocks = 0;
-    rc = tile_grid(n, 1, &blocks);
-    if (rc != FSDPSHARD_OK) return rc;
-    const void* k =
-        blocked ? (fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1, true>)
-                   : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8, true>)
-                                 : reinterpret_cast<const void*>(&stream_mix_kernel<0, true>))
-                : (fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1, false>)
-                   : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8, false>)
-                                 : reinterpret_cast<const void*>(&stream_mix_kernel<0, false>));
-    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in));   // as the step
-}
-}  // namespace
-
-extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0,
-                                    float* s1, float* s2, uint16_t* out, int64_t n, void* stream) {
-    return stream_mix_impl(contribs, fan_in, s0, s1, s2, out, n, false, stream);
-}
-
-extern "C" int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in,
-                                            float* state, uint16_t* out, int64_t n, void* stream) {
-    return stream_mix_impl(contribs, fan_in, state, nullptr, nullptr, out, n, true, stream);
 }

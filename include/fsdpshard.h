@@ -10,8 +10,8 @@
  *   - Counts and indices are int64_t.  bf16 values travel as uint16_t bit patterns.
  *   - "device" pointers are HIP device allocations on the current HIP device; "host" pointers are
  *     ordinary process memory.  The caller owns every buffer; the library never allocates device
- *     memory and keeps no state besides the process-wide tuning setting below and, per device,
- *     the cached LDS size of one compute unit (queried once, used to size launches).
+ *     memory and keeps no state besides, per device, the cached LDS size of one compute unit
+ *     (queried once, used to size launches).
  *   - `stream` is a hipStream_t passed as void* (NULL = the device's null stream).  GPU calls are
  *     asynchronous and stream-ordered: they validate their arguments on the host, enqueue their
  *     kernels (one for most calls; two for the sums of squares; reshard_copy one per 96 pieces)
@@ -202,7 +202,8 @@ int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int64_t n, flo
  *                 flat_index0 (2-byte aligned; any phase); the call writes exactly the elements
  *                 of flat indices [lo, lo + n) and nothing else.  NULL skips the bf16 output.
  *   lo            flat index of the slice start, flat_index0 <= lo
- * No written buffer may overlap another buffer of the call.
+ * No written buffer (master, m, v, the bf16 window) may overlap another buffer of the call,
+ * the segment table and grad_sumsq included.
  * Errors: INVALID_ARG (nulls, n < 0, step < 1, betas outside [0,1), non-finite values,
  *         negative max_grad_norm, clipping without grad_sumsq, overlaps, n_segments < 0),
  *         ALIGNMENT, UNSUPPORTED, HIP.
@@ -261,8 +262,11 @@ int64_t grad_sumsq_workspace_bytes(int64_t n);
  *   segs, n_segments  as in adamw_shard_step (padding does not count)
  *   workspace         device, >= grad_sumsq_workspace_bytes(n) bytes, 8-byte aligned, scratch
  *   sumsq             device, one double, receives the sum (+0 for n == 0)
- * Two kernels are enqueued on `stream`; the workspace may be reused once they have run.
- * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, CAPACITY (workspace too small), OVERFLOW, HIP.
+ * The written buffers (workspace, sumsq) may not overlap each other, a gradient input or the
+ * segment table.  Two kernels are enqueued on `stream`; the workspace may be reused once they
+ * have run.
+ * Errors: INVALID_ARG (nulls, negative sizes, overlaps), ALIGNMENT, UNSUPPORTED,
+ *         CAPACITY (workspace too small), OVERFLOW, HIP.
  */
 int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in, const float* grad,
                      int64_t n, const fsdpshard_segment* segs, int32_t n_segments, float scale,
@@ -274,7 +278,8 @@ int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in, const floa
  * [FSDP], communication pattern: after the all-gather every rank holds the full bf16 parameter
  * tensor, each rank's slice sitting at [lo, hi) of the flat layout; this writes one slice's part.
  * Arguments as in adamw_shard_step (master 16-byte aligned; flat_bf16 any 2-byte phase; segs
- * may be NULL with n_segments == 0).
+ * may be NULL with n_segments == 0).  The written window may not overlap master or the segment
+ * table.
  * Errors: INVALID_ARG, ALIGNMENT, HIP.
  */
 int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs,
@@ -296,6 +301,8 @@ int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs
  *   segs, n_segments   device segment table of the slice (padding does not count), or NULL/0
  *   workspace          device, >= grad_sumsq_workspace_bytes(n) bytes, 8-byte aligned
  *   sumsq              device, one double, receives this rank's part (+0 when n == 0)
+ * The written buffers (out, workspace, sumsq) may not overlap each other, a contribution or the
+ * segment table.
  * Errors: INVALID_ARG (nulls, overlaps, accumulate not 0 or 1), ALIGNMENT, UNSUPPORTED,
  *         CAPACITY (workspace too small), OVERFLOW, HIP.
  */
@@ -357,13 +364,6 @@ const char* fsdpshard_strerror(int code);
 
 /* FSDPSHARD_ABI_VERSION of the loaded library. */
 int fsdpshard_abi_version(void);
-
-/*
- * Tuning knob of adamw_shard_step: how many consecutive 512-element groups each wavefront owns
- * (1, 2 or 4; 0 restores the built-in choice).  Process-wide; results do not depend on it.
- * Returns the previous setting, or -1 for an unsupported value.
- */
-int fsdpshard_set_groups_per_wave(int groups);
 
 #ifdef __cplusplus
 }

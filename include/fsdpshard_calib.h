@@ -4,8 +4,15 @@
  * fsdpshard_stream_copy is a plain streaming copy of 16-byte vectors: its bandwidth is the
  * achievable-HBM reference on the same GPU, and its known byte count calibrates the hardware
  * fetch / write byte counters against which the step kernel's counter readings are scaled.
+ * fsdpshard_stream_rw measures pure reads, pure writes and fixed read : write byte ratios.
  * fsdpshard_stream_mix replays the step's exact access pattern with trivial arithmetic, which
- * separates what the memory system allows for that pattern from what the kernel's code costs.
+ * separates what the memory system allows for that pattern from what the kernel's code costs;
+ * fsdpshard_stream_mix_phased moves the same bytes with each work-group's reads and writes in
+ * separate phases.
+ *
+ * The step's bytes per parameter follow the 2 + 2 + 4 + 8 accounting of "FSDP: Fully Sharded
+ * Data Parallel Training at Scale" (memory-breakdown passage): at fan-in F it reads 2F + 12 and
+ * writes 12 + 2 bytes, so at F = 8 two thirds of its bytes are reads.
  */
 #ifndef FSDPSHARD_CALIB_H
 #define FSDPSHARD_CALIB_H
@@ -16,6 +23,8 @@
 extern "C" {
 #endif
 
+#define FSDPSHARD_CALIB_MAX_STREAMS 8
+
 /*
  * fsdpshard_stream_copy -- dst[0 .. bytes) = src[0 .. bytes).
  *   src, dst  device, 16-byte aligned, non-overlapping
@@ -24,6 +33,26 @@ extern "C" {
  * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, HIP).
  */
 int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/*
+ * fsdpshard_stream_rw -- n_src read streams and n_dst write streams, each `bytes` long.
+ *   Every 16-byte vector of every source is read once (non-temporal); destination vector i of
+ *   stream w receives the XOR of the sources' vectors i mixed with i and w (non-temporal).  With
+ *   n_dst == 0 nothing is written except, for a vector whose XOR equals a fixed constant (almost
+ *   never), that value to *sink, so the loads cannot be optimised away.  Work-groups of 256
+ *   threads each cover 16 KiB of every stream in address order (no XCD remapping).
+ *   src      host array of n_src device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS), 16-byte aligned
+ *   dst      host array of n_dst device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS), 16-byte
+ *            aligned; no destination may overlap another stream; n_src + n_dst >= 1
+ *   bytes    >= 0, a multiple of 16
+ *   per_cu   resident work-groups per CU (0: as many as the registers allow)
+ *   sink     device, one uint32 (4-byte aligned); required when n_dst == 0, else may be NULL
+ * Pure reads (n_dst 0), pure writes (n_src 0), a copy (1, 1) and the fused step's 2 : 1 read :
+ * write byte ratio at fan-in 8 (2, 1).
+ * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, OVERFLOW, HIP).
+ */
+int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* const* dst, int32_t n_dst,
+                        int64_t bytes, int32_t per_cu, uint32_t* sink, void* stream);
 
 /*
  * fsdpshard_stream_mix -- the fused step's memory traffic without its arithmetic: for every
@@ -46,6 +75,23 @@ int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float*
  */
 int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in, float* state,
                                  uint16_t* out, int64_t n, void* stream);
+
+/*
+ * fsdpshard_stream_mix_phased -- the bytes of fsdpshard_stream_mix_blocked, ordered in phases:
+ * each wavefront owns `groups_per_wave` consecutive 512-element groups and loads all of them
+ * (state, then contributions), the work-group of 4 wavefronts meets at a barrier once every
+ * wavefront holds its data, and only then are the state and out vectors stored.  With
+ * per_cu == 1 each CU alternates between a read phase of 4 * groups_per_wave groups and a write
+ * phase of the same groups.
+ *   contribs, fan_in   fan_in 1, 4 or 8 (others: UNSUPPORTED); state, out, n as
+ *                      fsdpshard_stream_mix_blocked
+ *   groups_per_wave    1, 2 or 4 (others: UNSUPPORTED)
+ *   per_cu             resident work-groups per CU (0: as many as the registers allow)
+ * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, UNSUPPORTED, OVERFLOW, HIP).
+ */
+int fsdpshard_stream_mix_phased(const uint16_t* const* contribs, int32_t fan_in, float* state,
+                                uint16_t* out, int64_t n, int32_t groups_per_wave, int32_t per_cu,
+                                void* stream);
 
 #ifdef __cplusplus
 }

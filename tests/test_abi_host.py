@@ -210,12 +210,71 @@ def test_reduce_and_unflatten_validation_errors():
     assert lib.fsdpshard_stream_copy(m, out, 8, None) == INVALID
 
 
-def test_groups_per_wave_knob():
-    prev = F.set_groups_per_wave(4)
-    assert F.set_groups_per_wave(prev) == 4
-    assert F.lib().fsdpshard_set_groups_per_wave(3) == -1
-    with pytest.raises(ValueError):
-        F.set_groups_per_wave(8)
+def test_written_buffers_checked_against_segments_and_inputs():
+    """A segment table, gradient input, workspace or sum that overlaps a buffer the call writes is
+    refused before anything is launched."""
+    lib = F.lib()
+    hp = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    a, b, c = _Fake.at(0), _Fake.at(1), _Fake.at(2)
+    g = [_Fake.at(3), _Fake.at(4)]
+    out = _Fake.at(5)
+    n = 100                                   # 400 bytes per fp32 shard, 200 per bf16 one
+    # the segment table (n_segments * 32 bytes) inside master, m, v or the bf16 window
+    for table in (a + 64, b + 256, c, out + 96):
+        assert _step(lib, a, b, c, g, 2, n, table, 2, hp, out, 0, 0) == INVALID
+    arr = (ctypes.c_void_p * 2)(*g)
+    blk = lib.adamw_shard_step_blocked
+    # the blocked state of 100 elements spans 3 * 512 floats
+    assert blk(a, arr, 2, n, a + 4096, 1, ctypes.byref(hp), out, 0, 0, None) == INVALID
+    clip = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1, 1.0, out + 8)
+    assert blk(a, arr, 2, n, None, 0, ctypes.byref(clip), out, 0, 0, None) == INVALID
+    f32 = lib.adamw_shard_step_f32grad
+    assert f32(a, b, c, g[0], n, b + 32, 1, ctypes.byref(hp), out, 0, 0, None) == INVALID
+
+    ws, res, g32 = _Fake.at(7), _Fake.at(8), _Fake.at(9)
+    sq = lib.grad_sumsq_shard
+    assert sq(arr, 2, None, n, None, 0, 1.0, g[0] + 32, 8, res, None) == INVALID   # ws in G_0
+    assert sq(arr, 2, None, n, None, 0, 1.0, ws, 8, g[1] + 64, None) == INVALID    # sum in G_1
+    assert sq(None, 0, g32, n, None, 0, 1.0, g32 + 128, 8, res, None) == INVALID   # ws in grad
+    assert sq(None, 0, g32, n, None, 0, 1.0, ws, 8, g32 + 392, None) == INVALID    # sum in grad
+    assert sq(arr, 2, None, n, ws, 1, 1.0, ws, 8, res, None) == INVALID            # table = ws
+    assert sq(arr, 2, None, n, res - 24, 1, 1.0, ws, 8, res, None) == INVALID      # table over sum
+
+    rs = lib.reduce_shard_sumsq
+    o = _Fake.at(10)
+    assert rs(arr, 2, n, 1.0, o, 0, None, 0, g[0] + 16, 8, res, None) == INVALID    # ws in G_0
+    assert rs(arr, 2, n, 1.0, o, 0, None, 0, ws, 8, g[1], None) == INVALID          # sum in G_1
+    assert rs(arr, 2, n, 1.0, o, 0, o + 64, 1, ws, 8, res, None) == INVALID         # table in out
+    assert rs(arr, 2, n, 1.0, o, 0, ws, 1, ws, 8, res, None) == INVALID             # table = ws
+
+    m = _Fake.at(6)
+    assert lib.unflatten_bf16(m, 10, out + 8, 1, out, 0, 0, None) == INVALID        # table in window
+
+
+def test_calibration_call_validation():
+    lib = F.lib()
+    vp = ctypes.c_void_p
+    src = (vp * 2)(_Fake.at(1), _Fake.at(2))
+    dst = (vp * 1)(_Fake.at(3))
+    rw = lib.fsdpshard_stream_rw
+    assert rw(src, 2, dst, 1, 0, 0, None, None) == OK
+    assert rw(src, 0, dst, 0, 16, 0, None, None) == INVALID          # no stream at all
+    assert rw(src, 1, dst, 0, 16, 0, None, None) == INVALID          # pure reads need a sink
+    assert rw(src, 9, dst, 1, 16, 0, None, None) == INVALID          # more than 8 streams
+    assert rw(src, 2, dst, 1, 8, 0, None, None) == INVALID           # not whole vectors
+    assert rw(src, 2, dst, 1, 16, -1, None, None) == INVALID
+    assert rw((vp * 1)(_Fake.at(1, 8)), 1, dst, 1, 16, 0, None, None) == ALIGN
+    assert rw(src, 2, (vp * 1)(_Fake.at(1, 16)), 1, 64, 0, None, None) == INVALID   # overlap
+    assert rw(src, 1, dst, 0, 16, 0, _Fake.at(4, 2), None) == ALIGN   # sink not 4-byte aligned
+    ph = lib.fsdpshard_stream_mix_phased
+    g8 = (vp * 8)(*[_Fake.at(10 + r) for r in range(8)])
+    st, out = _Fake.at(20), _Fake.at(21)
+    assert ph(g8, 8, st, out, 0, 4, 1, None) == OK
+    assert ph(g8, 2, st, out, 0, 4, 1, None) == UNSUP                # fan-in 1, 4, 8 only
+    assert ph(g8, 8, st, out, 0, 3, 1, None) == UNSUP                # 1, 2 or 4 groups per wave
+    assert ph(g8, 8, st, out, 12, 4, 1, None) == INVALID             # whole vectors only
+    assert ph(g8, 8, st, out, 0, 4, -1, None) == INVALID
+    assert ph(g8, 8, st, _Fake.at(20, 64), 64, 4, 1, None) == INVALID   # out inside the state
 
 
 def test_segment_dtype_matches_struct():

@@ -18,6 +18,7 @@ import workloads as W
 from oracle import clip as OC
 from oracle import layout as OL
 from oracle import step as OS
+import blocked_layout as BL
 from gpu_helpers import Guarded, assert_bf16, assert_f32, bit_equal, say, to_dev16
 
 pytestmark = pytest.mark.gpu
@@ -29,10 +30,10 @@ SENT = np.float32(np.uint32(0x7FB0B0B0).view(np.float32))
 def test_conversion_matches_definition(n):
     say(f"blocked conversion n={n}")
     a, b, c = (W.np_f32_normal([80, k], n, 1.0) for k in range(3))
-    st = Guarded(np.full(OL.blocked_state_len(n), SENT, dtype=np.float32))
+    st = Guarded(np.full(BL.blocked_state_len(n), SENT, dtype=np.float32))
     F.state_to_blocked(*(torch.from_numpy(x).cuda() for x in (a, b, c)), st.data(), n=n)
     torch.cuda.synchronize()
-    assert bit_equal(st.data_host(), OL.to_blocked(a, b, c, fill=SENT))
+    assert bit_equal(st.data_host(), BL.to_blocked(a, b, c, fill=SENT))
     st.assert_guards("blocked state")
     back = [Guarded(np.full(n, SENT, dtype=np.float32)) for _ in range(3)]
     F.state_from_blocked(st.data(), *(g.data() for g in back), n=n)
@@ -76,7 +77,7 @@ def test_blocked_step_matches_oracle_and_separate_layout(case):
     master0 = W.np_f32_normal([seed, 1], n, 0.02)
     m0 = W.np_f32_normal([seed, 2], n, 1e-3)
     v0 = (np.abs(W.np_f32_normal([seed, 3], n, 1e-3)) ** 2).astype(np.float32)
-    blk = Guarded(OL.to_blocked(master0, m0, v0, fill=SENT))
+    blk = Guarded(BL.to_blocked(master0, m0, v0, fill=SENT))
     sep = [Guarded(master0), Guarded(m0), Guarded(v0)]
     flat_b = Guarded(np.zeros(n, np.uint16), pre=d)
     flat_s = Guarded(np.zeros(n, np.uint16), pre=d)
@@ -111,7 +112,7 @@ def test_blocked_step_matches_oracle_and_separate_layout(case):
                                flat=flat_s.window(), **kw)
             om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, ohp, t)
         torch.cuda.synchronize()
-        gm, gmm, gv = OL.from_blocked(blk.data_host(), n)
+        gm, gmm, gv = BL.from_blocked(blk.data_host(), n)
         assert_f32(gm, om, f"master step {t}")
         assert_f32(gmm, omm, f"m step {t}")
         assert_f32(gv, ov, f"v step {t}")
@@ -122,7 +123,7 @@ def test_blocked_step_matches_oracle_and_separate_layout(case):
     # Unused slots of the last block are never touched.
     st = blk.data_host()
     tail = np.ones(st.size, bool)
-    tail[np.nonzero(OL.to_blocked(np.zeros(n, np.float32), np.zeros(n, np.float32),
+    tail[np.nonzero(BL.to_blocked(np.zeros(n, np.float32), np.zeros(n, np.float32),
                                   np.zeros(n, np.float32), fill=1.0) == 0.0)] = False
     assert (st[tail].view(np.uint32) == np.uint32(0x7FB0B0B0)).all()
     blk.assert_guards("blocked state")

@@ -4,9 +4,12 @@ Each trial draws a whole case from a seeded generator: tensor sizes and padding 
 size and rank, per-tensor weight-decay mask, fan-in (compile-time and run-time fan-ins up to 64)
 or an fp32 gradient shard, AdamW hyperparameters, gradient scale, clipping by the global norm
 (the squared norm taken on the GPU, as a caller would; with bf16 contributions either from the
-contributions or from the fp32 shard that reduce_shard_sumsq writes), the bf16 window's phase and
-the groups per wave.  Two steps per trial; fp32 state within relative 1e-5, bf16 within 1 ulp, NaN padding
-gradients ignored, guard bands intact.
+contributions or from the fp32 shard that reduce_shard_sumsq writes) and the bf16 window's phase.
+Two steps per trial; fp32 state within relative 1e-5, bf16 within 1 ulp, NaN padding gradients
+ignored, guard bands intact.  The library is also expected to equal the oracle bit for bit (same
+operations in the same order, no contraction, IEEE division and square root); with clipping that
+holds whenever the float32 scale formed from the device's sum of squares equals the one formed
+from the oracle's exactly rounded sum (the two sums differ in rounding order only).
 """
 
 import random
@@ -20,7 +23,8 @@ import workloads as W
 from oracle import clip as OC
 from oracle import layout as OL
 from oracle import step as OS
-from gpu_helpers import Guarded, assert_bf16, assert_f32, say, to_dev16
+import blocked_layout as BL
+from gpu_helpers import Guarded, assert_bf16, assert_f32, bit_equal, say, to_dev16
 
 pytestmark = pytest.mark.gpu
 SIZE_CHOICES = [1, 3, 7, 16, 100, 513, 2049, 4099, 30001, 70003]
@@ -44,8 +48,24 @@ def _draw(rng):
               weight_decay=rng.choice([0.0, 0.01, 0.1]),
               grad_scale=rng.choice([1.0, 0.5, 0.125]))
     return dict(sizes=sizes, pad=pad, N=N, k=k, wd=wd, F_in=rng.choice(FAN_CHOICES), hp=hp,
-                clip=rng.choice([0.0, 0.0, 1e-3, 10.0]), d=rng.randrange(8),
-                groups=rng.choice([0, 1, 2, 4]))
+                clip=rng.choice([0.0, 0.0, 1e-3, 10.0]), d=rng.randrange(8))
+
+
+def _same_scale(sumsq, clip, base, oracle_scale):
+    """Whether the float32 clip scale formed from the device's sum of squares equals the one the
+    oracle formed from its exactly rounded sum (then the steps must agree bit for bit)."""
+    torch.cuda.synchronize()
+    return float(OC.clipped_scale(float(sumsq.item()), clip, base)) == oracle_scale
+
+
+def _check_step(got, want, t, exact):
+    """Tolerance checks of one step (fp32 relative 1e-5, bf16 1 ulp), then bit equality."""
+    for (g, w), what in zip(zip(got, want), ("master", "m", "v")):
+        assert_f32(g, w, f"{what} step {t}")
+    assert_bf16(got[3], want[3], f"bf16 step {t}")
+    if exact:
+        for (g, w), what in zip(zip(got, want), ("master", "m", "v", "bf16")):
+            assert bit_equal(g, w), f"{what} step {t} not bit-equal to the oracle"
 
 
 @pytest.mark.parametrize("trial", range(40))
@@ -61,7 +81,7 @@ def test_random_fused_steps(trial):
     real = (flags & OL.PADDING) == 0
     F_in, hp, clip, d = c["F_in"], c["hp"], c["clip"], c["d"]
     say(f"random trial {trial}: n={n} lo={lo} segs={L.n_segments} F={F_in} clip={clip} d={d} "
-        f"groups={c['groups']} hp={hp}")
+        f"hp={hp}")
     sd = F.segments_to_device(segs)
     seed = 5000 + trial
     master0 = W.np_f32_normal([seed, 1], n, 0.02)
@@ -71,63 +91,59 @@ def test_random_fused_steps(trial):
     flat = Guarded(np.zeros(n, np.uint16), pre=d)
     om, omm, ov = master0.copy(), m0.copy(), v0.copy()
     sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
-    prev = F.set_groups_per_wave(c["groups"])
-    try:
-        for t in (1, 2):
-            ohp = dict(hp)
-            kw = dict(step=t, segs=sd, n_segments=L.n_segments, flat=flat.window(),
-                      flat_index0=lo - d, lo=lo, **hp)
-            if F_in == -1:
-                grad = W.np_f32_normal([seed, 10 + t], n, 1e-2)
-                grad[~real] = np.nan
-                gdev = torch.from_numpy(grad).cuda()
-                if clip:
-                    F.grad_sumsq_shard(sumsq, grad=gdev, n=n, scale=hp["grad_scale"], segs=sd,
-                                       n_segments=L.n_segments)
-                    osum = OC.sumsq_exact(grad * np.float32(hp["grad_scale"]), real)
-                    ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
-                    kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
-                F.adamw_shard_step_f32grad(gm.data(), gmm.data(), gv.data(), gdev, **kw)
-                om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, grad, flags, ohp, t)
-            else:
-                contribs = [W.np_bf16_normal([seed, 20 + t, r], n, 1e-2) for r in range(F_in)]
-                for cb in contribs:
-                    cb[~real] = 0x7FC0
-                dev = [to_dev16(cb) for cb in contribs]
-                if clip and trial % 2:
-                    # Reduce once into an fp32 shard with its norm, then the fp32-gradient step.
-                    acc = torch.empty(n, dtype=torch.float32, device="cuda")
-                    F.reduce_shard_sumsq(dev, acc, sumsq, scale=hp["grad_scale"], segs=sd,
-                                         n_segments=L.n_segments)
-                    ograd = OS.reduce_contributions(contribs, hp["grad_scale"])
-                    osum = OC.sumsq_exact(ograd, real)
-                    ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, 1.0))
-                    kw.update(max_grad_norm=clip, grad_sumsq=sumsq, grad_scale=1.0)
-                    F.adamw_shard_step_f32grad(gm.data(), gmm.data(), gv.data(), acc, **kw)
-                    om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, ograd, flags, ohp, t)
-                    torch.cuda.synchronize()
-                    assert_f32(gm.data_host(), om, f"master step {t}")
-                    assert_f32(gmm.data_host(), omm, f"m step {t}")
-                    assert_f32(gv.data_host(), ov, f"v step {t}")
-                    assert_bf16(flat.data_host(), oout, f"bf16 step {t}")
-                    continue
-                if clip:
-                    F.grad_sumsq_shard(sumsq, contribs=dev, n=n, scale=hp["grad_scale"],
-                                       segs=sd, n_segments=L.n_segments)
-                    osum = OC.grad_sumsq(contribs, real, hp["grad_scale"])
-                    ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
-                    kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
-                F.adamw_shard_step(gm.data(), gmm.data(), gv.data(), dev, **kw)
-                om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, ohp, t)
-            torch.cuda.synchronize()
-            assert_f32(gm.data_host(), om, f"master step {t}")
-            assert_f32(gmm.data_host(), omm, f"m step {t}")
-            assert_f32(gv.data_host(), ov, f"v step {t}")
-            assert_bf16(flat.data_host(), oout, f"bf16 step {t}")
-        for g, what in ((gm, "master"), (gmm, "m"), (gv, "v"), (flat, "flat window")):
-            g.assert_guards(what)
-    finally:
-        F.set_groups_per_wave(prev)
+    for t in (1, 2):
+        ohp = dict(hp)
+        exact = True
+        kw = dict(step=t, segs=sd, n_segments=L.n_segments, flat=flat.window(),
+                  flat_index0=lo - d, lo=lo, **hp)
+        if F_in == -1:
+            grad = W.np_f32_normal([seed, 10 + t], n, 1e-2)
+            grad[~real] = np.nan
+            gdev = torch.from_numpy(grad).cuda()
+            if clip:
+                F.grad_sumsq_shard(sumsq, grad=gdev, n=n, scale=hp["grad_scale"], segs=sd,
+                                   n_segments=L.n_segments)
+                osum = OC.sumsq_exact(grad * np.float32(hp["grad_scale"]), real)
+                ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                exact = _same_scale(sumsq, clip, hp["grad_scale"], ohp["grad_scale"])
+                kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
+            F.adamw_shard_step_f32grad(gm.data(), gmm.data(), gv.data(), gdev, **kw)
+            om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, grad, flags, ohp, t)
+        else:
+            contribs = [W.np_bf16_normal([seed, 20 + t, r], n, 1e-2) for r in range(F_in)]
+            for cb in contribs:
+                cb[~real] = 0x7FC0
+            dev = [to_dev16(cb) for cb in contribs]
+            if clip and trial % 2:
+                # Reduce once into an fp32 shard with its norm, then the fp32-gradient step.
+                acc = torch.empty(n, dtype=torch.float32, device="cuda")
+                F.reduce_shard_sumsq(dev, acc, sumsq, scale=hp["grad_scale"], segs=sd,
+                                     n_segments=L.n_segments)
+                ograd = OS.reduce_contributions(contribs, hp["grad_scale"])
+                osum = OC.sumsq_exact(ograd, real)
+                ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, 1.0))
+                exact = _same_scale(sumsq, clip, 1.0, ohp["grad_scale"])
+                kw.update(max_grad_norm=clip, grad_sumsq=sumsq, grad_scale=1.0)
+                F.adamw_shard_step_f32grad(gm.data(), gmm.data(), gv.data(), acc, **kw)
+                om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, ograd, flags, ohp, t)
+                torch.cuda.synchronize()
+                _check_step((gm.data_host(), gmm.data_host(), gv.data_host(), flat.data_host()),
+                            (om, omm, ov, oout), t, exact)
+                continue
+            if clip:
+                F.grad_sumsq_shard(sumsq, contribs=dev, n=n, scale=hp["grad_scale"],
+                                   segs=sd, n_segments=L.n_segments)
+                osum = OC.grad_sumsq(contribs, real, hp["grad_scale"])
+                ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                exact = _same_scale(sumsq, clip, hp["grad_scale"], ohp["grad_scale"])
+                kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
+            F.adamw_shard_step(gm.data(), gmm.data(), gv.data(), dev, **kw)
+            om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, ohp, t)
+        torch.cuda.synchronize()
+        _check_step((gm.data_host(), gmm.data_host(), gv.data_host(), flat.data_host()),
+                    (om, omm, ov, oout), t, exact)
+    for g, what in ((gm, "master"), (gmm, "m"), (gv, "v"), (flat, "flat window")):
+        g.assert_guards(what)
 
 
 @pytest.mark.parametrize("trial", range(24))
@@ -153,12 +169,13 @@ def test_random_blocked_steps(trial):
     m0 = W.np_f32_normal([seed, 2], n, 1e-3)
     v0 = (np.abs(W.np_f32_normal([seed, 3], n, 1e-3)) ** 2).astype(np.float32)
     unused = 0x7FB0B0B0
-    blk = Guarded(OL.to_blocked(master0, m0, v0, fill=np.uint32(unused).view(np.float32)))
+    blk = Guarded(BL.to_blocked(master0, m0, v0, fill=np.uint32(unused).view(np.float32)))
     flat = Guarded(np.zeros(n, np.uint16), pre=d)
     om, omm, ov = master0.copy(), m0.copy(), v0.copy()
     sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
     for t in (1, 2):
         ohp = dict(hp)
+        exact = True
         kw = dict(step=t, segs=sd, n_segments=L.n_segments, flat=flat.window(),
                   flat_index0=lo - d, lo=lo, **hp)
         if F_in == -1:
@@ -170,6 +187,7 @@ def test_random_blocked_steps(trial):
                                    n_segments=L.n_segments)
                 osum = OC.sumsq_exact(grad * np.float32(hp["grad_scale"]), real)
                 ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                exact = _same_scale(sumsq, clip, hp["grad_scale"], ohp["grad_scale"])
                 kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
             F.adamw_shard_step_f32grad_blocked(blk.data(), gdev, n=n, **kw)
             om, omm, ov, oout = OS.shard_step_f32grad(om, omm, ov, grad, flags, ohp, t)
@@ -183,17 +201,15 @@ def test_random_blocked_steps(trial):
                                    n_segments=L.n_segments)
                 osum = OC.grad_sumsq(contribs, real, hp["grad_scale"])
                 ohp["grad_scale"] = float(OC.clipped_scale(osum, clip, hp["grad_scale"]))
+                exact = _same_scale(sumsq, clip, hp["grad_scale"], ohp["grad_scale"])
                 kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
             F.adamw_shard_step_blocked(blk.data(), dev, n=n, **kw)
             om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, ohp, t)
         torch.cuda.synchronize()
-        gm, gmm, gv = OL.from_blocked(blk.data_host(), n)
-        assert_f32(gm, om, f"master step {t}")
-        assert_f32(gmm, omm, f"m step {t}")
-        assert_f32(gv, ov, f"v step {t}")
-        assert_bf16(flat.data_host(), oout, f"bf16 step {t}")
+        gm, gmm, gv = BL.from_blocked(blk.data_host(), n)
+        _check_step((gm, gmm, gv, flat.data_host()), (om, omm, ov, oout), t, exact)
     st = blk.data_host().view(np.uint32)
-    used = OL.to_blocked(np.ones(n, np.float32), np.ones(n, np.float32), np.ones(n, np.float32),
+    used = BL.to_blocked(np.ones(n, np.float32), np.ones(n, np.float32), np.ones(n, np.float32),
                          fill=0.0) != 0.0
     assert (st[~used] == np.uint32(unused)).all(), "unused slots of the last block written"
     blk.assert_guards("blocked state")
