@@ -104,6 +104,8 @@ def lib():
     h.grad_sumsq_workspace_bytes.restype = c_i64
     h.grad_sumsq_shard.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_i64, c_vp, c_i32,
                                    ctypes.c_float, c_vp, c_i64, c_vp, c_vp]
+    h.grad_sumsq_shard_noalloc.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_i64, c_vp, c_i32,
+                                           ctypes.c_float, c_vp, c_vp]
     h.reduce_shard_sumsq.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float, c_vp,
                                      c_i32, c_vp, c_i32, c_vp, c_i64, c_vp, c_vp]
     h.reshard_plan.argtypes = [ctypes.POINTER(c_i64), c_i32, c_i64, c_i32, c_i64, c_i32, c_i32,
@@ -127,7 +129,7 @@ def lib():
                  "reshard_plan", "reshard_copy",
                  "fsdpshard_abi_version", "fsdpshard_stream_copy", "fsdpshard_stream_rw",
                  "fsdpshard_stream_mix", "fsdpshard_stream_mix_blocked",
-                 "fsdpshard_stream_mix_phased", "reduce_shard_sumsq",
+                 "fsdpshard_stream_mix_phased", "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
                  "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
                  "state_to_blocked", "state_from_blocked"):
         getattr(h, name).restype = ctypes.c_int
@@ -420,6 +422,29 @@ def grad_sumsq_shard(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=No
         arr_p, fan_in, gp, n, _segs(segs, n_segments), int(n_segments), float(scale),
         _ptr(workspace, "workspace"), wbytes, _ptr(sumsq, "sumsq", {torch.float64}, 1),
         _stream(stream, sumsq)))
+
+
+NOALLOC_MAX_ELEMS = 65536 * 32768
+
+
+def grad_sumsq_shard_noalloc(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=None,
+                             n_segments=0, stream=None):
+    """grad_sumsq_shard without a workspace: the partials go to the library's own per-device
+    array (slices up to NOALLOC_MAX_ELEMS elements; calls overlapping on one GPU race)."""
+    import torch
+    if (contribs is None) == (grad is None):
+        raise ValueError("give exactly one of contribs and grad")
+    if n is None:
+        n = grad.numel() if grad is not None else contribs[0].numel()
+    n = int(n)
+    if contribs is not None:
+        arr = _contrib_array(contribs, n)
+        arr_p, fan_in, gp = ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), None
+    else:
+        arr_p, fan_in, gp = None, 0, _ptr(grad, "grad", {torch.float32}, n)
+    _check("grad_sumsq_shard_noalloc", lib().grad_sumsq_shard_noalloc(
+        arr_p, fan_in, gp, n, _segs(segs, n_segments), int(n_segments), float(scale),
+        _ptr(sumsq, "sumsq", {torch.float64}, 1), _stream(stream, sumsq)))
 
 
 def reduce_shard_sumsq(contribs, out, sumsq, accumulate=False, scale=1.0, n=None, segs=None,

@@ -38,6 +38,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fsdpshard.h"
 #include "stream_common.h"
@@ -1263,10 +1264,12 @@ extern "C" int64_t grad_sumsq_workspace_bytes(int64_t n) {
     return sumsq_partials(n) * static_cast<int64_t>(sizeof(double));
 }
 
-extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
-                                const float* grad, int64_t n, const fsdpshard_segment* segs,
-                                int32_t n_segments, float scale, void* workspace,
-                                int64_t workspace_bytes, double* sumsq, void* stream) {
+namespace {
+
+// Checks of grad_sumsq_shard's inputs and result pointer shared by its two entry points.
+int check_sumsq_args(const uint16_t* const* contribs, int32_t fan_in, const float* grad, int64_t n,
+                     const fsdpshard_segment* segs, int32_t n_segments, double* sumsq,
+                     int64_t* parts) {
     if (n < 0 || sumsq == nullptr || n_segments < 0 || (n_segments > 0 && segs == nullptr))
         return FSDPSHARD_ERR_INVALID_ARG;
     if (fan_in == 0) {
@@ -1279,14 +1282,17 @@ extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
     if (!aligned8(sumsq)) return FSDPSHARD_ERR_ALIGNMENT;
     if (segs != nullptr && !aligned8(segs)) return FSDPSHARD_ERR_ALIGNMENT;
     if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
-    const int64_t parts = sumsq_partials(n);
-    if (parts > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
-    const int64_t need = parts * static_cast<int64_t>(sizeof(double));
-    if (parts > 0 && (workspace == nullptr || workspace_bytes < need))
-        return FSDPSHARD_ERR_CAPACITY;
-    if (parts > 0 && !aligned8(workspace)) return FSDPSHARD_ERR_ALIGNMENT;
-    // The two written buffers (workspace, sumsq) must not overlap each other or an input.
-    const void* wr[2] = {parts > 0 ? workspace : nullptr, sumsq};
+    *parts = sumsq_partials(n);
+    if (*parts > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
+    return FSDPSHARD_OK;
+}
+
+// The written buffers (the partials when they are the caller's, and sumsq) must not overlap
+// each other or an input.
+int check_sumsq_overlaps(const uint16_t* const* contribs, int32_t fan_in, const float* grad,
+                         int64_t n, const fsdpshard_segment* segs, int32_t n_segments,
+                         const void* workspace, int64_t need, const double* sumsq) {
+    const void* wr[2] = {workspace, sumsq};
     const int64_t wb[2] = {need, 8};
     const int64_t sb = seg_bytes(segs, n_segments);
     if (overlaps(wr[0], wb[0], wr[1], wb[1])) return FSDPSHARD_ERR_INVALID_ARG;
@@ -1299,12 +1305,20 @@ extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
         }
         if (overlaps(wr[i], wb[i], segs, sb)) return FSDPSHARD_ERR_INVALID_ARG;
     }
+    return FSDPSHARD_OK;
+}
+
+// The two kernels of the sum of squares: one float64 partial per work-group into `partials`,
+// then their fixed-order sum into *sumsq.
+int launch_sumsq(const uint16_t* const* contribs, int32_t fan_in, const float* grad, int64_t n,
+                 const fsdpshard_segment* segs, int32_t n_segments, float scale, double* partials,
+                 int64_t parts, double* sumsq, void* stream) {
     SumsqParams p;
     for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
         p.contrib[r] = (fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
     p.grad32 = fan_in == 0 ? grad : nullptr;
     p.segs = segs;
-    p.partials = static_cast<double*>(workspace);
+    p.partials = partials;
     p.result = sumsq;
     p.n = n;
     p.groups_per_wave = kSumsqGroups;
@@ -1312,18 +1326,104 @@ extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
     p.fan_in = fan_in;
     p.n_partials = static_cast<int32_t>(parts);
     p.scale = scale;
-    int rc = FSDPSHARD_OK;
     if (parts > 0) {
         const void* k = fan_in == 0   ? reinterpret_cast<const void*>(&sumsq_kernel<-1>)
                         : fan_in == 1 ? reinterpret_cast<const void*>(&sumsq_kernel<1>)
                         : fan_in == 4 ? reinterpret_cast<const void*>(&sumsq_kernel<4>)
                         : fan_in == 8 ? reinterpret_cast<const void*>(&sumsq_kernel<8>)
                                       : reinterpret_cast<const void*>(&sumsq_kernel<0>);
-        rc = launch(k, static_cast<unsigned>(parts), &p, stream);
+        const int rc = launch(k, static_cast<unsigned>(parts), &p, stream);
         if (rc != FSDPSHARD_OK) return rc;
     }
     // One work-group adds the partials (or writes +0 for an empty slice).
     return launch(reinterpret_cast<const void*>(&sumsq_finish_kernel), 1, &p, stream);
+}
+
+}  // namespace
+
+extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
+                                const float* grad, int64_t n, const fsdpshard_segment* segs,
+                                int32_t n_segments, float scale, void* workspace,
+                                int64_t workspace_bytes, double* sumsq, void* stream) {
+    int64_t parts = 0;
+    int rc = check_sumsq_args(contribs, fan_in, grad, n, segs, n_segments, sumsq, &parts);
+    if (rc != FSDPSHARD_OK) return rc;
+    const int64_t need = parts * static_cast<int64_t>(sizeof(double));
+    if (parts > 0 && (workspace == nullptr || workspace_bytes < need))
+        return FSDPSHARD_ERR_CAPACITY;
+    if (parts > 0 && !aligned8(workspace)) return FSDPSHARD_ERR_ALIGNMENT;
+    rc = check_sumsq_overlaps(contribs, fan_in, grad, n, segs, n_segments,
+                              parts > 0 ? workspace : nullptr, need, sumsq);
+    if (rc != FSDPSHARD_OK) return rc;
+    return launch_sumsq(contribs, fan_in, grad, n, segs, n_segments, scale,
+                        static_cast<double*>(workspace), parts, sumsq, stream);
+}
+
+// ------------------------------------------------------------------------------------------------
+// grad_sumsq_shard without a caller workspace, for callers that cannot allocate device memory.
+// The float64 partials go to `scratch`, a library-owned array in each device's global segment
+// (one copy per GPU, held until the process ends).  In host code `scratch` names a host-side
+// stand-in, never the device array: kernels receive the device address that hipGetSymbolAddress
+// returned for the device the call runs on, looked up once per device and kept.
+
+static __device__ __align__(256) double scratch[FSDPSHARD_NOALLOC_MAX_PARTIALS];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+double* g_scratch_addr[kMaxDevices];   // device address of `scratch` per device; null until set
+
+// Device of `stream` (the null stream: the current device).
+int stream_device(void* stream, int* dev) {
+    if (stream != nullptr) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &d) != hipSuccess)
+            return FSDPSHARD_ERR_HIP;
+        *dev = d;
+        return FSDPSHARD_OK;
+    }
+    return hipGetDevice(dev) == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
+}
+
+// The device address of `scratch` on device `dev`: on the first call for that device, looked up
+// with that device current (then the caller's current device is restored).
+int scratch_address(int dev, double** out) {
+    if (dev < 0 || dev >= kMaxDevices) return FSDPSHARD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return FSDPSHARD_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return FSDPSHARD_ERR_HIP;
+        void* addr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return FSDPSHARD_ERR_HIP;
+        if (e != hipSuccess || addr == nullptr) return FSDPSHARD_ERR_HIP;
+        g_scratch_addr[dev] = static_cast<double*>(addr);
+    }
+    *out = g_scratch_addr[dev];
+    return FSDPSHARD_OK;
+}
+
+}  // namespace
+
+extern "C" int grad_sumsq_shard_noalloc(const uint16_t* const* contribs, int32_t fan_in,
+                                        const float* grad, int64_t n,
+                                        const fsdpshard_segment* segs, int32_t n_segments,
+                                        float scale, double* sumsq, void* stream) {
+    int64_t parts = 0;
+    int rc = check_sumsq_args(contribs, fan_in, grad, n, segs, n_segments, sumsq, &parts);
+    if (rc != FSDPSHARD_OK) return rc;
+    if (parts > FSDPSHARD_NOALLOC_MAX_PARTIALS) return FSDPSHARD_ERR_CAPACITY;
+    rc = check_sumsq_overlaps(contribs, fan_in, grad, n, segs, n_segments, nullptr, 0, sumsq);
+    if (rc != FSDPSHARD_OK) return rc;
+    int dev = 0;
+    rc = stream_device(stream, &dev);
+    if (rc != FSDPSHARD_OK) return rc;
+    double* partials = nullptr;
+    rc = scratch_address(dev, &partials);
+    if (rc != FSDPSHARD_OK) return rc;
+    return launch_sumsq(contribs, fan_in, grad, n, segs, n_segments, scale, partials, parts, sumsq,
+                        stream);
 }
 
 extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_in, int64_t n,

@@ -273,6 +273,28 @@ int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in, const floa
                      void* workspace, int64_t workspace_bytes, double* sumsq, void* stream);
 
 /*
+ * grad_sumsq_shard_noalloc -- grad_sumsq_shard with no workspace argument.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).  Its float64 partials live in a library-owned array of
+ * FSDPSHARD_NOALLOC_MAX_PARTIALS doubles (512 KiB) in each device's global segment, held by every
+ * GPU the library runs on until the process ends; its device address is looked up once per
+ * device, on the first call whose stream belongs to that device (make that first call outside a
+ * graph capture).  Slices of up to FSDPSHARD_NOALLOC_MAX_ELEMS elements are accepted; a longer
+ * slice returns CAPACITY.  Every partial the second kernel reads is written by the first kernel
+ * of the same call, so nothing has to be cleared between calls; but all calls on one GPU share
+ * the one array, so calls that overlap in time on one GPU (work on different streams, or host
+ * threads without an ordering between their calls) race and give wrong sums.
+ * Arguments, results and the other errors are those of grad_sumsq_shard.
+ */
+#define FSDPSHARD_NOALLOC_MAX_PARTIALS 65536
+#define FSDPSHARD_NOALLOC_MAX_ELEMS ((int64_t)FSDPSHARD_NOALLOC_MAX_PARTIALS * 32768)
+int grad_sumsq_shard_noalloc(const uint16_t* const* contribs, int32_t fan_in, const float* grad,
+                             int64_t n, const fsdpshard_segment* segs, int32_t n_segments,
+                             float scale, double* sumsq, void* stream);
+
+/*
  * unflatten_bf16 -- flat[lo + i] = bf16_rne(master[i]) for real elements, +0 for padding.
  *
  * [FSDP], communication pattern: after the all-gather every rank holds the full bf16 parameter

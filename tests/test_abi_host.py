@@ -335,6 +335,22 @@ def test_sumsq_validation_and_workspace():
     assert f(arr, 2, None, 100, None, 0, 1.0, ws, 8, ws, None) == INVALID          # overlap
 
 
+def test_noalloc_sumsq_validation():
+    # The allocation-free sum of squares takes no workspace and refuses slices longer than its
+    # library-owned array covers (CAPACITY), before any HIP call.
+    lib = F.lib()
+    arr = (ctypes.c_void_p * 2)(_Fake.at(3), _Fake.at(4))
+    res = _Fake.at(8)
+    f = lib.grad_sumsq_shard_noalloc
+    assert F.NOALLOC_MAX_ELEMS == 2 ** 31
+    assert f(arr, 2, None, F.NOALLOC_MAX_ELEMS + 1, None, 0, 1.0, res, None) == CAPACITY
+    assert f(arr, 2, None, 100, None, 0, 1.0, None, None) == INVALID
+    assert f(arr, 2, None, 100, None, 0, 1.0, res + 4, None) == ALIGN
+    assert f(arr, 2, None, 100, None, 0, 1.0, _Fake.at(3, 16), None) == INVALID   # sum in G_0
+    assert f(arr, 65, None, 100, None, 0, 1.0, res, None) == UNSUP
+    assert f(None, 0, None, 100, None, 0, 1.0, res, None) == INVALID
+
+
 def test_reduce_sumsq_validation():
     # Every error is reported before anything is launched (fake device addresses are never
     # dereferenced).
