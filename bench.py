@@ -451,10 +451,17 @@ def time_launches(torch, launch, stream, reps=5, warm=2, evict=None):
     return total / reps
 
 
-def mix_references(F, torch, S, stream, evict, phased=False):
+# Launch shapes of the step's traffic replica (groups per wave, work-groups per CU, XCD run,
+# phased): the step's own shape, the best unphased shapes of a sweep of the exact bytes at
+# fan-in 8, and phased shapes (each work-group's loads before any of its stores).
+MIX_SHAPES = [(1, 2, 32, 0), (1, 1, 16, 0), (1, 1, 64, 0), (1, 2, 32, 1), (2, 1, 32, 1),
+              (4, 1, 32, 1)]
+
+
+def mix_references(F, torch, S, stream, evict, shapes=False):
     """The step's loads and stores with trivial arithmetic on this slice's own buffers: in the
-    step's order (same grid, tile map and work-groups per CU), and, with `phased`, each
-    work-group's reads and writes in separate phases (blocked state only)."""
+    step's order (same grid, tile map and work-groups per CU), and, with `shapes`, in the other
+    launch shapes of MIX_SHAPES (blocked state only); `best` is the fastest of them."""
     n8 = S.L.n - S.L.n % 8
     if n8 == 0:
         return None
@@ -469,14 +476,17 @@ def mix_references(F, torch, S, stream, evict, phased=False):
     ref = {"step_order": {"GBps": round(n8 * bpp / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4),
                           "kernel": "fsdpshard_stream_mix" + ("_blocked" if S.blocked else "")},
            "flushed": evict is not None}
-    if phased and S.blocked and S.w.fan_in in (1, 4, 8):
-        for G, per_cu in ((1, 2), (2, 1), (2, 2), (4, 1)):
-            ms = time_launches(torch, lambda: F.stream_mix_phased(
-                S.grads, S.state, out16, n8, G, per_cu, stream=stream), stream, evict=evict)
-            ref[f"phased_g{G}_cu{per_cu}"] = {
-                "GBps": round(n8 * bpp / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4),
-                "kernel": f"fsdpshard_stream_mix_phased ({G} groups per wave, {per_cu} "
-                          "work-groups per CU)"}
+    best = dict(ref["step_order"], shape="the step's")
+    if shapes and S.blocked and S.w.fan_in in (1, 4, 8):
+        for G, per_cu, run, phased in MIX_SHAPES:
+            ms = time_launches(torch, lambda: F.stream_mix_shaped(
+                S.grads, S.state, out16, n8, G, per_cu, run, phased, stream=stream), stream,
+                evict=evict)
+            name = f"g{G}_cu{per_cu}_run{run}" + ("_phased" if phased else "")
+            ref[name] = {"GBps": round(n8 * bpp / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4)}
+            if ref[name]["GBps"] > best["GBps"]:
+                best = dict(ref[name], shape=name)
+    ref["best"] = best
     del out16
     return ref
 
@@ -509,10 +519,21 @@ def measure_workload(F, W, torch, name, blocked, args, dev, stream, mix=True):
     return out
 
 
+# Launch shapes of the plain-stream probes (vectors per thread, threads per work-group,
+# work-groups per CU, XCD run): the fastest few of a sweep of 216 shapes per stream kind on
+# MI355X.
+CEILING_SHAPES = {
+    "read": [(1, 1024, 0, 1), (4, 1024, 0, 32), (2, 512, 0, 32)],
+    "write": [(2, 256, 2, 256), (1, 256, 4, 1), (8, 256, 1, 32)],
+    "copy": [(2, 256, 0, 256), (1, 256, 0, 1), (2, 1024, 0, 32)],
+    "read2_write1": [(1, 256, 0, 256), (2, 512, 0, 32), (1, 256, 0, 32)],
+}
+
+
 def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=4 << 30):
     """What the memory system does for plain streams on this GPU: pure reads, pure writes, a
-    copy, and the step's 2 : 1 read : write byte ratio, each with and without a cap of 2
-    work-groups per CU (best reported), plus the time bound they imply for the step's bytes."""
+    copy, and the step's 2 : 1 read : write byte ratio (each the best of a few launch shapes),
+    plus the time bound the pure rates imply for the step's bytes."""
     bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(3)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     for b in bufs:
@@ -523,15 +544,16 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=4 
     out = {}
     for name, (srcs, dsts, moved) in cases.items():
         best = None
-        for per_cu in (0, 2):
-            ms = time_launches(torch, lambda: F.stream_rw(srcs, dsts, nbytes, per_cu=per_cu,
-                                                          sink=sink, stream=stream),
-                               stream, reps=10)
+        for vpt, threads, per_cu, run in CEILING_SHAPES[name]:
+            ms = time_launches(torch, lambda: F.stream_rw(
+                srcs, dsts, nbytes, vectors_per_thread=vpt, threads_per_group=threads,
+                per_cu=per_cu, xcd_run=run, sink=sink, stream=stream), stream, reps=10)
             gbps = moved / (ms / 1e3) / 1e9
             if best is None or gbps > best["GBps"]:
-                best = {"GBps": round(gbps, 1), "per_cu": per_cu}
+                best = {"GBps": round(gbps, 1), "shape": [vpt, threads, per_cu, run]}
         out[name] = best
-        log(f"  {name}: {best['GBps']} GB/s (work-groups per CU {best['per_cu'] or 'uncapped'})")
+        log(f"  {name}: {best['GBps']} GB/s (vectors per thread, threads, per CU, XCD run: "
+            f"{best['shape']})")
     ms = time_launches(torch, lambda: F.stream_copy(A, B, stream=stream), stream, reps=10)
     out["copy_plain"] = {"GBps": round(2 * nbytes / (ms / 1e3) / 1e9, 1),
                          "kernel": "fsdpshard_stream_copy (the counters' calibration kernel)"}
@@ -649,7 +671,7 @@ def main():
 
     mix_ref = None
     if not args.no_copy_reference and args.path == "fused":
-        mix_ref = mix_references(F, torch, S, stream, evict, phased=True)
+        mix_ref = mix_references(F, torch, S, stream, evict, shapes=True)
         for k, x in (mix_ref or {}).items():
             if isinstance(x, dict):
                 log(f"  traffic replica {k}: {x['GBps']} GB/s")

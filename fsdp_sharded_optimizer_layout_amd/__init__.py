@@ -121,15 +121,15 @@ def lib():
     h.fsdpshard_stream_mix_blocked.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_i64,
                                                c_vp]
     h.fsdpshard_stream_rw.argtypes = [ctypes.POINTER(c_vp), c_i32, ctypes.POINTER(c_vp), c_i32,
-                                      c_i64, c_i32, c_vp, c_vp]
-    h.fsdpshard_stream_mix_phased.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_i64,
-                                              c_i32, c_i32, c_vp]
+                                      c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
+    h.fsdpshard_stream_mix_shaped.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_i64,
+                                              c_i32, c_i32, c_i32, c_i32, c_vp]
     for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
                  "adamw_shard_step_f32grad", "reduce_shard_accumulate", "grad_sumsq_shard",
                  "reshard_plan", "reshard_copy",
                  "fsdpshard_abi_version", "fsdpshard_stream_copy", "fsdpshard_stream_rw",
                  "fsdpshard_stream_mix", "fsdpshard_stream_mix_blocked",
-                 "fsdpshard_stream_mix_phased", "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
+                 "fsdpshard_stream_mix_shaped", "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
                  "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
                  "state_to_blocked", "state_from_blocked"):
         getattr(h, name).restype = ctypes.c_int
@@ -488,9 +488,11 @@ def stream_copy(src, dst, nbytes=None, stream=None):
         _ptr(src, "src"), _ptr(dst, "dst"), nbytes, _stream(stream, src)))
 
 
-def stream_rw(srcs, dsts, nbytes, per_cu=0, sink=None, stream=None):
-    """Measurement aid: len(srcs) read streams and len(dsts) write streams of ``nbytes`` each
-    (pure reads when ``dsts`` is empty; then ``sink`` is a device tensor of at least 4 bytes)."""
+def stream_rw(srcs, dsts, nbytes, vectors_per_thread=4, threads_per_group=256, per_cu=0,
+              xcd_run=0, sink=None, stream=None):
+    """Measurement aid: len(srcs) read streams and len(dsts) write streams of ``nbytes`` each in
+    one launch shape (pure reads when ``dsts`` is empty; then ``sink`` is a device tensor of at
+    least 4 bytes)."""
     nbytes = int(nbytes)
     for i, t in enumerate(list(srcs) + list(dsts)):
         _need_bytes(t, f"stream {i}", nbytes)
@@ -500,8 +502,9 @@ def stream_rw(srcs, dsts, nbytes, per_cu=0, sink=None, stream=None):
     dst_arr = (c_vp * max(1, len(dsts)))(*[_ptr(t, "destination") for t in dsts])
     _check("fsdpshard_stream_rw", lib().fsdpshard_stream_rw(
         ctypes.cast(src_arr, ctypes.POINTER(c_vp)), len(srcs),
-        ctypes.cast(dst_arr, ctypes.POINTER(c_vp)), len(dsts), nbytes, int(per_cu),
-        _ptr(sink, "sink"), _stream(stream, like)))
+        ctypes.cast(dst_arr, ctypes.POINTER(c_vp)), len(dsts), nbytes, int(vectors_per_thread),
+        int(threads_per_group), int(per_cu), int(xcd_run), _ptr(sink, "sink"),
+        _stream(stream, like)))
 
 
 def stream_mix(contribs, s0, s1, s2, out, n=None, stream=None):
@@ -526,16 +529,18 @@ def stream_mix_blocked(contribs, state, out, n, stream=None):
         _ptr(out, "out"), n, _stream(stream, state)))
 
 
-def stream_mix_phased(contribs, state, out, n, groups_per_wave, per_cu, stream=None):
-    """Measurement aid: stream_mix_blocked's bytes with each work-group's loads and stores in
-    separate phases (see fsdpshard_stream_mix_phased)."""
+def stream_mix_shaped(contribs, state, out, n, groups_per_wave, per_cu, xcd_run, phased,
+                      stream=None):
+    """Measurement aid: stream_mix_blocked's bytes in another launch shape, optionally with each
+    work-group's loads and stores in separate phases (see fsdpshard_stream_mix_shaped)."""
     n = int(n)
     arr = _contrib_array(contribs, n)
     _need_bytes(state, "state", 4 * state_blocked_elems(n))
     _need_bytes(out, "out", 2 * n)
-    _check("fsdpshard_stream_mix_phased", lib().fsdpshard_stream_mix_phased(
+    _check("fsdpshard_stream_mix_shaped", lib().fsdpshard_stream_mix_shaped(
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(state, "state"),
-        _ptr(out, "out"), n, int(groups_per_wave), int(per_cu), _stream(stream, state)))
+        _ptr(out, "out"), n, int(groups_per_wave), int(per_cu), int(xcd_run),
+        1 if phased else 0, _stream(stream, state)))
 
 
 # ------------------------------------------------------------------------------ reshard

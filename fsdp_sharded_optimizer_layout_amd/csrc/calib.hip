@@ -4,15 +4,18 @@
 //   * stream_copy_kernel   one read and one write stream (the classic copy).
 //   * stream_rw_kernel     R read streams and W write streams of equal length: pure reads
 //                          (W = 0), pure writes (R = 0), a copy (1, 1), or the 2 : 1 read : write
-//                          byte ratio of the fused step at fan-in 8 (2, 1).
+//                          byte ratio of the fused step at fan-in 8 (2, 1), in any launch shape
+//                          (vectors per thread, threads per work-group, work-groups per CU, XCD
+//                          run length).
 //   * stream_mix_kernel    the fused step's exact loads and stores (same vector width, cache
 //                          hints, tile map, load issue order and work-groups per CU) with
 //                          trivial integer arithmetic in place of the reduction and the update.
-//   * stream_mix_phased_kernel
-//                          the same bytes as the blocked-state step, ordered in phases: each
-//                          wave loads G consecutive groups, the work-group meets at a barrier,
-//                          and only then does any wave of it store.  With one work-group per CU
-//                          a CU alternates between a pure-read and a pure-write phase.
+//   * stream_mix_shaped_kernel
+//                          the same bytes as the blocked-state step in other shapes: G groups
+//                          per wave, any work-groups per CU and XCD run, and optionally in phases
+//                          (the work-group meets at a barrier after its loads, before any store;
+//                          with one work-group per CU a CU alternates between a pure-read and a
+//                          pure-write phase).
 //
 // Every kernel checks each vector index against the stream length, so any grid is safe.
 
@@ -38,10 +41,29 @@ __global__ __launch_bounds__(kBlock) void stream_copy_kernel(const uint4* __rest
 }
 
 // ------------------------------------------------------------------------------------------------
+// Work-group -> tile with a run length chosen at launch (the library kernels fix theirs at
+// compile time): run <= 1 is the identity, otherwise each XCD streams runs of `run` tiles.
+__device__ __forceinline__ int64_t tile_index_rt(int64_t run) {
+    const int64_t b = blockIdx.x;
+    if (run <= 1) return b;
+    const int64_t whole = static_cast<int64_t>(gridDim.x) / (kXcds * run) * (kXcds * run);
+    if (b >= whole) return b;
+    const int64_t x = b % kXcds, q = b / kXcds;
+    return (q / run) * (kXcds * run) + x * run + q % run;
+}
+
+inline int launch_shaped(const void* kernel, unsigned blocks, int threads, void* params,
+                         void* stream, int per_cu) {
+    void* args[] = {params};
+    const hipError_t e = hipLaunchKernel(kernel, dim3(blocks), dim3(threads), args,
+                                         occupancy_lds(per_cu), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FSDPSHARD_OK : FSDPSHARD_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------------------
 // R read streams, W write streams.
 
 constexpr int kRwMaxStreams = FSDPSHARD_CALIB_MAX_STREAMS;
-constexpr int kRwVecs = 4;   // 16-byte vectors per thread per stream (a work-group: 16 KiB each)
 constexpr uint32_t kSinkMagic = 0x9E3779B9u;
 
 struct RwParams {
@@ -49,33 +71,37 @@ struct RwParams {
     u32x4_t* dst[kRwMaxStreams];
     uint32_t* sink;
     int64_t nvec;
+    int64_t run;
     int32_t n_src, n_dst;
 };
 
-// Thread t of work-group b handles vectors b * 1024 + u * 256 + t, u = 0..3, of every stream:
-// all loads first, then the XOR of the loaded words (mixed with the index) to every write stream.
-// With no write stream, a lane whose XOR equals a fixed constant stores it to `sink`, so the
-// loads cannot be dropped and almost no bytes are written.
-__global__ __launch_bounds__(kBlock) void stream_rw_kernel(RwParams p) {
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * (kBlock * kRwVecs) + threadIdx.x;
-    u32x4_t x[kRwVecs];
+// Thread t of the work-group on tile b handles vectors b * T * V + u * T + t, u < V (T threads
+// per work-group, V vectors per thread), of every stream: all loads first, then the XOR of the
+// loaded words (mixed with the index) to every write stream.  With no write stream, a lane whose
+// XOR equals a fixed constant stores it to `sink`, so the loads cannot be dropped and almost no
+// bytes are written.
+template <int V>
+__global__ __launch_bounds__(1024) void stream_rw_kernel(RwParams p) {
+    const int64_t T = blockDim.x;
+    const int64_t base = tile_index_rt(p.run) * T * V + threadIdx.x;
+    u32x4_t x[V];
 #pragma unroll
-    for (int u = 0; u < kRwVecs; ++u) {
-        const uint32_t i32 = static_cast<uint32_t>(base + u * kBlock);
+    for (int u = 0; u < V; ++u) {
+        const uint32_t i32 = static_cast<uint32_t>(base + u * T);
         x[u] = u32x4_t{i32, i32 ^ 0x55555555u, i32 ^ 0x33333333u, i32 ^ 0x0F0F0F0Fu};
     }
 #pragma unroll
     for (int r = 0; r < kRwMaxStreams; ++r) {
         if (r >= p.n_src) break;
 #pragma unroll
-        for (int u = 0; u < kRwVecs; ++u) {
-            const int64_t i = base + u * kBlock;
+        for (int u = 0; u < V; ++u) {
+            const int64_t i = base + u * T;
             if (i < p.nvec) x[u] ^= __builtin_nontemporal_load(p.src[r] + i);
         }
     }
     if (p.n_dst == 0) {
 #pragma unroll
-        for (int u = 0; u < kRwVecs; ++u)
+        for (int u = 0; u < V; ++u)
             if ((x[u].x ^ x[u].y ^ x[u].z ^ x[u].w) == kSinkMagic) *p.sink = x[u].x;
         return;
     }
@@ -83,8 +109,8 @@ __global__ __launch_bounds__(kBlock) void stream_rw_kernel(RwParams p) {
     for (int w = 0; w < kRwMaxStreams; ++w) {
         if (w >= p.n_dst) break;
 #pragma unroll
-        for (int u = 0; u < kRwVecs; ++u) {
-            const int64_t i = base + u * kBlock;
+        for (int u = 0; u < V; ++u) {
+            const int64_t i = base + u * T;
             if (i < p.nvec) {
                 u32x4_t y = x[u];
                 y.x += static_cast<uint32_t>(w);
@@ -102,6 +128,7 @@ struct MixParams {
     float* s[3];
     uint16_t* out;
     int64_t nvec;
+    int64_t run;             // XCD run length of the shaped replica
     int32_t fan_in;
 };
 
@@ -155,15 +182,16 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
                                     __float_as_uint(st[2][1]), x));
 }
 
-// Blocked-state replica in phases: wave w owns G consecutive groups; it issues every load of
-// its G groups (state first, then the contributions) and folds all loaded words into one XOR,
-// so it holds all its data before the work-group barrier; no wave of the work-group stores
-// before every wave has loaded.  Same bytes per element as stream_mix_kernel.
-template <int F, int G>
-__global__ __launch_bounds__(kBlock) void stream_mix_phased_kernel(MixParams p) {
+// Blocked-state replica of any shape: wave w owns G consecutive groups and issues every load of
+// them (state first, then the contributions), folding all loaded words into one XOR so that it
+// holds all its data; with PHASED no wave of the work-group stores before every wave has loaded
+// (a work-group barrier), otherwise each wave stores as soon as it can.  Same bytes per element
+// as stream_mix_kernel; work-groups take tiles through the XCD map with run length p.run.
+template <int F, int G, bool PHASED>
+__global__ __launch_bounds__(kBlock) void stream_mix_shaped_kernel(MixParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
-    const int64_t base = tile_base<kStepXcdRun>(wave, G);
+    const int64_t base = (tile_index_rt(p.run) * kWavesPerBlock + wave) * (kWave * G);
     float st[G][3][kVec];
     uint4 raw[G][F];
     uint32_t x[G];
@@ -190,9 +218,11 @@ __global__ __launch_bounds__(kBlock) void stream_mix_phased_kernel(MixParams p) 
                 for (int e = 1; e < kVec; ++e) x[g] ^= __float_as_uint(st[g][k][e]);
         }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PHASED) {
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int64_t vec = base + g * kWave + lane;
@@ -210,12 +240,12 @@ __global__ __launch_bounds__(kBlock) void stream_mix_phased_kernel(MixParams p) 
     }
 }
 
-template <int G>
-const void* phased_kernel(int fan_in) {
+template <int G, bool PHASED>
+const void* shaped_kernel(int fan_in) {
     switch (fan_in) {
-        case 1: return reinterpret_cast<const void*>(&stream_mix_phased_kernel<1, G>);
-        case 4: return reinterpret_cast<const void*>(&stream_mix_phased_kernel<4, G>);
-        case 8: return reinterpret_cast<const void*>(&stream_mix_phased_kernel<8, G>);
+        case 1: return reinterpret_cast<const void*>(&stream_mix_shaped_kernel<1, G, PHASED>);
+        case 4: return reinterpret_cast<const void*>(&stream_mix_shaped_kernel<4, G, PHASED>);
+        case 8: return reinterpret_cast<const void*>(&stream_mix_shaped_kernel<8, G, PHASED>);
         default: return nullptr;
     }
 }
@@ -253,6 +283,7 @@ void fill_mix(MixParams& p, const uint16_t* const* contribs, int32_t fan_in, flo
     p.out = out;
     p.nvec = n / kVec;
     p.fan_in = fan_in;
+    p.run = 1;
 }
 
 int stream_mix_impl(const uint16_t* const* contribs, int32_t fan_in, float* s0, float* s1,
@@ -299,13 +330,22 @@ extern "C" int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, 
 }
 
 extern "C" int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* const* dst,
-                                   int32_t n_dst, int64_t bytes, int32_t per_cu, uint32_t* sink,
-                                   void* stream) {
+                                   int32_t n_dst, int64_t bytes, int32_t vectors_per_thread,
+                                   int32_t threads_per_group, int32_t per_cu, int32_t xcd_run,
+                                   uint32_t* sink, void* stream) {
     if (n_src < 0 || n_dst < 0 || n_src > kRwMaxStreams || n_dst > kRwMaxStreams ||
-        n_src + n_dst == 0 || bytes < 0 || (bytes & 15) != 0 || per_cu < 0 ||
+        n_src + n_dst == 0 || bytes < 0 || (bytes & 15) != 0 || per_cu < 0 || xcd_run < 0 ||
         (n_src > 0 && src == nullptr) || (n_dst > 0 && dst == nullptr) ||
         (n_dst == 0 && sink == nullptr))
         return FSDPSHARD_ERR_INVALID_ARG;
+    const void* k = vectors_per_thread == 1   ? reinterpret_cast<const void*>(&stream_rw_kernel<1>)
+                    : vectors_per_thread == 2 ? reinterpret_cast<const void*>(&stream_rw_kernel<2>)
+                    : vectors_per_thread == 4 ? reinterpret_cast<const void*>(&stream_rw_kernel<4>)
+                    : vectors_per_thread == 8 ? reinterpret_cast<const void*>(&stream_rw_kernel<8>)
+                                              : nullptr;
+    if (k == nullptr || (threads_per_group != 256 && threads_per_group != 512 &&
+                         threads_per_group != 1024))
+        return FSDPSHARD_ERR_UNSUPPORTED;
     for (int r = 0; r < n_src; ++r) {
         if (src[r] == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
         if (!aligned16(src[r])) return FSDPSHARD_ERR_ALIGNMENT;
@@ -328,13 +368,13 @@ extern "C" int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* 
     }
     p.sink = sink;
     p.nvec = bytes / 16;
+    p.run = xcd_run;
     p.n_src = n_src;
     p.n_dst = n_dst;
-    const int64_t per_block = static_cast<int64_t>(kBlock) * kRwVecs;
+    const int64_t per_block = static_cast<int64_t>(threads_per_group) * vectors_per_thread;
     const int64_t blocks = (p.nvec + per_block - 1) / per_block;
     if (blocks > 0x7FFFFFFF) return FSDPSHARD_ERR_OVERFLOW;
-    return launch(reinterpret_cast<const void*>(&stream_rw_kernel), static_cast<unsigned>(blocks),
-                  &p, stream, per_cu);
+    return launch_shaped(k, static_cast<unsigned>(blocks), threads_per_group, &p, stream, per_cu);
 }
 
 extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan_in, float* s0,
@@ -347,21 +387,26 @@ extern "C" int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int
     return stream_mix_impl(contribs, fan_in, state, nullptr, nullptr, out, n, true, stream);
 }
 
-extern "C" int fsdpshard_stream_mix_phased(const uint16_t* const* contribs, int32_t fan_in,
+extern "C" int fsdpshard_stream_mix_shaped(const uint16_t* const* contribs, int32_t fan_in,
                                            float* state, uint16_t* out, int64_t n,
                                            int32_t groups_per_wave, int32_t per_cu,
-                                           void* stream) {
+                                           int32_t xcd_run, int32_t phased, void* stream) {
     int rc = check_mix(contribs, fan_in, state, nullptr, nullptr, out, n, true);
     if (rc != FSDPSHARD_OK) return rc;
-    if (per_cu < 0) return FSDPSHARD_ERR_INVALID_ARG;
-    const void* k = groups_per_wave == 1   ? phased_kernel<1>(fan_in)
-                    : groups_per_wave == 2 ? phased_kernel<2>(fan_in)
-                    : groups_per_wave == 4 ? phased_kernel<4>(fan_in)
+    if (per_cu < 0 || xcd_run < 0 || (phased != 0 && phased != 1)) return FSDPSHARD_ERR_INVALID_ARG;
+    const bool ph = phased != 0;
+    const void* k = groups_per_wave == 1   ? (ph ? shaped_kernel<1, true>(fan_in)
+                                                 : shaped_kernel<1, false>(fan_in))
+                    : groups_per_wave == 2 ? (ph ? shaped_kernel<2, true>(fan_in)
+                                                 : shaped_kernel<2, false>(fan_in))
+                    : groups_per_wave == 4 ? (ph ? shaped_kernel<4, true>(fan_in)
+                                                 : shaped_kernel<4, false>(fan_in))
                                            : nullptr;
     if (k == nullptr) return FSDPSHARD_ERR_UNSUPPORTED;
     if (n == 0) return FSDPSHARD_OK;
     MixParams p;
     fill_mix(p, contribs, fan_in, state, nullptr, nullptr, out, n);
+    p.run = xcd_run;
     unsigned blocks = 0;
     rc = tile_grid(n, groups_per_wave, &blocks);
     if (rc != FSDPSHARD_OK) return rc;

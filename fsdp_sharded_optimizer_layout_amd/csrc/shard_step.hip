@@ -221,13 +221,17 @@ __device__ __forceinline__ uint4 rephase(const uint32_t (&w)[4], const uint32_t 
     return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-__device__ __forceinline__ void store_bf16_vec(uint16_t* out, int64_t e0, int shift,
-                                               const uint32_t (&w)[4], bool valid, int cnt,
-                                               bool next_ok, bool prev_ok) {
-    // Every lane takes part in the permutes (inactive lanes would read back zeros).
-    uint32_t x[4];
+// The next lane's 8 packed words (every lane must take part in the permutes: inactive lanes
+// would read back zeros).  The last lane of the wave gets its own words back.
+__device__ __forceinline__ void next_lane_words(const uint32_t (&w)[4], uint32_t (&x)[4]) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = __shfl_down(w[k], 1, kWave);
+}
+
+// Stores this lane's part of the bf16 slice given the next lane's words x (see above).
+__device__ __forceinline__ void store_bf16_words(uint16_t* out, int64_t e0, int shift,
+                                                 const uint32_t (&w)[4], const uint32_t (&x)[4],
+                                                 bool valid, int cnt, bool next_ok, bool prev_ok) {
     if (!valid) return;
 
     uint32_t narrow = 0;  // bit e: write element e with a 2-byte store
@@ -260,6 +264,21 @@ __device__ __forceinline__ void store_bf16_vec(uint16_t* out, int64_t e0, int sh
             if (narrow & (1u << e))
                 out[e0 + e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
     }
+}
+
+__device__ __forceinline__ void store_bf16_vec(uint16_t* out, int64_t e0, int shift,
+                                               const uint32_t (&w)[4], bool valid, int cnt,
+                                               bool next_ok, bool prev_ok) {
+    uint32_t x[4];
+    next_lane_words(w, x);
+    store_bf16_words(out, e0, shift, w, x, valid, cnt, next_ok, prev_ok);
+}
+
+// LDS-only work-group barrier: this wave's LDS writes are complete before it waits, and no LDS
+// read after it is issued before every wave has arrived.  (Global stores in flight are not
+// waited for, unlike __syncthreads.)
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -419,8 +438,14 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
 // A wave's complete group (compile-time gradient source F >= 1 or F == -1): every HBM load of
 // the group is issued first (gradients non-temporal), then the segment cursor is placed, then
 // the group is reduced, updated and stored.
+// With `edges` (an off-phase destination and a work-group whose four groups are all whole),
+// the group edges between the work-group's waves are stored whole: each wave's first lane
+// publishes its packed words in LDS, and after a barrier the previous wave's last lane builds
+// the aligned 16-byte vector that spans the edge, as every other lane does from its right
+// neighbour.  Only the work-group's own first and last edges are left to 2-byte stores.
 template <int F, bool OUT, bool BLK>
-__device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb, int lane) {
+__device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb, int lane,
+                                                 int wave, bool edges) {
     uint4 raw[F > 0 ? F : 1];
     float gf[kVec], th[kVec], mm[kVec], vv[kVec];
     const int64_t e0 = (gb + lane) * kVec;
@@ -456,12 +481,24 @@ __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb
     store8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
     store8(state_ptr<BLK>(p, 2, e0), true, kVec, vv);
     if constexpr (OUT) {
-        uint32_t w[4];
+        uint32_t w[4], x[4];
         pack_out(fl, th, w);
+        next_lane_words(w, x);
         const int s = p.out_shift;
-        const bool next_ok = (lane < kWave - 1) && ((gb + lane + 1) * kVec + s <= p.n);
-        const bool prev_ok = (lane > 0) && (e0 + s <= p.n);
-        store_bf16_vec(p.out, e0, s, w, true, kVec, next_ok, prev_ok);
+        bool next_ok = (lane < kWave - 1) && ((gb + lane + 1) * kVec + s <= p.n);
+        bool prev_ok = (lane > 0) && (e0 + s <= p.n);
+        if (edges) {
+            __shared__ uint4 first_words[kWavesPerBlock];
+            if (lane == 0) first_words[wave] = make_uint4(w[0], w[1], w[2], w[3]);
+            lds_barrier();
+            if (lane == kWave - 1 && wave < kWavesPerBlock - 1) {
+                const uint4 y = first_words[wave + 1];
+                x[0] = y.x; x[1] = y.y; x[2] = y.z; x[3] = y.w;
+                next_ok = true;
+            }
+            if (lane == 0 && wave > 0) prev_ok = true;
+        }
+        store_bf16_words(p.out, e0, s, w, x, true, kVec, next_ok, prev_ok);
     }
 }
 
@@ -478,7 +515,11 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     if (gb >= nvec) return;
     if constexpr (F != 0) {
         if (gb + kWave <= p.n / kVec) {
-            step_whole_group<F, OUT, BLK>(p, gb, lane);
+            // The edge exchange needs all four waves of the work-group here (a barrier): the
+            // condition is the same for all of them.
+            const int64_t tile_end = (gb / (kWave * kWavesPerBlock) + 1) * (kWave * kWavesPerBlock);
+            const bool edges = OUT && p.out_shift != 0 && tile_end <= p.n / kVec;
+            step_whole_group<F, OUT, BLK>(p, gb, lane, wave, edges);
             return;
         }
     }
@@ -980,12 +1021,14 @@ __global__ __launch_bounds__(kBlock) void state_pack_kernel(StatePackParams p) {
 // Host-side launch helpers.
 
 // Work-groups per CU of the reduction kernels (see occupancy_lds): the fp32 accumulation is 4-10 %
-// faster with 2 per CU; the plain reduction of a single contribution wants 4 per CU (2 cost it a
-// quarter); the reduction fused with the sum of squares wants 2 per CU, 3 for a single
+// faster with 2 per CU, except from a single contribution, which does 3 % better with 4; the
+// plain reduction of a single contribution is fastest uncapped (4 % ahead of 4 per CU; 2 cost it
+// a quarter); the reduction fused with the sum of squares wants 2 per CU, 3 for a single
 // contribution and 1 where its loads are software-pipelined (reduce_sq_pipelined); the sum of
 // squares and unflatten are fastest uncapped.
 constexpr int kReduceGroupsPerCU = 2;
-constexpr int kReduceOneStreamGroupsPerCU = 4;
+constexpr int kReduceOneStreamGroupsPerCU = 0;
+constexpr int kAccumulateOneStreamGroupsPerCU = 4;
 constexpr int kReduceSqGroupsPerCU = 2;
 constexpr int kReduceOneStreamSqGroupsPerCU = 3;
 constexpr int kReduceSqPipelinedGroupsPerCU = 1;
@@ -1153,8 +1196,10 @@ int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, fl
     unsigned blocks = 0;
     rc = tile_grid(n, groups, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    return launch(k, blocks, &p, stream,
-                  fan_in == 1 && !accumulate ? kReduceOneStreamGroupsPerCU : kReduceGroupsPerCU);
+    const int per_cu = fan_in != 1  ? kReduceGroupsPerCU
+                       : accumulate ? kAccumulateOneStreamGroupsPerCU
+                                    : kReduceOneStreamGroupsPerCU;
+    return launch(k, blocks, &p, stream, per_cu);
 }
 
 int64_t sumsq_partials(int64_t n) {

@@ -7,8 +7,8 @@
  * fsdpshard_stream_rw measures pure reads, pure writes and fixed read : write byte ratios.
  * fsdpshard_stream_mix replays the step's exact access pattern with trivial arithmetic, which
  * separates what the memory system allows for that pattern from what the kernel's code costs;
- * fsdpshard_stream_mix_phased moves the same bytes with each work-group's reads and writes in
- * separate phases.
+ * fsdpshard_stream_mix_shaped moves the same bytes in other launch shapes, optionally with each
+ * work-group's reads and writes in separate phases.
  *
  * The step's bytes per parameter follow the 2 + 2 + 4 + 8 accounting of "FSDP: Fully Sharded
  * Data Parallel Training at Scale" (memory-breakdown passage): at fan-in F it reads 2F + 12 and
@@ -35,24 +35,32 @@ extern "C" {
 int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /*
- * fsdpshard_stream_rw -- n_src read streams and n_dst write streams, each `bytes` long.
+ * fsdpshard_stream_rw -- n_src read streams and n_dst write streams, each `bytes` long, in a
+ * chosen launch shape.
  *   Every 16-byte vector of every source is read once (non-temporal); destination vector i of
  *   stream w receives the XOR of the sources' vectors i mixed with i and w (non-temporal).  With
  *   n_dst == 0 nothing is written except, for a vector whose XOR equals a fixed constant (almost
- *   never), that value to *sink, so the loads cannot be optimised away.  Work-groups of 256
- *   threads each cover 16 KiB of every stream in address order (no XCD remapping).
- *   src      host array of n_src device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS), 16-byte aligned
- *   dst      host array of n_dst device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS), 16-byte
- *            aligned; no destination may overlap another stream; n_src + n_dst >= 1
- *   bytes    >= 0, a multiple of 16
- *   per_cu   resident work-groups per CU (0: as many as the registers allow)
- *   sink     device, one uint32 (4-byte aligned); required when n_dst == 0, else may be NULL
+ *   never), that value to *sink, so the loads cannot be optimised away.
+ *   src                host array of n_src device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS),
+ *                      16-byte aligned
+ *   dst                host array of n_dst device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS),
+ *                      16-byte aligned; no destination may overlap another stream;
+ *                      n_src + n_dst >= 1
+ *   bytes              >= 0, a multiple of 16
+ *   vectors_per_thread 1, 2, 4 or 8 (others: UNSUPPORTED); a thread's vectors are a work-group
+ *                      width apart
+ *   threads_per_group  256, 512 or 1024 (others: UNSUPPORTED)
+ *   per_cu             resident work-groups per CU (0: as many as the registers allow)
+ *   xcd_run            0 or 1: work-group b takes tile b; r > 1: each XCD streams runs of r
+ *                      consecutive tiles (the tile map of the step kernels)
+ *   sink               device, one uint32 (4-byte aligned); required when n_dst == 0
  * Pure reads (n_dst 0), pure writes (n_src 0), a copy (1, 1) and the fused step's 2 : 1 read :
  * write byte ratio at fan-in 8 (2, 1).
- * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, OVERFLOW, HIP).
+ * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, UNSUPPORTED, OVERFLOW, HIP).
  */
 int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* const* dst, int32_t n_dst,
-                        int64_t bytes, int32_t per_cu, uint32_t* sink, void* stream);
+                        int64_t bytes, int32_t vectors_per_thread, int32_t threads_per_group,
+                        int32_t per_cu, int32_t xcd_run, uint32_t* sink, void* stream);
 
 /*
  * fsdpshard_stream_mix -- the fused step's memory traffic without its arithmetic: for every
@@ -77,21 +85,23 @@ int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in
                                  uint16_t* out, int64_t n, void* stream);
 
 /*
- * fsdpshard_stream_mix_phased -- the bytes of fsdpshard_stream_mix_blocked, ordered in phases:
- * each wavefront owns `groups_per_wave` consecutive 512-element groups and loads all of them
- * (state, then contributions), the work-group of 4 wavefronts meets at a barrier once every
- * wavefront holds its data, and only then are the state and out vectors stored.  With
- * per_cu == 1 each CU alternates between a read phase of 4 * groups_per_wave groups and a write
- * phase of the same groups.
+ * fsdpshard_stream_mix_shaped -- the bytes of fsdpshard_stream_mix_blocked in another launch
+ * shape: each wavefront owns `groups_per_wave` consecutive 512-element groups and issues every
+ * load of them (state, then contributions) before any store.  With phased == 1 the work-group
+ * of 4 wavefronts also meets at a barrier once every wavefront holds its data, so no store of
+ * the work-group precedes its last load; with per_cu == 1 each CU then alternates between a
+ * read phase of 4 * groups_per_wave groups and a write phase of the same groups.
  *   contribs, fan_in   fan_in 1, 4 or 8 (others: UNSUPPORTED); state, out, n as
  *                      fsdpshard_stream_mix_blocked
  *   groups_per_wave    1, 2 or 4 (others: UNSUPPORTED)
  *   per_cu             resident work-groups per CU (0: as many as the registers allow)
+ *   xcd_run            as in fsdpshard_stream_rw
+ *   phased             0 or 1
  * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, UNSUPPORTED, OVERFLOW, HIP).
  */
-int fsdpshard_stream_mix_phased(const uint16_t* const* contribs, int32_t fan_in, float* state,
+int fsdpshard_stream_mix_shaped(const uint16_t* const* contribs, int32_t fan_in, float* state,
                                 uint16_t* out, int64_t n, int32_t groups_per_wave, int32_t per_cu,
-                                void* stream);
+                                int32_t xcd_run, int32_t phased, void* stream);
 
 #ifdef __cplusplus
 }

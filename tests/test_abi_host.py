@@ -256,25 +256,33 @@ def test_calibration_call_validation():
     vp = ctypes.c_void_p
     src = (vp * 2)(_Fake.at(1), _Fake.at(2))
     dst = (vp * 1)(_Fake.at(3))
-    rw = lib.fsdpshard_stream_rw
-    assert rw(src, 2, dst, 1, 0, 0, None, None) == OK
-    assert rw(src, 0, dst, 0, 16, 0, None, None) == INVALID          # no stream at all
-    assert rw(src, 1, dst, 0, 16, 0, None, None) == INVALID          # pure reads need a sink
-    assert rw(src, 9, dst, 1, 16, 0, None, None) == INVALID          # more than 8 streams
-    assert rw(src, 2, dst, 1, 8, 0, None, None) == INVALID           # not whole vectors
-    assert rw(src, 2, dst, 1, 16, -1, None, None) == INVALID
-    assert rw((vp * 1)(_Fake.at(1, 8)), 1, dst, 1, 16, 0, None, None) == ALIGN
-    assert rw(src, 2, (vp * 1)(_Fake.at(1, 16)), 1, 64, 0, None, None) == INVALID   # overlap
-    assert rw(src, 1, dst, 0, 16, 0, _Fake.at(4, 2), None) == ALIGN   # sink not 4-byte aligned
-    ph = lib.fsdpshard_stream_mix_phased
+    rw = lambda s_, ns, d_, nd, b, pc=0, sink=None, v=4, t=256, run=0: lib.fsdpshard_stream_rw(
+        s_, ns, d_, nd, b, v, t, pc, run, sink, None)
+    assert rw(src, 2, dst, 1, 0) == OK
+    assert rw(src, 0, dst, 0, 16) == INVALID                        # no stream at all
+    assert rw(src, 1, dst, 0, 16) == INVALID                        # pure reads need a sink
+    assert rw(src, 9, dst, 1, 16) == INVALID                        # more than 8 streams
+    assert rw(src, 2, dst, 1, 8) == INVALID                         # not whole vectors
+    assert rw(src, 2, dst, 1, 16, pc=-1) == INVALID
+    assert rw(src, 2, dst, 1, 16, run=-1) == INVALID
+    assert rw(src, 2, dst, 1, 16, v=3) == UNSUP                     # 1, 2, 4 or 8 vectors
+    assert rw(src, 2, dst, 1, 16, t=128) == UNSUP                   # 256, 512 or 1024 threads
+    assert rw((vp * 1)(_Fake.at(1, 8)), 1, dst, 1, 16) == ALIGN
+    assert rw(src, 2, (vp * 1)(_Fake.at(1, 16)), 1, 64) == INVALID   # overlap
+    assert rw(src, 1, dst, 0, 16, sink=_Fake.at(4, 2)) == ALIGN      # sink not 4-byte aligned
+    ph = lambda fi, o, n, g=4, pc=1, run=32, phased=1: lib.fsdpshard_stream_mix_shaped(
+        g8, fi, st, o, n, g, pc, run, phased, None)
     g8 = (vp * 8)(*[_Fake.at(10 + r) for r in range(8)])
     st, out = _Fake.at(20), _Fake.at(21)
-    assert ph(g8, 8, st, out, 0, 4, 1, None) == OK
-    assert ph(g8, 2, st, out, 0, 4, 1, None) == UNSUP                # fan-in 1, 4, 8 only
-    assert ph(g8, 8, st, out, 0, 3, 1, None) == UNSUP                # 1, 2 or 4 groups per wave
-    assert ph(g8, 8, st, out, 12, 4, 1, None) == INVALID             # whole vectors only
-    assert ph(g8, 8, st, out, 0, 4, -1, None) == INVALID
-    assert ph(g8, 8, st, _Fake.at(20, 64), 64, 4, 1, None) == INVALID   # out inside the state
+    assert ph(8, out, 0) == OK
+    assert ph(8, out, 0, phased=0) == OK
+    assert ph(2, out, 0) == UNSUP                                   # fan-in 1, 4, 8 only
+    assert ph(8, out, 0, g=3) == UNSUP                              # 1, 2 or 4 groups per wave
+    assert ph(8, out, 12) == INVALID                                # whole vectors only
+    assert ph(8, out, 0, pc=-1) == INVALID
+    assert ph(8, out, 0, run=-1) == INVALID
+    assert ph(8, out, 0, phased=2) == INVALID
+    assert ph(8, _Fake.at(20, 64), 64) == INVALID                   # out inside the state
 
 
 def test_segment_dtype_matches_struct():

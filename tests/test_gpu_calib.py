@@ -25,17 +25,20 @@ def _index_pattern(nvec):
 
 
 @pytest.mark.parametrize("n_src,n_dst", [(1, 1), (2, 1), (0, 2), (3, 2)])
-@pytest.mark.parametrize("per_cu", [0, 2])
-def test_stream_rw_writes_what_it_reads(n_src, n_dst, per_cu):
-    nvec = 1024 * 7 + 333                       # 8 work-groups, the last one partial
+@pytest.mark.parametrize("vpt,threads,per_cu,run", [(4, 256, 0, 0), (1, 1024, 2, 1), (2, 512, 0, 4),
+                                                    (8, 256, 1, 2)])
+def test_stream_rw_writes_what_it_reads(n_src, n_dst, vpt, threads, per_cu, run):
+    nvec = 8192 * 11 + 333                      # many work-groups, the last one partial
     nbytes = nvec * 16
     rng = np.random.default_rng(n_src * 10 + n_dst)
     srcs = [rng.integers(0, 2 ** 32, (nvec, 4), dtype=np.uint32) for _ in range(n_src)]
     dsts = [np.full((nvec + GUARD, 4), 0xA5A5A5A5, dtype=np.uint32) for _ in range(n_dst)]
     sd = [_dev_u32(s) for s in srcs]
     dd = [_dev_u32(d) for d in dsts]
-    say(f"stream_rw {n_src} read, {n_dst} write streams, {nvec} vectors, per_cu {per_cu}")
-    F.stream_rw(sd, dd, nbytes, per_cu=per_cu)
+    say(f"stream_rw {n_src} read, {n_dst} write streams, {nvec} vectors, shape "
+        f"{vpt}/{threads}/{per_cu}/{run}")
+    F.stream_rw(sd, dd, nbytes, vectors_per_thread=vpt, threads_per_group=threads, per_cu=per_cu,
+                xcd_run=run)
     torch.cuda.synchronize()
     want = _index_pattern(nvec)
     for s in srcs:
@@ -59,16 +62,16 @@ def test_stream_rw_pure_reads_leave_the_sink():
     assert int(sink.item()) == 7
 
 
-def _mix_expected(contribs, state, n, phased):
+def _mix_expected(contribs, state, n, shaped):
     """What the replicas write: per 8-element vector, x = XOR of the contributions' words (and,
-    phased, of every state word but each array's first); the state's first word of each array
-    XOR x; out = (master[1], m[1], v[1], x) of the vector."""
+    for the shaped replica, of every state word but each array's first); the state's first word
+    of each array XOR x; out = (master[1], m[1], v[1], x) of the vector."""
     nvec = n // 8
     x = np.zeros(nvec, dtype=np.uint32)
     for c in contribs:
         x ^= np.bitwise_xor.reduce(c.view(np.uint32).reshape(nvec, 4), axis=1)
     sep = [a.view(np.uint32).reshape(nvec, 8).copy() for a in BL.from_blocked(state, n)]
-    if phased:
+    if shaped:
         for a in sep:
             x ^= np.bitwise_xor.reduce(a[:, 1:], axis=1)
     out = np.stack([sep[0][:, 1], sep[1][:, 1], sep[2][:, 1], x], axis=1)
@@ -78,9 +81,10 @@ def _mix_expected(contribs, state, n, phased):
 
 
 @pytest.mark.parametrize("fan_in", [1, 8])
-@pytest.mark.parametrize("groups,per_cu", [(0, 0), (1, 2), (2, 1), (4, 1)])
-def test_mix_replicas_move_the_steps_bytes(fan_in, groups, per_cu):
-    n = 8 * (64 * 4 * 4 * 5 + 97)                # 5 whole tiles of 16 groups plus a ragged tail
+@pytest.mark.parametrize("groups,per_cu,run,phased", [(0, 0, 0, 0), (1, 2, 32, 1), (2, 1, 2, 1),
+                                                      (4, 1, 1, 1), (1, 1, 16, 0), (2, 2, 4, 0)])
+def test_mix_replicas_move_the_steps_bytes(fan_in, groups, per_cu, run, phased):
+    n = 8 * (64 * 4 * 4 * 21 + 97)               # 21 whole tiles of 16 groups plus a ragged tail
     rng = np.random.default_rng(fan_in + groups)
     contribs = [rng.integers(0, 2 ** 16, n, dtype=np.uint16) for _ in range(fan_in)]
     sep = [rng.standard_normal(n).astype(np.float32) for _ in range(3)]
@@ -89,13 +93,14 @@ def test_mix_replicas_move_the_steps_bytes(fan_in, groups, per_cu):
     st = torch.from_numpy(np.concatenate([state, np.full(GUARD, unused, np.float32)])).cuda()
     out = torch.full((2 * n // 2 + GUARD,), 0x5A5A, dtype=torch.int16, device="cuda")
     cd = [torch.from_numpy(c.view(np.int16)).cuda() for c in contribs]
-    say(f"mix replica fan-in {fan_in} groups {groups} per_cu {per_cu} n={n}")
+    say(f"mix replica fan-in {fan_in} groups {groups} per_cu {per_cu} run {run} phased {phased} "
+        f"n={n}")
     if groups == 0:
         F.stream_mix_blocked(cd, st, out, n)
     else:
-        F.stream_mix_phased(cd, st, out, n, groups, per_cu)
+        F.stream_mix_shaped(cd, st, out, n, groups, per_cu, run, phased)
     torch.cuda.synchronize()
-    want_sep, want_out = _mix_expected(contribs, state, n, phased=groups > 0)
+    want_sep, want_out = _mix_expected(contribs, state, n, shaped=groups > 0)
     got = st.cpu().numpy()
     for k, (g, w) in enumerate(zip(BL.from_blocked(got[:state.size], n), want_sep)):
         assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), f"state array {k}"
