@@ -524,7 +524,7 @@ def measure_workload(F, W, torch, name, blocked, args, dev, stream, mix=True):
 # MI355X.
 CEILING_SHAPES = {
     "read": [(1, 1024, 0, 1), (4, 1024, 0, 32), (2, 512, 0, 32)],
-    "write": [(2, 256, 2, 256), (1, 256, 4, 1), (8, 256, 1, 32)],
+    "write": [(2, 256, 2, 256), (1, 256, 4, 1), (2, 256, 2, 32)],
     "copy": [(2, 256, 0, 256), (1, 256, 0, 1), (2, 1024, 0, 32)],
     "read2_write1": [(1, 256, 0, 256), (2, 512, 0, 32), (1, 256, 0, 32)],
 }

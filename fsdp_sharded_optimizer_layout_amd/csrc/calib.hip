@@ -341,7 +341,6 @@ extern "C" int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* 
     const void* k = vectors_per_thread == 1   ? reinterpret_cast<const void*>(&stream_rw_kernel<1>)
                     : vectors_per_thread == 2 ? reinterpret_cast<const void*>(&stream_rw_kernel<2>)
                     : vectors_per_thread == 4 ? reinterpret_cast<const void*>(&stream_rw_kernel<4>)
-                    : vectors_per_thread == 8 ? reinterpret_cast<const void*>(&stream_rw_kernel<8>)
                                               : nullptr;
     if (k == nullptr || (threads_per_group != 256 && threads_per_group != 512 &&
                          threads_per_group != 1024))

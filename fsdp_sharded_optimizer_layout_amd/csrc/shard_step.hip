@@ -65,6 +65,8 @@ struct StepParams {
     int32_t n_segs;
     int32_t fan_in;
     int32_t out_shift;       // first slice element whose destination is 16-byte aligned (0..7)
+    int32_t out_line_vecs;   // with out_shift: element 8 * out_line_vecs + out_shift is the first
+                             // whose destination starts a 64-byte line (0..3)
     float b1, b2, c1, c2, bc1, bc2, eps, lr, dec, scale;
 };
 
@@ -281,6 +283,77 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The aligned 16-byte vector made of x's elements s..7 followed by y's elements 0..s-1.
+__device__ __forceinline__ uint4 rephase_rt(const uint32_t (&x)[4], const uint32_t (&y)[4], int s) {
+    switch (s) {
+        case 0: return make_uint4(x[0], x[1], x[2], x[3]);
+        case 1: return rephase<1>(x, y);
+        case 2: return rephase<2>(x, y);
+        case 3: return rephase<3>(x, y);
+        case 4: return rephase<4>(x, y);
+        case 5: return rephase<5>(x, y);
+        case 6: return rephase<6>(x, y);
+        default: return rephase<7>(x, y);
+    }
+}
+
+// bf16 stores of one whole 512-element group whose destination does not start a 64-byte line.
+// S = 8q + s (q = out_line_vecs, s = out_shift) is the first slice element whose destination
+// does.  U_i is the aligned 16-byte destination vector of group elements 8i + s .. 8i + s + 7
+// (lane i's elements s..7, lane i + 1's elements 0..s-1).  Lane j stores U_{j+q}, so a wave
+// writes the 16 whole 64-byte lines that begin at its group element S, and no line inside a
+// work-group has two writing waves.  U_63 (when s != 0) and U_64..U_{63+q} hold the next
+// wave's first elements; with the exchange (`exch`: the work-group's four groups are whole)
+// their words come from the next wave's lanes 0..q through LDS, and the previous wave likewise
+// stores this wave's U_0..U_{q-1} and elements 0..s-1.  A wave without an exchanging neighbour
+// on a side stores that side itself: U_0..U_{q-1} from lanes 0..q-1, and 2-byte stores for
+// what none of its aligned vectors covers.  Group element e goes to out[8 * gb + e].
+__device__ __forceinline__ void store_bf16_lines(uint16_t* out, int s, int q, int64_t gb, int lane,
+                                                 int wave, bool exch, const uint32_t (&w)[4]) {
+    __shared__ uint4 head_words[kWavesPerBlock][4];
+    const bool prev_ex = exch && wave > 0;
+    const bool next_ex = exch && wave < kWavesPerBlock - 1;
+    const int a = lane + q;                    // this lane stores U_a
+    uint32_t x[4], y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {              // every lane takes part in the permutes
+        x[k] = __shfl(w[k], a & (kWave - 1), kWave);
+        y[k] = __shfl(w[k], (a + 1) & (kWave - 1), kWave);
+    }
+    if (exch) {
+        if (lane <= q) head_words[wave][lane] = make_uint4(w[0], w[1], w[2], w[3]);
+        lds_barrier();
+        if (next_ex && a >= kWave) {
+            const uint4 t = head_words[wave + 1][a - kWave];
+            x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+        }
+        if (next_ex && a + 1 >= kWave) {
+            const uint4 t = head_words[wave + 1][a + 1 - kWave];
+            y[0] = t.x; y[1] = t.y; y[2] = t.z; y[3] = t.w;
+        }
+    }
+    const bool own = a + 1 < kWave || (a + 1 == kWave && s == 0);   // U_a from this wave alone
+    if (own || next_ex) st_u4_nt(out + (gb + a) * kVec + s, rephase_rt(x, y, s));
+    if (!prev_ex) {
+        if (q > 0) {                           // wave-uniform: lanes 0..q-1 store U_0..U_{q-1}
+            uint32_t z[4];
+            next_lane_words(w, z);
+            if (lane < q) st_u4_nt(out + (gb + lane) * kVec + s, rephase_rt(w, z, s));
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e)
+                if (e < s) out[gb * kVec + e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+    if (!next_ex && lane == kWave - 1 && s != 0) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+            if (e >= s)
+                out[(gb + lane) * kVec + e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // The fused step.
 
@@ -438,11 +511,10 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
 // A wave's complete group (compile-time gradient source F >= 1 or F == -1): every HBM load of
 // the group is issued first (gradients non-temporal), then the segment cursor is placed, then
 // the group is reduced, updated and stored.
-// With `edges` (an off-phase destination and a work-group whose four groups are all whole),
-// the group edges between the work-group's waves are stored whole: each wave's first lane
-// publishes its packed words in LDS, and after a barrier the previous wave's last lane builds
-// the aligned 16-byte vector that spans the edge, as every other lane does from its right
-// neighbour.  Only the work-group's own first and last edges are left to 2-byte stores.
+// With `edges` (a destination that does not start a 64-byte line, and a work-group whose four
+// groups are all whole) the waves of the work-group exchange their first lanes' bf16 words
+// through LDS so that every 64-byte line of bf16 output inside the work-group is written by one
+// wave in whole 16-byte vectors (store_bf16_lines).
 template <int F, bool OUT, bool BLK>
 __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb, int lane,
                                                  int wave, bool edges) {
@@ -481,24 +553,12 @@ __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb
     store8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
     store8(state_ptr<BLK>(p, 2, e0), true, kVec, vv);
     if constexpr (OUT) {
-        uint32_t w[4], x[4];
+        uint32_t w[4];
         pack_out(fl, th, w);
-        next_lane_words(w, x);
-        const int s = p.out_shift;
-        bool next_ok = (lane < kWave - 1) && ((gb + lane + 1) * kVec + s <= p.n);
-        bool prev_ok = (lane > 0) && (e0 + s <= p.n);
-        if (edges) {
-            __shared__ uint4 first_words[kWavesPerBlock];
-            if (lane == 0) first_words[wave] = make_uint4(w[0], w[1], w[2], w[3]);
-            lds_barrier();
-            if (lane == kWave - 1 && wave < kWavesPerBlock - 1) {
-                const uint4 y = first_words[wave + 1];
-                x[0] = y.x; x[1] = y.y; x[2] = y.z; x[3] = y.w;
-                next_ok = true;
-            }
-            if (lane == 0 && wave > 0) prev_ok = true;
-        }
-        store_bf16_words(p.out, e0, s, w, x, true, kVec, next_ok, prev_ok);
+        if (p.out_shift == 0 && p.out_line_vecs == 0)
+            st_u4_nt(p.out + e0, make_uint4(w[0], w[1], w[2], w[3]));
+        else
+            store_bf16_lines(p.out, p.out_shift, p.out_line_vecs, gb, lane, wave, edges, w);
     }
 }
 
@@ -518,7 +578,8 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
             // The edge exchange needs all four waves of the work-group here (a barrier): the
             // condition is the same for all of them.
             const int64_t tile_end = (gb / (kWave * kWavesPerBlock) + 1) * (kWave * kWavesPerBlock);
-            const bool edges = OUT && p.out_shift != 0 && tile_end <= p.n / kVec;
+            const bool edges =
+                OUT && (p.out_shift != 0 || p.out_line_vecs != 0) && tile_end <= p.n / kVec;
             step_whole_group<F, OUT, BLK>(p, gb, lane, wave, edges);
             return;
         }
@@ -1058,6 +1119,13 @@ int out_shift_of(const uint16_t* out) {
     return static_cast<int>((kVec - phase) % kVec);
 }
 
+// First slice element whose bf16 destination starts a 64-byte line (0..31; out_shift_of(out)
+// is this value mod 8).
+int out_line_shift_of(const uint16_t* out) {
+    const unsigned off = static_cast<unsigned>(reinterpret_cast<uintptr_t>(out) & 63u);
+    return static_cast<int>(((64u - off) & 63u) / 2u);
+}
+
 bool is_finite(double x) { return std::isfinite(x); }
 
 // Bytes of a device segment table.
@@ -1138,6 +1206,7 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     p.n_segs = segs == nullptr ? 0 : n_segments;
     p.fan_in = fan_in;
     p.out_shift = out == nullptr ? 0 : out_shift_of(out);
+    p.out_line_vecs = out == nullptr ? 0 : out_line_shift_of(out) / kVec;
     const double t = static_cast<double>(hp->step);
     p.b1 = static_cast<float>(hp->beta1);
     p.b2 = static_cast<float>(hp->beta2);

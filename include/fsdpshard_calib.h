@@ -47,7 +47,7 @@ int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* strea
  *                      16-byte aligned; no destination may overlap another stream;
  *                      n_src + n_dst >= 1
  *   bytes              >= 0, a multiple of 16
- *   vectors_per_thread 1, 2, 4 or 8 (others: UNSUPPORTED); a thread's vectors are a work-group
+ *   vectors_per_thread 1, 2 or 4 (others: UNSUPPORTED); a thread's vectors are a work-group
  *                      width apart
  *   threads_per_group  256, 512 or 1024 (others: UNSUPPORTED)
  *   per_cu             resident work-groups per CU (0: as many as the registers allow)

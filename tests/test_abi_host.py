@@ -265,7 +265,8 @@ def test_calibration_call_validation():
     assert rw(src, 2, dst, 1, 8) == INVALID                         # not whole vectors
     assert rw(src, 2, dst, 1, 16, pc=-1) == INVALID
     assert rw(src, 2, dst, 1, 16, run=-1) == INVALID
-    assert rw(src, 2, dst, 1, 16, v=3) == UNSUP                     # 1, 2, 4 or 8 vectors
+    assert rw(src, 2, dst, 1, 16, v=3) == UNSUP                     # 1, 2 or 4 vectors
+    assert rw(src, 2, dst, 1, 16, v=8) == UNSUP
     assert rw(src, 2, dst, 1, 16, t=128) == UNSUP                   # 256, 512 or 1024 threads
     assert rw((vp * 1)(_Fake.at(1, 8)), 1, dst, 1, 16) == ALIGN
     assert rw(src, 2, (vp * 1)(_Fake.at(1, 16)), 1, 64) == INVALID   # overlap

@@ -26,7 +26,7 @@ def _index_pattern(nvec):
 
 @pytest.mark.parametrize("n_src,n_dst", [(1, 1), (2, 1), (0, 2), (3, 2)])
 @pytest.mark.parametrize("vpt,threads,per_cu,run", [(4, 256, 0, 0), (1, 1024, 2, 1), (2, 512, 0, 4),
-                                                    (8, 256, 1, 2)])
+                                                    (4, 256, 1, 2)])
 def test_stream_rw_writes_what_it_reads(n_src, n_dst, vpt, threads, per_cu, run):
     nvec = 8192 * 11 + 333                      # many work-groups, the last one partial
     nbytes = nvec * 16

@@ -89,9 +89,12 @@ def test_step_sizes_and_fanins(i):
     run_case(n=n, F_in=FANS[i % len(FANS)], d=(3 * i) % 8, steps=2, seed=i)
 
 
-@pytest.mark.parametrize("d", range(8))
+@pytest.mark.parametrize("d", range(32))
 @pytest.mark.parametrize("F_in", [1, 8, 3])
 def test_every_output_phase(d, F_in):
+    # d elements between the 128-byte aligned guard and the window: every phase of the slice
+    # start against a 16-byte vector and a 64-byte line; 6151 elements are three whole
+    # work-groups (the bf16 edge exchange) and a tail
     run_case(n=6151, F_in=F_in, d=d, steps=2, seed=40 + d)
 
 

@@ -48,7 +48,7 @@ def _draw(rng):
               weight_decay=rng.choice([0.0, 0.01, 0.1]),
               grad_scale=rng.choice([1.0, 0.5, 0.125]))
     return dict(sizes=sizes, pad=pad, N=N, k=k, wd=wd, F_in=rng.choice(FAN_CHOICES), hp=hp,
-                clip=rng.choice([0.0, 0.0, 1e-3, 10.0]), d=rng.randrange(8))
+                clip=rng.choice([0.0, 0.0, 1e-3, 10.0]), d=rng.randrange(32))
 
 
 def _same_scale(sumsq, clip, base, oracle_scale):
