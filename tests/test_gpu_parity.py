@@ -98,6 +98,15 @@ def test_every_output_phase(d, F_in):
     run_case(n=6151, F_in=F_in, d=d, steps=2, seed=40 + d)
 
 
+@pytest.mark.parametrize("d", range(32))
+@pytest.mark.parametrize("F_in", [1, 8])
+def test_every_output_phase_with_a_partial_last_work_group(d, F_in):
+    # 5157 elements: two whole work-groups (which exchange bf16 edge words through LDS), then a
+    # work-group whose first two groups are whole and whose third holds the slice's last 37
+    # elements, so its whole groups store their edges without the exchange
+    run_case(n=5157, F_in=F_in, d=d, steps=2, seed=90 + d)
+
+
 @pytest.mark.parametrize("F_in", [1, 3, 8])
 def test_many_groups_and_edges(F_in):
     # hundreds of work-groups (the XCD tile map's whole blocks and identity tail), a ragged last
