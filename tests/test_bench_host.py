@@ -43,3 +43,22 @@ def test_counter_traffic_is_reported_only_for_the_measured_code(tmp_path, monkey
     assert bench.counter_traffic("other", str(src)) is None
     src.write_text("int f() { return 2; }\n")
     assert bench.counter_traffic("w", str(src)) is None
+
+
+def test_host_cores_are_stated():
+    c = bench.host_cores()
+    assert c["os_cpu_count"] >= 1 and c["affinity"] >= 1
+    assert 1 <= c["usable"] <= c["affinity"]
+    if c["cgroup_quota"] is not None:
+        assert c["usable"] <= c["cgroup_quota"]
+
+
+def test_cpu_baseline_legs_report_the_contract_fields():
+    # Tiny samples: the legs' structure, not their speed.
+    one = bench.cpu_baseline_single("p1000003_n8_rank3", seconds=0.2, sample=4096)
+    assert one["kind"] == "oracle" and one["cores"] == 1 and one["unit"] == "params/s"
+    assert one["value"] > 0 and "4096 elements" in one["sample"]
+    par = bench.cpu_baseline("p1000003_n8_rank3", 2, seconds=0.2, chunk=8192)
+    assert par["kind"] == "oracle" and par["cores"] == 2 and par["value"] > 0
+    assert set(par["host"]) == {"os_cpu_count", "affinity", "cgroup_quota", "usable"}
+    assert "2 processes" in par["sample"]
