@@ -162,8 +162,9 @@ def test_clipped_fp32_path_full_size(name):
     """Clipping through an fp32 shard at full size, as the benchmark's clipped32 path runs it:
     reduce_shard_sumsq, then the clipped fp32-gradient step on the blocked state.  The fp32 shard
     is compared bit for bit with the oracle's reduction on the sampled windows; the fused float64
-    sum and grad_sumsq_shard's sum over the same shard (too long for the oracle's exact sum) with
-    a float64 sum of that shard taken on the host; the step on the windows with the oracle, whose
+    sum, grad_sumsq_shard's sum over the same shard and grad_sumsq_shard's sum from the bf16
+    contributions (too long for the oracle's exact sum) with a float64 sum of that shard taken on
+    the host; the step on the windows with the oracle, whose
     clipping coefficient comes from the host's sum."""
     w = W.WORKLOADS[name]
     L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
@@ -190,6 +191,9 @@ def test_clipped_fp32_path_full_size(name):
     sq = torch.zeros(1, dtype=torch.float64, device="cuda")
     scale = 0.5
     F.reduce_shard_sumsq(grads, g32, sq, scale=scale, segs=segs_dev, n_segments=L.n_segments)
+    sq_bf16 = torch.zeros(1, dtype=torch.float64, device="cuda")     # from the contributions
+    F.grad_sumsq_shard(sq_bf16, contribs=grads, n=n, scale=scale, segs=segs_dev,
+                       n_segments=L.n_segments)
     contribs = [g[idx_t].cpu().numpy().view(np.uint16) for g in grads]
     del grads
     torch.cuda.synchronize()
@@ -203,7 +207,8 @@ def test_clipped_fp32_path_full_size(name):
     sq2 = torch.zeros(1, dtype=torch.float64, device="cuda")
     F.grad_sumsq_shard(sq2, grad=g32, n=n, segs=segs_dev, n_segments=L.n_segments)
     assert abs(float(sq2.item()) - host) <= 1e-12 * host
-    say(f"  fp32 shard and sum ok (sum {fused:.6e}, host {host:.6e})")
+    assert abs(float(sq_bf16.item()) - host) <= 1e-12 * host
+    say(f"  fp32 shard and sums ok (sum {fused:.6e}, host {host:.6e})")
 
     max_norm = 0.5 * math.sqrt(host)                    # clipping on: coefficient about 1/2
     phase = lo % 8
