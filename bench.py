@@ -227,7 +227,7 @@ def cpu_baseline_single(workload, seconds=12.0, sample=1 << 26):
 def _oracle_worker(args):
     workload, a, b, seconds, barrier, results = args
     w, flags, master, m, v, grads, n_real = _oracle_inputs(workload, a, b)
-    barrier.wait()                     # every worker starts stepping at the same moment
+    barrier.wait(timeout=600)          # every worker starts stepping at the same moment
     steps, el = _oracle_steps(w, flags, master, m, v, grads, seconds)
     results.put((n_real * steps, el))
 
@@ -236,7 +236,7 @@ def cpu_baseline(workload, procs, seconds=12.0, chunk=1 << 22):
     """The same oracle in `procs` processes, each stepping its own contiguous 4 Mi-element chunk
     of the slice (valid because the step is elementwise once the layout is fixed).  The workers
     draw their inputs, meet at a barrier, then step for `seconds`; rate = all workers' real
-    parameters x steps / the longest worker's stepping time."""
+    parameters x steps / the longest worker's stepping time.  None if a worker fails."""
     import multiprocessing as mp
 
     import workloads as W
@@ -254,7 +254,13 @@ def cpu_baseline(workload, procs, seconds=12.0, chunk=1 << 22):
                for i in range(procs)]
     for p in workers:
         p.start()
-    done = [results.get() for _ in workers]
+    import queue
+    try:
+        done = [results.get(timeout=seconds + 900) for _ in workers]
+    except queue.Empty:                # a worker died: no parallel figure rather than a hang
+        for p in workers:
+            p.terminate()
+        return None
     for p in workers:
         p.join()
     total = sum(d[0] for d in done)
@@ -705,8 +711,11 @@ def main():
         log(f"cpu oracle, one thread: {cpu_single['value']:.3e} params/s")
         if args.cpu_procs >= 0:
             cpu = cpu_baseline(w.name, procs)
-            log(f"cpu oracle, {cpu['cores']} processes: {cpu['value']:.3e} params/s")
-        else:
+            if cpu is None:
+                log("cpu oracle: a worker process failed; reporting the one-thread figure")
+            else:
+                log(f"cpu oracle, {cpu['cores']} processes: {cpu['value']:.3e} params/s")
+        if cpu is None:
             cpu = cpu_single
 
     value = L.n_real / (ms_per_step / 1e3)
