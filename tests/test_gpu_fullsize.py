@@ -232,3 +232,66 @@ def test_clipped_fp32_path_full_size(name):
     _check(got, oout, f"{name} clipped fp32 bf16", exact)
     del state, g32, flat
     torch.cuda.empty_cache()
+
+
+def test_slice_beyond_2_31_elements():
+    """A slice longer than 2^31 elements (one tensor of 2^31 + 777, fan-in 1, blocked state), so
+    every 32-bit boundary of element, vector and partial indices is crossed: two steps compared
+    bit for bit with the oracle on windows at the start, across 2^31 and at the end; the sum of
+    squares (65,537 partials) against a float64 sum of the inputs taken on the host; the
+    allocation-free sum of squares refuses the length (its array holds 65,536 partials)."""
+    n = (1 << 31) + 777
+    w = W.Workload("beyond_2_31", "one tensor of 2^31 + 777 elements", [n], 1, 1, 0, 1, 2,
+                   1e-3, ("normal", 0.02))
+    L, segs = F.shard_layout(w.sizes, 1, 0)
+    lo_o, hi_o, osegs = OL.segments(w.sizes, 1, None, 1, 0)
+    assert (L.lo, L.n, L.n_segments) == (0, n, 1) and (lo_o, hi_o) == (0, n)
+    say(f"slice beyond 2^31: n={n}")
+    rng = np.random.default_rng(31)
+    spans = [(0, WIN), ((1 << 31) - WIN, (1 << 31) + WIN), (n - WIN, n)]
+    spans += [(int(s), int(s) + WIN) for s in rng.integers(0, n - WIN, 16)]
+    idx = np.unique(np.concatenate([np.arange(a, min(b, n), dtype=np.int64) for a, b in spans]))
+    idx_t = torch.from_numpy(idx).cuda()
+    flags = _flags_at(osegs, idx)
+    segs_dev = F.segments_to_device(segs)
+    master, m, v = W.torch_state(w, n, 3, "cuda")
+    om, omm, ov = (x[idx_t].cpu().numpy() for x in (master, m, v))
+    state = torch.empty(F.state_blocked_elems(n), dtype=torch.float32, device="cuda")
+    F.state_to_blocked(master, m, v, state)
+    torch.cuda.synchronize()
+    del master, m, v
+    torch.cuda.empty_cache()
+    pos = [torch.from_numpy(_blocked_index(idx, k)).cuda() for k in range(3)]
+    grads = [torch.empty(n, dtype=torch.int16, device="cuda")]
+    flat = torch.full((n,), int(SENT16), dtype=torch.int16, device="cuda")
+    for t in (1, 2):
+        W.torch_grads_into(w, grads, t, 3)
+        F.adamw_shard_step_blocked(state, grads, step=t, n=n, segs=segs_dev,
+                                   n_segments=L.n_segments, flat=flat, flat_index0=0, lo=0,
+                                   **w.hp)
+        contribs = [grads[0][idx_t].cpu().numpy().view(np.uint16)]
+        torch.cuda.synchronize()
+        om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, w.hp, t)
+        for k, want, what in ((0, om, "master"), (1, omm, "m"), (2, ov, "v")):
+            _check(state[pos[k]].cpu().numpy(), want, f"beyond 2^31 {what} step {t}")
+        _check(flat[idx_t].cpu().numpy().view(np.uint16), oout, f"beyond 2^31 bf16 step {t}")
+        say(f"  step {t} ok")
+    del state, pos, flat
+    torch.cuda.empty_cache()
+
+    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    assert F.grad_sumsq_workspace_bytes(n) == 8 * 65_537
+    F.grad_sumsq_shard(sq, contribs=grads, n=n, segs=segs_dev, n_segments=L.n_segments)
+    parts = []
+    chunk = 1 << 27
+    for a in range(0, n, chunk):
+        bits = grads[0][a:a + chunk].cpu().numpy().view(np.uint16).astype(np.uint32) << 16
+        x = bits.view(np.float32).astype(np.float64)
+        parts.append(float(np.dot(x, x)))
+    host = math.fsum(parts)
+    assert abs(float(sq.item()) - host) <= 1e-12 * host, (float(sq.item()), host)
+    with pytest.raises(F.FsdpShardError) as e:
+        F.grad_sumsq_shard_noalloc(sq, contribs=grads, n=n)
+    assert e.value.code == 3
+    del grads
+    torch.cuda.empty_cache()
