@@ -302,7 +302,7 @@ int stream_mix_impl(const uint16_t* const* contribs, int32_t fan_in, float* s0, 
                 : (fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_kernel<1, false>)
                    : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_kernel<8, false>)
                                  : reinterpret_cast<const void*>(&stream_mix_kernel<0, false>));
-    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in));   // as the step
+    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in, blocks));   // as the step
 }
 
 }  // namespace

@@ -1081,18 +1081,28 @@ __global__ __launch_bounds__(kBlock) void state_pack_kernel(StatePackParams p) {
 // ------------------------------------------------------------------------------------------------
 // Host-side launch helpers.
 
-// Work-groups per CU of the reduction kernels (see occupancy_lds): the fp32 accumulation is 4-10 %
-// faster with 2 per CU, except from a single contribution, which does 3 % better with 4; the
-// plain reduction of a single contribution is fastest uncapped (4 % ahead of 4 per CU; 2 cost it
-// a quarter); the reduction fused with the sum of squares wants 2 per CU, 3 for a single
-// contribution and 1 where its loads are software-pipelined (reduce_sq_pipelined); the sum of
-// squares and unflatten are fastest uncapped.
-constexpr int kReduceGroupsPerCU = 2;
-constexpr int kReduceOneStreamGroupsPerCU = 0;
-constexpr int kAccumulateOneStreamGroupsPerCU = 4;
+// Work-groups per CU of the reduction kernels (see occupancy_lds).  Measured on one GPU at
+// 2^24..2^29.75 elements against the other caps (0-4), 4 alternating rounds per point:
+//   plain reduction:  fan-in 1 takes 4 (2-6 % ahead of uncapped, 2 costs a third), fan-in 2
+//                     takes 3 (10-12 % ahead of 2); other fan-ins 2 (within 1 % of the best
+//                     at 4, 8 and 16 from 2^26 up; at 3, 3 per CU is 3 % slower at 2^26 and
+//                     3-5 % faster from 2^28);
+//   fp32 accumulation: fan-in 1 takes 2 (4-5 % ahead of 4), fan-in 2 and run-time fan-ins
+//                     above 8 take 3 (2 % and 5 % ahead of 2), others 2;
+// the reduction fused with the sum of squares wants 2 per CU, 3 for a single contribution and 1
+// where its loads are software-pipelined (reduce_sq_pipelined); the sum of squares and
+// unflatten are fastest uncapped; the blocked-state packing takes 2 (14-20 % ahead of
+// uncapped).
+inline int reduce_groups_per_cu(int fan_in, bool accumulate) {
+    if (fan_in == 1) return accumulate ? 2 : 4;
+    if (fan_in == 2 || (accumulate && fan_in > 8)) return 3;
+    return 2;
+}
+
 constexpr int kReduceSqGroupsPerCU = 2;
 constexpr int kReduceOneStreamSqGroupsPerCU = 3;
 constexpr int kReduceSqPipelinedGroupsPerCU = 1;
+constexpr int kStatePackGroupsPerCU = 2;
 
 template <int F, bool BLK>
 const void* step_kernel(bool out) {
@@ -1224,7 +1234,7 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     if (rc != FSDPSHARD_OK) return rc;
     const void* k = blocked ? pick_step_kernel<true>(fan_in, out != nullptr)
                             : pick_step_kernel<false>(fan_in, out != nullptr);
-    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in));
+    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in, blocks));
 }
 
 int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, float scale,
@@ -1265,10 +1275,7 @@ int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, fl
     unsigned blocks = 0;
     rc = tile_grid(n, groups, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    const int per_cu = fan_in != 1  ? kReduceGroupsPerCU
-                       : accumulate ? kAccumulateOneStreamGroupsPerCU
-                                    : kReduceOneStreamGroupsPerCU;
-    return launch(k, blocks, &p, stream, per_cu);
+    return launch(k, blocks, &p, stream, reduce_groups_per_cu(fan_in, accumulate));
 }
 
 int64_t sumsq_partials(int64_t n) {
@@ -1348,7 +1355,7 @@ int launch_state_pack(float* master, float* m, float* v, int64_t n, float* state
     if (rc != FSDPSHARD_OK) return rc;
     return launch(to_blocked ? reinterpret_cast<const void*>(&state_pack_kernel<true>)
                              : reinterpret_cast<const void*>(&state_pack_kernel<false>),
-                  blocks, &p, stream);
+                  blocks, &p, stream, kStatePackGroupsPerCU);
 }
 }  // namespace
 

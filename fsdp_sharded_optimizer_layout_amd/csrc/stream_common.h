@@ -161,12 +161,32 @@ inline int check_contribs(const uint16_t* const* contribs, int32_t fan_in) {
 // concurrent access streams.  The cap is set by reserving LDS that the kernels never touch (a
 // dynamic LDS size at launch), sized from the device's LDS per CU so that exactly `per_cu`
 // work-groups fit: halfway between lds/(per_cu+1) and lds/per_cu, which leaves room for the few
-// bytes of static LDS a kernel declares itself.  Measured on one GPU against the register-limited
-// occupancy: the fused step is 4-10 % faster with 2 per CU at fan-in 1 and 8 and from an fp32
-// gradient; at fan-in 4 the 2,000-tensor slice is 5 % faster with 3 per CU (2 gains nothing
-// there), and at fan-in 2 and 16 both are within 1 %, so other fan-ins take 3.
-constexpr int step_groups_per_cu(int fan_in) {
-    return fan_in == 1 || fan_in == 8 || fan_in == -1 ? 2 : 3;
+// bytes of static LDS a kernel declares itself.
+//
+// The fused step takes 2 or 3 per CU by its gradient source and the size of the launch.  With
+// few gradient streams a third work-group per CU keeps more requests in flight through the ramp
+// and tail of a short launch; in a long one the steady state dominates, and there the extra
+// streams cost more than they bring.  Measured on one GPU (blocked and separate state, slices of
+// 2^23..2^28 elements, 4 alternating rounds of 10 launches per point, a cache flush before each
+// launch that moves under 2 GB), 3 against 2 per CU:
+//   fan-in 2 and 4:      1-5 % faster up to 32,768 work-groups, 2-8 % slower from 65,536;
+//   fp32 gradient:       2-5 % faster up to 32,768 (65,536 separate), 2 % slower at 131,072;
+//   fan-in 3 (run-time): 1-10 % faster up to 65,536, 1.5 % slower at 131,072;
+//   fan-in 16:           2 % faster up to 8,192, 3-8 % slower from 32,768;
+//   fan-in 8:            4 % faster at 4,096, 3-11 % slower from 16,384;
+//   fan-in 1:            2-10 % slower at every size (blocked state).
+// three_up_to is the largest launch, in work-groups, that still takes 3.
+inline int step_groups_per_cu(int fan_in, int64_t work_groups) {
+    int64_t three_up_to;
+    switch (fan_in) {
+        case 1: three_up_to = 0; break;
+        case 8: three_up_to = 4096; break;
+        case 2:
+        case 4: three_up_to = 32768; break;
+        case -1: three_up_to = 65536; break;                              // fp32 gradient
+        default: three_up_to = fan_in < 8 ? 65536 : 8192; break;          // run-time fan-in loop
+    }
+    return work_groups <= three_up_to ? 3 : 2;
 }
 
 constexpr int kMaxDevices = 64;
