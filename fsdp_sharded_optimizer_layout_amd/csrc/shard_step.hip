@@ -1090,9 +1090,9 @@ __global__ __launch_bounds__(kBlock) void state_pack_kernel(StatePackParams p) {
 //   fp32 accumulation: fan-in 1 takes 2 (4-5 % ahead of 4), fan-in 2 and run-time fan-ins
 //                     above 8 take 3 (2 % and 5 % ahead of 2), others 2;
 // the reduction fused with the sum of squares wants 2 per CU, 3 for a single contribution and 1
-// where its loads are software-pipelined (reduce_sq_pipelined); the sum of squares and
-// unflatten are fastest uncapped; the blocked-state packing takes 2 (14-20 % ahead of
-// uncapped).
+// where its loads are software-pipelined (reduce_sq_pipelined); unflatten is fastest uncapped
+// (the sum of squares has its own rule, sumsq_groups_per_cu); the blocked-state packing takes 2
+// (14-20 % ahead of uncapped).
 inline int reduce_groups_per_cu(int fan_in, bool accumulate) {
     if (fan_in == 1) return accumulate ? 2 : 4;
     if (fan_in == 2 || (accumulate && fan_in > 8)) return 3;
@@ -1431,6 +1431,18 @@ int check_sumsq_overlaps(const uint16_t* const* contribs, int32_t fan_in, const 
 
 // The two kernels of the sum of squares: one float64 partial per work-group into `partials`,
 // then their fixed-order sum into *sumsq.
+// Work-groups per CU of sumsq_kernel (see occupancy_lds; 0 = uncapped).  Measured on one GPU at
+// 2^25..2^29.75 elements, caps 1-4 against uncapped, 4 alternating rounds: uncapped is best for
+// one, two, three and sixteen contributions and for an fp32 gradient (every cap 1-4 is 0-330 %
+// slower at 2^28 and above); four contributions do 0.4-3.6 % better with 2; eight do 2.4 %
+// better with 1 from 8,192 work-groups (2^28 elements) up.  Against uncapped in a second run:
+// 1-3 % faster for four and eight contributions at 2^28 and above, within 1 % at 2^25.
+inline int sumsq_groups_per_cu(int32_t fan_in, int64_t work_groups) {
+    if (fan_in == 4) return 2;
+    if (fan_in == 8) return work_groups >= 8192 ? 1 : 0;
+    return 0;
+}
+
 int launch_sumsq(const uint16_t* const* contribs, int32_t fan_in, const float* grad, int64_t n,
                  const fsdpshard_segment* segs, int32_t n_segments, float scale, double* partials,
                  int64_t parts, double* sumsq, void* stream) {
@@ -1453,7 +1465,8 @@ int launch_sumsq(const uint16_t* const* contribs, int32_t fan_in, const float* g
                         : fan_in == 4 ? reinterpret_cast<const void*>(&sumsq_kernel<4>)
                         : fan_in == 8 ? reinterpret_cast<const void*>(&sumsq_kernel<8>)
                                       : reinterpret_cast<const void*>(&sumsq_kernel<0>);
-        const int rc = launch(k, static_cast<unsigned>(parts), &p, stream);
+        const int rc = launch(k, static_cast<unsigned>(parts), &p, stream,
+                              sumsq_groups_per_cu(fan_in, parts));
         if (rc != FSDPSHARD_OK) return rc;
     }
     // One work-group adds the partials (or writes +0 for an empty slice).
