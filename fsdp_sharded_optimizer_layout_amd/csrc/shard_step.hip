@@ -28,9 +28,12 @@
 //     a compare per group after that, and a per-element scan only in groups that hold an edge.
 //   * The bf16 destination may start at any 2-byte phase inside a 16-byte vector (a slice starts
 //     wherever floor(kP/N) falls).  The state streams stay aligned; the bf16 result is re-phased
-//     across lanes (each lane borrows its right neighbour's first elements through a lane
-//     permute) so interior stores stay 16-byte aligned, and only the two edge lanes of a group
-//     write their leftover elements with 2-byte stores.
+//     across lanes (lane permutes, and LDS between the waves of a work-group) so that every
+//     store inside a work-group is an aligned 16-byte vector and each wave writes whole 64-byte
+//     lines; only the elements at a work-group's two ends, whose lines it shares with its
+//     neighbours, go out as 2-byte stores.
+//   * Resident work-groups per CU are capped (2 or 3, by gradient source and launch size) by
+//     reserving LDS the kernel never touches: fewer concurrent streams suit the HBM.
 // Arithmetic is IEEE float32 with no contraction (the library is built with -ffp-contract=off),
 // correctly rounded division and square root, denormals kept.
 
