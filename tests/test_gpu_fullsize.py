@@ -295,3 +295,59 @@ def test_slice_beyond_2_31_elements():
     assert e.value.code == 3
     del grads
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fan_in", [2, 3, 16])
+def test_large_slice_other_fan_ins(fan_in):
+    """Fan-ins 2, 3 (the run-time loop) and 16 on a ragged slice of 2^27 + 123 elements, long
+    enough for their 2-work-groups-per-CU launch, blocked and separate state alike: two steps
+    compared bit for bit with the oracle on sampled windows (start, end, random)."""
+    n = (1 << 27) + 123
+    w = W.Workload(f"large_f{fan_in}", "one tensor of 2^27 + 123 elements", [n], 1, 1, 0,
+                   fan_in, 2, 1e-3, ("uniform", 0.05))
+    L, segs = F.shard_layout(w.sizes, 1, 0)
+    _, _, osegs = OL.segments(w.sizes, 1, None, 1, 0)
+    say(f"large slice, fan-in {fan_in}: n={n}")
+    rng = np.random.default_rng(fan_in)
+    idx = _windows(n, [], rng)
+    idx_t = torch.from_numpy(idx).cuda()
+    flags = _flags_at(osegs, idx)
+    segs_dev = F.segments_to_device(segs)
+    grads = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(fan_in)]
+    for blocked in (True, False):
+        master, m, v = W.torch_state(w, n, 11, "cuda")
+        om, omm, ov = (x[idx_t].cpu().numpy() for x in (master, m, v))
+        if blocked:
+            state = torch.empty(F.state_blocked_elems(n), dtype=torch.float32, device="cuda")
+            F.state_to_blocked(master, m, v, state)
+            torch.cuda.synchronize()
+            del master, m, v
+            pos = [torch.from_numpy(_blocked_index(idx, k)).cuda() for k in range(3)]
+            read = [lambda k=k: state[pos[k]].cpu().numpy() for k in range(3)]
+        else:
+            read = [lambda x=x: x[idx_t].cpu().numpy() for x in (master, m, v)]
+        flat = torch.full((n,), int(SENT16), dtype=torch.int16, device="cuda")
+        for t in (1, 2):
+            W.torch_grads_into(w, grads, t, 11)
+            kw = dict(step=t, segs=segs_dev, n_segments=L.n_segments, flat=flat, flat_index0=0,
+                      lo=0, **w.hp)
+            if blocked:
+                F.adamw_shard_step_blocked(state, grads, n=n, **kw)
+            else:
+                F.adamw_shard_step(master, m, v, grads, **kw)
+            contribs = [g[idx_t].cpu().numpy().view(np.uint16) for g in grads]
+            torch.cuda.synchronize()
+            om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, w.hp, t)
+            what = f"fan-in {fan_in} {'blocked' if blocked else 'separate'}"
+            for k, want, name in ((0, om, "master"), (1, omm, "m"), (2, ov, "v")):
+                _check(read[k](), want, f"{what} {name} step {t}")
+            _check(flat[idx_t].cpu().numpy().view(np.uint16), oout, f"{what} bf16 step {t}")
+        say(f"  {'blocked' if blocked else 'separate'} ok")
+        del read, flat
+        if blocked:
+            del state, pos
+        else:
+            del master, m, v
+        torch.cuda.empty_cache()
+    del grads
+    torch.cuda.empty_cache()
