@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "params updated/sec per GPU (sharded AdamW step); achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+# Bytes each way of the plain copy that calibrates the hardware byte counters (every run that
+# the counter summaries read launches it with exactly this size).
+CALIB_COPY_BYTES = 4 << 30
 DEFAULT_WORKLOAD = "dense7b_n8_rank0"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc")
@@ -99,13 +102,15 @@ def reshard_key(workload, dst_world, dst_pad, dst_rank):
 
 
 def summarize_counters(key, fetch_dir, write_dir, kernel_prefix=STEP_KERNEL, source=KERNEL_SOURCE,
-                       calib_kernel="stream_copy_kernel", calib_bytes=4 << 30):
+                       calib_kernel="stream_copy_kernel", calib_bytes=None):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, in KiB per
     dispatch) into per-launch HBM bytes of the measured kernel, each counter scaled by what it
     reads for the plain copy kernel, whose true traffic is calib_bytes read and calib_bytes
     written.  Writes the result into profiles/traffic.json under `key`."""
     import csv
     import statistics
+    if calib_bytes is None:
+        calib_bytes = CALIB_COPY_BYTES
 
     def per_dispatch(d, counter):
         path = os.path.join(d, "run_counter_collection.csv")
@@ -534,21 +539,36 @@ CEILING_SHAPES = {
     "copy": [(2, 256, 0, 256), (1, 256, 0, 1), (2, 1024, 0, 32)],
     "read2_write1": [(1, 256, 0, 256), (2, 512, 0, 32), (1, 256, 0, 32)],
 }
+# Streams read and written in place (as the step's state) take the shapes of their out-of-place
+# counterparts; eight read streams (the step's gradient count) the shapes that did best for them.
+CEILING_SHAPES["inplace"] = CEILING_SHAPES["copy"]
+CEILING_SHAPES["read1_inplace1"] = CEILING_SHAPES["read2_write1"]
+CEILING_SHAPES["read8"] = [(1, 256, 0, 32), (1, 256, 0, 256), (2, 512, 0, 32)]
+CEILING_SHAPES["read8_write1"] = [(1, 256, 0, 1), (1, 256, 0, 32), (2, 512, 0, 32)]
+CEILING_SHAPES["read7_inplace1"] = CEILING_SHAPES["read8_write1"]
 
 
-def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=4 << 30):
-    """What the memory system does for plain streams on this GPU: pure reads, pure writes, a
-    copy, and the step's 2 : 1 read : write byte ratio (each the best of a few launch shapes),
-    plus the time bound the pure rates imply for the step's bytes."""
-    bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=2 << 30):
+    """What the memory system does for plain streams on this GPU, each the best of a few launch
+    shapes: pure reads and pure writes, a copy, the step's 2 : 1 read : write byte ratio, each
+    also with its written stream read and written in place as the step's state is, and eight
+    read streams (the step's gradient streams at fan-in 8) alone, into one write stream and with
+    one of them written in place; plus the time bound the pure rates imply for the step's
+    bytes."""
+    # One allocation cut into nine streams, so that the calibration copy below can move
+    # CALIB_COPY_BYTES between two halves of it.
+    n4 = nbytes // 4
+    whole = torch.ones(9 * n4, dtype=torch.float32, device=dev)
+    bufs = [whole[i * n4:(i + 1) * n4] for i in range(9)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    for b in bufs:
-        b.fill_(1.0)
-    A, B, C = bufs
-    cases = {"read": ([A, B], [], 2 * nbytes), "write": ([], [A, B], 2 * nbytes),
-             "copy": ([A], [B], 2 * nbytes), "read2_write1": ([A, B], [C], 3 * nbytes)}
+    A, B, C = bufs[:3]
+    cases = {"read": ([A, B], []), "write": ([], [A, B]), "copy": ([A], [B]),
+             "read2_write1": ([A, B], [C]), "inplace": ([A], [A]), "read1_inplace1": ([A, B], [B]),
+             "read8": (bufs[:8], []), "read8_write1": (bufs[:8], [bufs[8]]),
+             "read7_inplace1": (bufs[:8], [bufs[7]])}
     out = {}
-    for name, (srcs, dsts, moved) in cases.items():
+    for name, (srcs, dsts) in cases.items():
+        moved = (len(srcs) + len(dsts)) * nbytes
         best = None
         for vpt, threads, per_cu, run in CEILING_SHAPES[name]:
             ms = time_launches(torch, lambda: F.stream_rw(
@@ -560,8 +580,11 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=4 
         out[name] = best
         log(f"  {name}: {best['GBps']} GB/s (vectors per thread, threads, per CU, XCD run: "
             f"{best['shape']})")
-    ms = time_launches(torch, lambda: F.stream_copy(A, B, stream=stream), stream, reps=10)
-    out["copy_plain"] = {"GBps": round(2 * nbytes / (ms / 1e3) / 1e9, 1),
+    c4 = CALIB_COPY_BYTES // 4
+    assert 2 * c4 <= whole.numel()
+    src, dst = whole[:c4], whole[c4:2 * c4]
+    ms = time_launches(torch, lambda: F.stream_copy(src, dst, stream=stream), stream, reps=10)
+    out["copy_plain"] = {"GBps": round(2 * CALIB_COPY_BYTES / (ms / 1e3) / 1e9, 1),
                          "kernel": "fsdpshard_stream_copy (the counters' calibration kernel)"}
     # If a channel could only read at the pure-read rate and write at the pure-write rate, one
     # after the other, the step's bytes would need at least this long.
@@ -571,7 +594,7 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=4 
         "read_bytes": read_bytes, "write_bytes": write_bytes,
         "meaning": "the step's read and write bytes at the pure-read and pure-write rates, one "
                    "after the other"}
-    del bufs, A, B, C, sink
+    del bufs, A, B, C, sink, src, dst, whole
     torch.cuda.empty_cache()
     return out
 
@@ -773,9 +796,11 @@ def main():
 
 # ----------------------------------------------------------------------------- reshard path
 
-def copy_reference(F, torch, dev, stream, nbytes=4 << 30):
+def copy_reference(F, torch, dev, stream, nbytes=None):
     """Plain 16-byte copy of nbytes (non-temporal loads and stores): the bandwidth a pure
     read+write stream reaches, and the calibration kernel of the counter runs."""
+    if nbytes is None:
+        nbytes = CALIB_COPY_BYTES
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     ms = time_launches(torch, lambda: F.stream_copy(src, dst, stream=stream), stream, reps=10,

@@ -4,9 +4,10 @@
 //   * stream_copy_kernel   one read and one write stream (the classic copy).
 //   * stream_rw_kernel     R read streams and W write streams of equal length: pure reads
 //                          (W = 0), pure writes (R = 0), a copy (1, 1), or the 2 : 1 read : write
-//                          byte ratio of the fused step at fan-in 8 (2, 1), in any launch shape
-//                          (vectors per thread, threads per work-group, work-groups per CU, XCD
-//                          run length).
+//                          byte ratio of the fused step at fan-in 8 (2, 1), any of them with a
+//                          write stream that is one of the read streams (read and written in
+//                          place, as the step's state), in any launch shape (vectors per thread,
+//                          threads per work-group, work-groups per CU, XCD run length).
 //   * stream_mix_kernel    the fused step's exact loads and stores (same vector width, cache
 //                          hints, tile map, load issue order and work-groups per CU) with
 //                          trivial integer arithmetic in place of the reduction and the update.
@@ -77,7 +78,8 @@ struct RwParams {
 
 // Thread t of the work-group on tile b handles vectors b * T * V + u * T + t, u < V (T threads
 // per work-group, V vectors per thread), of every stream: all loads first, then the XOR of the
-// loaded words (mixed with the index) to every write stream.  With no write stream, a lane whose
+// loaded words (mixed with the index) to every write stream.  A vector is read and written by the
+// same thread only, loads before stores, so a write stream may be one of the read streams.  With no write stream, a lane whose
 // XOR equals a fixed constant stores it to `sink`, so the loads cannot be dropped and almost no
 // bytes are written.
 template <int V>
@@ -354,8 +356,9 @@ extern "C" int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* 
         if (!aligned16(dst[w])) return FSDPSHARD_ERR_ALIGNMENT;
         for (int j = w + 1; j < n_dst; ++j)
             if (overlaps(dst[w], bytes, dst[j], bytes)) return FSDPSHARD_ERR_INVALID_ARG;
-        for (int r = 0; r < n_src; ++r)
-            if (overlaps(dst[w], bytes, src[r], bytes)) return FSDPSHARD_ERR_INVALID_ARG;
+        for (int r = 0; r < n_src; ++r)   // a destination may be a source itself (in place)
+            if (dst[w] != src[r] && overlaps(dst[w], bytes, src[r], bytes))
+                return FSDPSHARD_ERR_INVALID_ARG;
     }
     if (sink != nullptr && (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
         return FSDPSHARD_ERR_ALIGNMENT;

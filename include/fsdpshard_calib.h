@@ -38,14 +38,17 @@ int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* strea
  * fsdpshard_stream_rw -- n_src read streams and n_dst write streams, each `bytes` long, in a
  * chosen launch shape.
  *   Every 16-byte vector of every source is read once (non-temporal); destination vector i of
- *   stream w receives the XOR of the sources' vectors i mixed with i and w (non-temporal).  With
- *   n_dst == 0 nothing is written except, for a vector whose XOR equals a fixed constant (almost
- *   never), that value to *sink, so the loads cannot be optimised away.
+ *   stream w receives the XOR of the sources' vectors i, as they were before the call, mixed with
+ *   i and w (non-temporal).  With n_dst == 0 nothing is written except, for a vector whose XOR
+ *   equals a fixed constant (almost never), that value to *sink, so the loads cannot be
+ *   optimised away.
  *   src                host array of n_src device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS),
  *                      16-byte aligned
  *   dst                host array of n_dst device pointers (0 .. FSDPSHARD_CALIB_MAX_STREAMS),
- *                      16-byte aligned; no destination may overlap another stream;
- *                      n_src + n_dst >= 1
+ *                      16-byte aligned; n_src + n_dst >= 1.  A destination may not overlap
+ *                      another destination, nor a source unless it is that source's pointer
+ *                      exactly: that stream is then read and written in place, as the step
+ *                      does its fp32 state (every vector is loaded before it is stored)
  *   bytes              >= 0, a multiple of 16
  *   vectors_per_thread 1, 2 or 4 (others: UNSUPPORTED); a thread's vectors are a work-group
  *                      width apart
@@ -54,8 +57,9 @@ int fsdpshard_stream_copy(const void* src, void* dst, int64_t bytes, void* strea
  *   xcd_run            0 or 1: work-group b takes tile b; r > 1: each XCD streams runs of r
  *                      consecutive tiles (the tile map of the step kernels)
  *   sink               device, one uint32 (4-byte aligned); required when n_dst == 0
- * Pure reads (n_dst 0), pure writes (n_src 0), a copy (1, 1) and the fused step's 2 : 1 read :
- * write byte ratio at fan-in 8 (2, 1).
+ * Pure reads (n_dst 0), pure writes (n_src 0), a copy (1, 1), the fused step's 2 : 1 read :
+ * write byte ratio at fan-in 8 (2, 1); in place: one stream (src = dst = {A}) or one read
+ * stream and one in-place stream (src = {A, B}, dst = {B}).
  * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, UNSUPPORTED, OVERFLOW, HIP).
  */
 int fsdpshard_stream_rw(const void* const* src, int32_t n_src, void* const* dst, int32_t n_dst,

@@ -270,6 +270,7 @@ def test_calibration_call_validation():
     assert rw(src, 2, dst, 1, 16, t=128) == UNSUP                   # 256, 512 or 1024 threads
     assert rw((vp * 1)(_Fake.at(1, 8)), 1, dst, 1, 16) == ALIGN
     assert rw(src, 2, (vp * 1)(_Fake.at(1, 16)), 1, 64) == INVALID   # overlap
+    assert rw(src, 2, (vp * 2)(_Fake.at(2), _Fake.at(2)), 2, 64) == INVALID  # one array written twice
     assert rw(src, 1, dst, 0, 16, sink=_Fake.at(4, 2)) == ALIGN      # sink not 4-byte aligned
     ph = lambda fi, o, n, g=4, pc=1, run=32, phased=1: lib.fsdpshard_stream_mix_shaped(
         g8, fi, st, o, n, g, pc, run, phased, None)

@@ -53,6 +53,30 @@ def test_stream_rw_writes_what_it_reads(n_src, n_dst, vpt, threads, per_cu, run)
         assert np.array_equal(d.cpu().numpy().view(np.uint32).reshape(-1, 4), s)
 
 
+@pytest.mark.parametrize("n_src", [1, 2])
+@pytest.mark.parametrize("vpt,threads,per_cu,run", [(4, 256, 0, 0), (2, 512, 2, 32)])
+def test_stream_rw_in_place(n_src, vpt, threads, per_cu, run):
+    """A write stream that is also a read stream (the last one): it receives the XOR of the
+    sources as they were before the call, and nothing past the stream changes."""
+    nvec = 8192 * 11 + 333
+    nbytes = nvec * 16
+    rng = np.random.default_rng(70 + n_src)
+    srcs = [rng.integers(0, 2 ** 32, (nvec + GUARD, 4), dtype=np.uint32) for _ in range(n_src)]
+    sd = [_dev_u32(s) for s in srcs]
+    say(f"stream_rw in place, {n_src} read streams, shape {vpt}/{threads}/{per_cu}/{run}")
+    F.stream_rw(sd, [sd[-1]], nbytes, vectors_per_thread=vpt, threads_per_group=threads,
+                per_cu=per_cu, xcd_run=run)
+    torch.cuda.synchronize()
+    want = _index_pattern(nvec)
+    for s in srcs:
+        want = want ^ s[:nvec]
+    got = sd[-1].cpu().numpy().view(np.uint32).reshape(-1, 4)
+    assert np.array_equal(got[:nvec], want)
+    assert np.array_equal(got[nvec:], srcs[-1][nvec:]), "past the stream written"
+    for s, d in zip(srcs[:-1], sd[:-1]):
+        assert np.array_equal(d.cpu().numpy().view(np.uint32).reshape(-1, 4), s)
+
+
 def test_stream_rw_pure_reads_leave_the_sink():
     nvec = 4096 + 17
     src = _dev_u32(np.ones((nvec, 4), dtype=np.uint32))
