@@ -492,7 +492,7 @@ def stream_rw(srcs, dsts, nbytes, vectors_per_thread=4, threads_per_group=256, p
               xcd_run=0, sink=None, stream=None):
     """Measurement aid: len(srcs) read streams and len(dsts) write streams of ``nbytes`` each in
     one launch shape (pure reads when ``dsts`` is empty; then ``sink`` is a device tensor of at
-    least 4 bytes)."""
+    least 4 bytes).  A destination that is one of the sources is read and written in place."""
     nbytes = int(nbytes)
     for i, t in enumerate(list(srcs) + list(dsts)):
         _need_bytes(t, f"stream {i}", nbytes)
