@@ -555,13 +555,14 @@ __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb
     float g[kVec];
     sum_grad<F>(p, e0, true, kVec, raw, gf, g);
     adam8(p, scale, fl, g, th, mm, vv);
-    if constexpr (BLK && F >= 1) {
+    if constexpr (BLK && (F == 1 || F == 8)) {
         // Store pacing: the wave waits kStorePace x 64 cycles before its stores.  Measured on
-        // one GPU (compile-time variants, 8 alternating rounds), with the blocked state and bf16
-        // contributions a pause of 24-32 made the step 1.0-1.8 % faster on the 7B-, 70B-shaped
-        // and one-layer slices and left the 2,000-tensor slice within 0.2 %; 64 and longer were
-        // slower.  The same pause slowed the separate-array step (0.5-1 %) and the fp32-gradient
-        // step (1.6-1.8 %), which therefore store at once.
+        // one GPU (compile-time variants, 8 alternating rounds), with the blocked state a pause of
+        // 24-32 made the step 1.0-1.8 % faster at fan-in 8 (7B-shaped and one-layer slices) and
+        // fan-in 1 (70B-shaped slice); 64 and longer were slower.  At fan-in 2 and 4 it cost
+        // 0.7-2.4 % on 2^28-element slices (within 1 % on small ones), at the run-time fan-ins
+        // 3 and 16 it gained nothing, and it slowed the separate-array step (0.5-1 %) and the
+        // fp32-gradient step (1.6-1.8 %): those store at once.
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_sleep(kStorePace);
         __builtin_amdgcn_sched_barrier(0);
