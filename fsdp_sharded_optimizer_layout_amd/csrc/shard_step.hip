@@ -577,11 +577,14 @@ __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb
                 store_bf16_lines(p.out, p.out_shift, p.out_line_vecs, gb, lane, wave, edges, w);
         }
     };
-    // Store order: at fan-in 1 with the blocked state the bf16 copy goes first (measured on one
-    // GPU, 10 alternating rounds: 1.0-2.4 % faster on the 70B-shaped slice and on 2^25- and
-    // 2^28-element slices); at fan-in 8 the state goes first (bf16 first was 1.4-1.6 % slower
-    // on the 7B-shaped slice).
-    constexpr bool kOutFirst = BLK && F == 1;
+    // Store order: at fan-in 1 and for the fp32 gradient the bf16 copy goes first (measured on
+    // one GPU, 8-10 alternating rounds: with the blocked state 1.0-2.4 % faster at fan-in 1 on
+    // the 70B-shaped slice and on 2^25- and 2^28-element slices; with separate arrays 1.2-1.4 %
+    // faster at fan-in 1 on the 70B-shaped slice; 0.5-0.7 % faster for the fp32 gradient on
+    // the 7B- and 70B-shaped slices in both layouts); at fan-in 8 the state goes first (bf16
+    // first was 1.4-1.6 % slower with the blocked state, 3.5 % with separate arrays, on the
+    // 7B-shaped slice).
+    constexpr bool kOutFirst = F == 1 || F == -1;
     if constexpr (kOutFirst) store_out();
     store8(state_ptr<BLK>(p, 0, e0), true, kVec, th);
     store8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
