@@ -2,8 +2,8 @@
 """Benchmark of one rank's sharded AdamW step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path PATH]
-                    [--state blocked|separate] [--no-extra-workloads] [--no-copy-reference]
-                    [--no-cpu-baseline]
+                    [--state blocked|separate] [--grads separate|interleaved]
+                    [--no-extra-workloads] [--no-copy-reference] [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over the rank's slice: the host layout call
 (shard_layout: flatten, floor-rule slice, segment table) and the fused GPU step
@@ -15,8 +15,9 @@ bracketed by HIP events on the stream it runs on, which gives the kernel's own a
 for the roofline figure.
 
 The default run times the 7B-shaped slice (the headline `value`), then, under "workloads", the
-70B-shaped, one-layer and 2,000-tensor slices and the separate-array entry point on the 7B-shaped
-slice, then the memory-system references under "ceiling", then the CPU oracle.
+70B-shaped, one-layer and 2,000-tensor slices, the separate-array entry point on the 7B-shaped
+slice and the 7B-shaped slice with its contributions interleaved in one array, then the
+memory-system references under "ceiling", then the CPU oracle.
 
 Prints one JSON line (the last line of stdout).
 """
@@ -43,10 +44,20 @@ CSRC = os.path.join(ROOT, "fsdp_sharded_optimizer_layout_amd", "csrc")
 KERNEL_SOURCE = [os.path.join(CSRC, "shard_step.hip"), os.path.join(CSRC, "stream_common.h")]
 RESHARD_SOURCE = os.path.join(CSRC, "reshard.hip")
 STEP_KERNEL = "void (anonymous namespace)::fused_step_kernel"
+INTERLEAVED_STEP_KERNEL = "void (anonymous namespace)::fused_step_interleaved_kernel"
 RESHARD_KERNEL = "(anonymous namespace)::reshard_kernel"
-# Workloads measured after the headline in the default run: (name, blocked state layout).
-EXTRA_WORKLOADS = [("dense70b_n64_rank0", True), ("llama_layer_n8_rank0", True),
-                   ("many_small_n16_rank3", True), ("dense7b_n8_rank0", False)]
+# Workloads measured after the headline in the default run: (name, layout).  Layouts: "blocked"
+# (blocked state, F separate contributions), "separate" (three state arrays, F contributions),
+# "interleaved" (blocked state, the F contributions interleaved per block in one array).
+EXTRA_WORKLOADS = [("dense70b_n64_rank0", "blocked"), ("llama_layer_n8_rank0", "blocked"),
+                   ("many_small_n16_rank3", "blocked"), ("dense7b_n8_rank0", "separate"),
+                   ("dense7b_n8_rank0", "interleaved")]
+LAYOUT_DESCRIPTION = {
+    "blocked": "blocked: one array, 512-element blocks of master, m, v",
+    "separate": "separate master, m, v arrays",
+    "interleaved": ("blocked state; the F contributions interleaved per 512-element block in "
+                    "one array"),
+}
 
 
 def log(msg):
@@ -79,8 +90,8 @@ def source_digest(source=KERNEL_SOURCE):
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def traffic_key(workload, blocked=True):
-    return workload if blocked else f"{workload}:separate"
+def traffic_key(workload, layout="blocked"):
+    return workload if layout == "blocked" else f"{workload}:{layout}"
 
 
 def counter_traffic(key, source=KERNEL_SOURCE):
@@ -283,12 +294,16 @@ def cpu_baseline(workload, procs, seconds=12.0, chunk=1 << 22):
 # ----------------------------------------------------------------------------- GPU measurement
 
 class Slice:
-    """Device buffers of one workload's slice: state (blocked or separate), F contributions,
-    the bf16 flat window and the segment table."""
+    """Device buffers of one workload's slice: state (blocked or separate), F contributions (and
+    with the interleaved layout their interleaved copy), the bf16 flat window and the segment
+    table.  `layout` is one of LAYOUT_DESCRIPTION's keys (True / False mean blocked /
+    separate)."""
 
-    def __init__(self, F, W, torch, name, blocked, dev):
+    def __init__(self, F, W, torch, name, layout, dev):
+        layout = {True: "blocked", False: "separate"}.get(layout, layout)
+        blocked = layout != "separate"
         w = W.WORKLOADS[name]
-        self.w, self.blocked, self.dev = w, blocked, dev
+        self.w, self.layout, self.blocked, self.dev = w, layout, blocked, dev
         self.L, segs = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
         n, lo = self.L.n, self.L.lo
         master, m, v = W.torch_state(w, n, 0, dev)
@@ -299,6 +314,11 @@ class Slice:
                 if s["flags"] & F.SEG_PADDING:
                     for g in self.grads:
                         g[int(s["shard_begin"]): int(s["shard_begin"] + s["length"])] = 0x7FC0
+        self.gi = None
+        if layout == "interleaved":
+            self.gi = torch.empty(F.grads_interleaved_elems(w.fan_in, n), dtype=torch.int16,
+                                  device=dev)
+            F.grads_to_interleaved(self.grads, self.gi, n=n)
         self.phase = lo % 8
         self.flat = torch.empty(n + self.phase, dtype=torch.int16, device=dev)
         self.segs_dev = F.segments_to_device(segs, dev)
@@ -319,7 +339,10 @@ class Slice:
                     flat_index0=L.lo - self.phase, lo=L.lo, stream=stream, **self.w.hp)
 
     def step_bf16(self, F, t, **kw):
-        if self.blocked:
+        if self.gi is not None:
+            F.adamw_shard_step_interleaved(self.state, self.gi, self.w.fan_in, step=t,
+                                           n=self.L.n, **kw)
+        elif self.blocked:
             F.adamw_shard_step_blocked(self.state, self.grads, step=t, n=self.L.n, **kw)
         else:
             F.adamw_shard_step(self.master, self.m, self.v, self.grads, step=t, **kw)
@@ -337,7 +360,9 @@ def build_stages(F, torch, S, path, stream, args):
     bpp = algorithmic_bytes_per_param(Fi)
     common = S.common(stream)
     stages = []
-    suffix = "_blocked" if S.blocked else ""
+    suffix = {"blocked": "_blocked", "separate": "", "interleaved": "_interleaved"}[S.layout]
+    if S.layout == "interleaved" and path != "fused":
+        raise ValueError("the interleaved contributions feed the fused step only (--path fused)")
     if path == "fused":
         stages.append(("adamw_shard_step" + suffix, lambda t: S.step_bf16(F, t, **common),
                        L.n_real * bpp))
@@ -502,18 +527,19 @@ def mix_references(F, torch, S, stream, evict, shapes=False):
     return ref
 
 
-def measure_workload(F, W, torch, name, blocked, args, dev, stream, mix=True):
+def measure_workload(F, W, torch, name, layout, args, dev, stream, mix=True):
     """The fused step of one workload: its stage timing, roofline figures and (like for like,
-    flushed when the step is) the traffic replica."""
-    S = Slice(F, W, torch, name, blocked, dev)
+    flushed when the step is) the traffic replica (not for the interleaved contributions, which
+    no replica reads)."""
+    S = Slice(F, W, torch, name, layout, dev)
     stages = build_stages(F, torch, S, "fused", stream, args)
     evict_mb, evict = make_evict(torch, dev, stages[0][2], args.evict_mb)
     r = time_stages(F, torch, S, stages, stream, args.steps, args.warmup, evict)
     st = r["stages"][0]
     bpp = algorithmic_bytes_per_param(S.w.fan_in)
     gbps = st["algorithmic_bytes"] / (st["avg_ms"] / 1e3) / 1e9
-    out = {"workload": name,
-           "state_layout": "blocked" if blocked else "separate master, m, v arrays",
+    out = {"workload": name, "layout": layout,
+           "state_layout": LAYOUT_DESCRIPTION[layout],
            "call": st["call"], "fan_in": S.w.fan_in, "slice_elems": S.L.n,
            "real_params": S.L.n_real, "segments": S.L.n_segments, "dest_phase": S.phase,
            "algorithmic_bytes_per_param": bpp,
@@ -521,9 +547,9 @@ def measure_workload(F, W, torch, name, blocked, args, dev, stream, mix=True):
            "ms_per_step": round(r["ms_per_step"], 4),
            "params_per_s": round(S.L.n_real / (r["ms_per_step"] / 1e3), 1),
            "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
-           "traffic": counter_traffic(traffic_key(name, blocked)),
+           "traffic": counter_traffic(traffic_key(name, layout)),
            "timing": r["timing"]}
-    if mix and not args.no_copy_reference:
+    if mix and layout != "interleaved" and not args.no_copy_reference:
         out["mix_reference"] = mix_references(F, torch, S, stream, evict)
     del S, evict
     torch.cuda.empty_cache()
@@ -626,6 +652,9 @@ def main():
                     help="optimizer-state layout: one array of 512-element blocks of master, m "
                          "and v (default), or three separate arrays (the split path always uses "
                          "separate arrays)")
+    ap.add_argument("--grads", choices=["separate", "interleaved"], default="separate",
+                    help="gradient contributions: F separate arrays (default), or interleaved per "
+                         "512-element block in one array (fused path, blocked state only)")
     ap.add_argument("--max-grad-norm", type=float, default=1.0)
     ap.add_argument("--evict-mb", type=int, default=-1,
                     help="MiB written between timed steps to flush the 256 MB last-level cache "
@@ -650,8 +679,11 @@ def main():
                               args.reshard_rank)
             summarize_counters(key, *args.summarize_counters, kernel_prefix=RESHARD_KERNEL,
                                source=RESHARD_SOURCE)
+        elif args.grads == "interleaved":
+            summarize_counters(traffic_key(args.workload, "interleaved"),
+                               *args.summarize_counters, kernel_prefix=INTERLEAVED_STEP_KERNEL)
         else:
-            summarize_counters(traffic_key(args.workload, args.state == "blocked"),
+            summarize_counters(traffic_key(args.workload, args.state),
                                *args.summarize_counters)
         return
 
@@ -677,7 +709,11 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     blocked = args.state == "blocked" and args.path != "split"
-    S = Slice(F, W, torch, w.name, blocked, dev)
+    if args.grads == "interleaved" and (not blocked or args.path != "fused"):
+        print("--grads interleaved needs the fused path and the blocked state", file=sys.stderr)
+        sys.exit(2)
+    layout = ("interleaved" if args.grads == "interleaved" else "blocked") if blocked else "separate"
+    S = Slice(F, W, torch, w.name, layout, dev)
     L, Fi = S.L, w.fan_in
     log(f"workload {w.name}: P={L.P} slice [{L.lo}, {L.hi}) n={L.n} n_real={L.n_real} "
         f"F={Fi} segments={L.n_segments}")
@@ -694,12 +730,12 @@ def main():
     for x in stage_info:
         log(f"  {x['call']}: {x['avg_ms']:.3f} ms, {x['GBps']} GB/s")
     achieved = main_stage["algorithmic_bytes"] / avg_kernel_s / 1e9
-    traffic = counter_traffic(traffic_key(w.name, blocked)) if args.path == "fused" else None
+    traffic = counter_traffic(traffic_key(w.name, layout)) if args.path == "fused" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic}
 
     mix_ref = None
-    if not args.no_copy_reference and args.path == "fused":
+    if not args.no_copy_reference and args.path == "fused" and layout != "interleaved":
         mix_ref = mix_references(F, torch, S, stream, evict, shapes=True)
         for k, x in (mix_ref or {}).items():
             if isinstance(x, dict):
@@ -712,10 +748,10 @@ def main():
     extra = None
     if args.path == "fused" and not args.no_extra_workloads:
         extra = []
-        for name, blk in EXTRA_WORKLOADS:
-            if name == w.name and blk == blocked:
+        for name, lay in EXTRA_WORKLOADS:
+            if name == w.name and lay == layout:
                 continue
-            x = measure_workload(F, W, torch, name, blk, args, dev, stream)
+            x = measure_workload(F, W, torch, name, lay, args, dev, stream)
             log(f"workload {name} ({x['state_layout']}): {x['kernel_avg_ms']:.4f} ms, "
                 f"{x['GBps']} GB/s, frac {x['frac']}")
             extra.append(x)
@@ -780,8 +816,7 @@ def main():
             "step_ms_min": round(min(r["step_ms"]), 4),
             "timing": r["timing"],
             "path": args.path,
-            "state_layout": ("blocked: one array, 512-element blocks of master, m, v" if blocked
-                             else "separate master, m, v arrays"),
+            "state_layout": LAYOUT_DESCRIPTION[layout],
             "stages": stage_info,
         },
         "roofline": roofline,

@@ -96,6 +96,11 @@ def lib():
     h.adamw_shard_step_f32grad_blocked.argtypes = [c_vp, c_vp, c_i64, c_vp, c_i32,
                                                    ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64,
                                                    c_vp]
+    h.grads_interleaved_elems.argtypes = [c_i32, c_i64]
+    h.grads_interleaved_elems.restype = c_i64
+    h.adamw_shard_step_interleaved.argtypes = [c_vp, c_vp, c_i32, c_i64, c_vp, c_i32,
+                                               ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64, c_vp]
+    h.grads_to_interleaved.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, c_vp, c_vp]
     h.state_to_blocked.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp]
     h.state_from_blocked.argtypes = [c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]
     h.reduce_shard_accumulate.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float,
@@ -131,6 +136,7 @@ def lib():
                  "fsdpshard_stream_mix", "fsdpshard_stream_mix_blocked",
                  "fsdpshard_stream_mix_shaped", "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
                  "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
+                 "adamw_shard_step_interleaved", "grads_to_interleaved",
                  "state_to_blocked", "state_from_blocked"):
         getattr(h, name).restype = ctypes.c_int
     _lib_handle = h
@@ -361,6 +367,44 @@ def adamw_shard_step_f32grad_blocked(state, grad, step, lr, n, beta1=0.9, beta2=
         _ptr(state, "state", {torch.float32}, state_blocked_elems(n)),
         _ptr(grad, "grad", {torch.float32}, n), n, _segs(segs, n_segments), int(n_segments),
         ctypes.byref(hp), _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, state)))
+
+
+def grads_interleaved_elems(fan_in, n):
+    """Elements of the interleaved gradient array of fan_in contributions of an n-element slice
+    (STATE_BLOCK-element blocks, one per rank in rank order, block after block)."""
+    v = int(lib().grads_interleaved_elems(int(fan_in), int(n)))
+    if v < 0:
+        raise ValueError(f"fan-in {fan_in} or slice length {n} out of range")
+    return v
+
+
+def adamw_shard_step_interleaved(state, grads, fan_in, step, lr, n, beta1=0.9, beta2=0.999,
+                                 eps=1e-8, weight_decay=0.0, grad_scale=1.0, segs=None,
+                                 n_segments=0, flat=None, flat_index0=0, lo=0, max_grad_norm=0.0,
+                                 grad_sumsq=None, stream=None):
+    """adamw_shard_step_blocked fed by the fan_in contributions interleaved in one array
+    ``grads`` of grads_interleaved_elems(fan_in, n) bf16 elements."""
+    import torch
+    n = int(n)
+    fan_in = int(fan_in)
+    hp = _hp(step, lr, beta1, beta2, eps, weight_decay, grad_scale, max_grad_norm, grad_sumsq)
+    if flat is not None and not isinstance(flat, int):
+        _ptr(flat, "flat", _bf16_dtypes(), n + int(lo) - int(flat_index0))
+    _check("adamw_shard_step_interleaved", lib().adamw_shard_step_interleaved(
+        _ptr(state, "state", {torch.float32}, state_blocked_elems(n)),
+        _ptr(grads, "grads", _bf16_dtypes(), grads_interleaved_elems(fan_in, n)), fan_in, n,
+        _segs(segs, n_segments), int(n_segments), ctypes.byref(hp),
+        _ptr(flat, "flat"), int(flat_index0), int(lo), _stream(stream, state)))
+
+
+def grads_to_interleaved(contribs, grads, n=None, stream=None):
+    """Copy the separate contributions (n elements each) into the interleaved array ``grads``."""
+    n = contribs[0].numel() if n is None else int(n)
+    arr = _contrib_array(contribs, n)
+    _check("grads_to_interleaved", lib().grads_to_interleaved(
+        ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n,
+        _ptr(grads, "grads", _bf16_dtypes(), grads_interleaved_elems(len(contribs), n)),
+        _stream(stream, grads)))
 
 
 def state_to_blocked(master, m, v, state, n=None, stream=None):

@@ -22,7 +22,9 @@
 //     Gradient loads and all full-vector stores carry the non-temporal hint (single-use
 //     streams); the state loads do not.
 //   * Contributions are reduced in registers in rank order 0..F-1 from +0 (fixed order, so the
-//     result is deterministic and matches a sequential float32 sum bit for bit).
+//     result is deterministic and matches a sequential float32 sum bit for bit).  They come as F
+//     arrays, or interleaved per 512-element block in one array (grad_src), which the step then
+//     streams as a single gradient array.
 //   * Segment flags (padding, weight decay) come from a per-wave cursor over the segment table:
 //     one binary search when a wave starts (issued after the tile's loads, so it overlaps them),
 //     a compare per group after that, and a per-element scan only in groups that hold an edge.
@@ -365,20 +367,40 @@ __device__ __forceinline__ void store_bf16_lines(uint16_t* out, int s, int q, in
 //
 // Reduced gradient of one vector, before the scale: the contributions summed in rank order from
 // +0.  Every HBM load is issued before the first add (the run-time fan-in loads four at a time).
-template <int F>
+//
+// Where rank r's vector at slice element e0 lives: its own array (p.contrib[r]), or with GIL the
+// interleaved buffer at p.contrib[0], whose block b holds every rank's elements
+// [512b, 512b + 512) one rank after another: rank r's element i at
+// ((i / 512) * fan_in + r) * 512 + i % 512.
+template <int F, bool GIL>
+__device__ __forceinline__ const uint16_t* grad_src(const StepParams& p, int r, int64_t e0) {
+    if constexpr (GIL) {
+        const uint64_t u = static_cast<uint64_t>(e0);
+        const int64_t fan_in = F > 0 ? F : p.fan_in;
+        return p.contrib[0] +
+               (static_cast<int64_t>(u / kStateBlock) * fan_in + r) * kStateBlock +
+               static_cast<int64_t>(u % kStateBlock);
+    } else {
+        return p.contrib[r] + e0;
+    }
+}
+
+template <int F, bool GIL = false>
 __device__ __forceinline__ void load_grad(const StepParams& p, int64_t e0, bool full, int cnt,
                                           uint4 (&raw)[F > 0 ? F : 1], float (&gf)[kVec]) {
     if constexpr (F > 0) {
 #pragma unroll
-        for (int r = 0; r < F; ++r)
-            raw[r] = full ? ld_u4_nt(p.contrib[r] + e0) : ld_u4_partial(p.contrib[r] + e0, cnt);
+        for (int r = 0; r < F; ++r) {
+            const uint16_t* src = grad_src<F, GIL>(p, r, e0);
+            raw[r] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
+        }
     } else if constexpr (F == -1) {
         if (full) ld8_f32_nt(p.grad32 + e0, gf);
         else load8(p.grad32 + e0, false, cnt, gf);
     }
 }
 
-template <int F>
+template <int F, bool GIL = false>
 __device__ __forceinline__ void sum_grad(const StepParams& p, int64_t e0, bool full, int cnt,
                                          const uint4 (&raw)[F > 0 ? F : 1],
                                          const float (&gf)[kVec], float (&g)[kVec]) {
@@ -399,7 +421,7 @@ __device__ __forceinline__ void sum_grad(const StepParams& p, int64_t e0, bool f
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (r0 + q < fan_in) {
-                    const uint16_t* src = p.contrib[r0 + q] + e0;
+                    const uint16_t* src = grad_src<F, GIL>(p, r0 + q, e0);
                     q4[q] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
                 }
             }
@@ -466,7 +488,7 @@ __device__ __forceinline__ float* state_ptr(const StepParams& p, int k, int64_t 
 
 // One 512-element group with per-lane bounds: the slice's last, partial group, and every group
 // of the run-time fan-in kernel.  TAIL = false drops the bounds for complete groups.
-template <int F, bool OUT, bool TAIL, bool BLK>
+template <int F, bool OUT, bool TAIL, bool BLK, bool GIL>
 __device__ __forceinline__ void step_group(const StepParams& p, float scale, const SegCursor& cur,
                                            int64_t vec, int64_t group_end_vec, int lane) {
     const int64_t n = p.n;
@@ -479,11 +501,11 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
     float g[kVec], gf[kVec], th[kVec], mm[kVec], vv[kVec];
     uint4 raw[F > 0 ? F : 1];
     if (valid) {
-        load_grad<F>(p, e0, full, cnt, raw, gf);
+        load_grad<F, GIL>(p, e0, full, cnt, raw, gf);
         load8(state_ptr<BLK>(p, 0, e0), full, cnt, th);
         load8(state_ptr<BLK>(p, 1, e0), full, cnt, mm);
         load8(state_ptr<BLK>(p, 2, e0), full, cnt, vv);
-        sum_grad<F>(p, e0, full, cnt, raw, gf, g);
+        sum_grad<F, GIL>(p, e0, full, cnt, raw, gf, g);
     } else {
 #pragma unroll
         for (int e = 0; e < kVec; ++e) g[e] = th[e] = mm[e] = vv[e] = 0.0f;
@@ -521,7 +543,7 @@ __device__ __forceinline__ void step_group(const StepParams& p, float scale, con
 // Pause before a group's stores, in units of 64 cycles (see step_whole_group).
 constexpr int kStorePace = 28;
 
-template <int F, bool OUT, bool BLK>
+template <int F, bool OUT, bool BLK, bool GIL>
 __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb, int lane,
                                                  int wave, bool edges) {
     uint4 raw[F > 0 ? F : 1];
@@ -537,7 +559,7 @@ __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb
         load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
         load8(state_ptr<BLK>(p, 2, e0), true, kVec, vv);
         __builtin_amdgcn_sched_barrier(0);
-        load_grad<F>(p, e0, true, kVec, raw, gf);
+        load_grad<F, GIL>(p, e0, true, kVec, raw, gf);
     } else {
         load8(state_ptr<BLK>(p, 0, e0), true, kVec, th);
         load8(state_ptr<BLK>(p, 1, e0), true, kVec, mm);
@@ -553,7 +575,7 @@ __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb
     uint32_t fl[kVec];
     element_flags(cur, (gb + kWave) * kVec, e0, fl);
     float g[kVec];
-    sum_grad<F>(p, e0, true, kVec, raw, gf, g);
+    sum_grad<F, GIL>(p, e0, true, kVec, raw, gf, g);
     adam8(p, scale, fl, g, th, mm, vv);
     if constexpr (BLK && (F == 1 || F == 8)) {
         // Store pacing: the wave waits kStorePace x 64 cycles before its stores.  Measured on
@@ -596,8 +618,8 @@ __device__ __forceinline__ void step_whole_group(const StepParams& p, int64_t gb
 // XCD-aware tile map.  One group per wave was measured fastest on MI355X for every fan-in and
 // state layout: waves owning 2 or 4 consecutive groups (all loads first) ran 7-15 % slower on
 // the 7B- and 70B-shaped slices.
-template <int F, bool OUT, bool BLK>
-__global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
+template <int F, bool OUT, bool BLK, bool GIL>
+__device__ __forceinline__ void fused_step_body(StepParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t nvec = (p.n + kVec - 1) / kVec;
@@ -610,7 +632,7 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
             const int64_t tile_end = (gb / (kWave * kWavesPerBlock) + 1) * (kWave * kWavesPerBlock);
             const bool edges =
                 OUT && (p.out_shift != 0 || p.out_line_vecs != 0) && tile_end <= p.n / kVec;
-            step_whole_group<F, OUT, BLK>(p, gb, lane, wave, edges);
+            step_whole_group<F, OUT, BLK, GIL>(p, gb, lane, wave, edges);
             return;
         }
     }
@@ -620,9 +642,21 @@ __global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
     int64_t gend = gb + kWave;
     if (gend > nvec) gend = nvec;
     if (gend == gb + kWave && gend * kVec <= p.n)
-        step_group<F, OUT, false, BLK>(p, scale, cur, gb + lane, gend, lane);
+        step_group<F, OUT, false, BLK, GIL>(p, scale, cur, gb + lane, gend, lane);
     else
-        step_group<F, OUT, true, BLK>(p, scale, cur, gb + lane, gend, lane);
+        step_group<F, OUT, true, BLK, GIL>(p, scale, cur, gb + lane, gend, lane);
+}
+
+template <int F, bool OUT, bool BLK>
+__global__ __launch_bounds__(kBlock) void fused_step_kernel(StepParams p) {
+    fused_step_body<F, OUT, BLK, false>(p);
+}
+
+// The blocked state with the F bf16 contributions interleaved per 512-element block in one
+// buffer (grad_src): the step then streams one gradient array instead of F.
+template <int F, bool OUT>
+__global__ __launch_bounds__(kBlock) void fused_step_interleaved_kernel(StepParams p) {
+    fused_step_body<F, OUT, true, true>(p);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1121,6 +1155,36 @@ __global__ __launch_bounds__(kBlock) void state_pack_kernel(StatePackParams p) {
     }
 }
 
+// Copy of F separate contributions into the interleaved buffer (grad_src): lane by lane, one
+// 16-byte vector per contribution, elements past the slice in the last block left untouched.
+struct InterleaveParams {
+    const uint16_t* contrib[FSDPSHARD_MAX_FAN_IN];
+    uint16_t* dst;
+    int64_t n;
+    int32_t fan_in;
+};
+
+__global__ __launch_bounds__(kBlock) void interleave_kernel(InterleaveParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int64_t vec = tile_base(wave, 1) + lane;
+    const int64_t e0 = vec * kVec;
+    if (e0 >= p.n) return;
+    const int cnt = static_cast<int>((p.n - e0) < kVec ? (p.n - e0) : kVec);
+    const uint64_t u = static_cast<uint64_t>(e0);
+    uint16_t* dst = p.dst + static_cast<int64_t>(u / kStateBlock) * p.fan_in * kStateBlock +
+                    static_cast<int64_t>(u % kStateBlock);
+    for (int r = 0; r < p.fan_in; ++r) {
+        const uint16_t* src = p.contrib[r] + e0;
+        uint16_t* d = dst + static_cast<int64_t>(r) * kStateBlock;
+        if (cnt == kVec) {
+            st_u4_nt(d, ld_u4_nt(src));
+        } else {
+            for (int e = 0; e < cnt; ++e) d[e] = src[e];
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // Host-side launch helpers.
 
@@ -1166,6 +1230,22 @@ const void* pick_step_kernel(int fan_in, bool out) {
     }
 }
 
+template <int F>
+const void* interleaved_step_kernel(bool out) {
+    return out ? reinterpret_cast<const void*>(&fused_step_interleaved_kernel<F, true>)
+               : reinterpret_cast<const void*>(&fused_step_interleaved_kernel<F, false>);
+}
+
+const void* pick_interleaved_step_kernel(int fan_in, bool out) {
+    switch (fan_in) {
+        case 1: return interleaved_step_kernel<1>(out);
+        case 2: return interleaved_step_kernel<2>(out);
+        case 4: return interleaved_step_kernel<4>(out);
+        case 8: return interleaved_step_kernel<8>(out);
+        default: return interleaved_step_kernel<0>(out);
+    }
+}
+
 // First slice element whose bf16 destination starts a 16-byte vector.
 int out_shift_of(const uint16_t* out) {
     const unsigned phase = static_cast<unsigned>(reinterpret_cast<uintptr_t>(out) & 15u) / 2u;
@@ -1186,18 +1266,25 @@ int64_t seg_bytes(const fsdpshard_segment* segs, int32_t n_segments) {
     return segs == nullptr ? 0 : static_cast<int64_t>(n_segments) * sizeof(fsdpshard_segment);
 }
 
-// Shared by the step entry points: exactly one of (contribs, fan_in >= 1) and (grad32,
-// fan_in == -1) is the gradient source.  With `blocked`, `master` is the blocked state array and
-// m, v are null.
+// Shared by the step entry points: exactly one of (contribs, fan_in >= 1), (grad32,
+// fan_in == -1) and (interleaved, fan_in >= 1) is the gradient source.  With `blocked`, `master`
+// is the blocked state array and m, v are null; the interleaved source needs the blocked state.
 int launch_step(float* master, float* m, float* v, const uint16_t* const* contribs, int32_t fan_in,
                 const float* grad32, int64_t n, const fsdpshard_segment* segs, int32_t n_segments,
                 const fsdpshard_adamw* hp, uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
-                void* stream, bool blocked = false) {
+                void* stream, bool blocked = false, const uint16_t* interleaved = nullptr) {
     if (master == nullptr || (!blocked && (m == nullptr || v == nullptr)) || hp == nullptr ||
         n < 0 || n_segments < 0 || (n_segments > 0 && segs == nullptr) || lo < 0)
         return FSDPSHARD_ERR_INVALID_ARG;
     int rc = FSDPSHARD_OK;
-    if (fan_in == -1) {
+    int64_t il_elems = 0;
+    if (interleaved != nullptr) {
+        if (!blocked || fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
+        if (fan_in > FSDPSHARD_MAX_FAN_IN) return FSDPSHARD_ERR_UNSUPPORTED;
+        if (!aligned16(interleaved)) return FSDPSHARD_ERR_ALIGNMENT;
+        il_elems = interleaved_elems(fan_in, n);
+        if (il_elems < 0) return FSDPSHARD_ERR_OVERFLOW;
+    } else if (fan_in == -1) {
         if (grad32 == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
         if (!aligned16(grad32)) return FSDPSHARD_ERR_ALIGNMENT;
     } else {
@@ -1232,7 +1319,9 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
         if (wr[i] == nullptr) continue;
         for (int j = i + 1; j < 4; ++j)
             if (overlaps(wr[i], wb[i], wr[j], wb[j])) return FSDPSHARD_ERR_INVALID_ARG;
-        if (fan_in == -1) {
+        if (interleaved != nullptr) {
+            if (overlaps(wr[i], wb[i], interleaved, il_elems * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+        } else if (fan_in == -1) {
             if (overlaps(wr[i], wb[i], grad32, fb)) return FSDPSHARD_ERR_INVALID_ARG;
         } else {
             for (int r = 0; r < fan_in; ++r)
@@ -1248,7 +1337,8 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     p.m = blocked ? nullptr : m;
     p.v = blocked ? nullptr : v;
     for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
-        p.contrib[r] = (fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
+        p.contrib[r] = (interleaved == nullptr && fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
+    if (interleaved != nullptr) p.contrib[0] = interleaved;
     p.segs = segs;
     p.grad32 = fan_in == -1 ? grad32 : nullptr;
     p.out = out;
@@ -1275,8 +1365,9 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     unsigned blocks = 0;
     rc = tile_grid(n, 1, &blocks);
     if (rc != FSDPSHARD_OK) return rc;
-    const void* k = blocked ? pick_step_kernel<true>(fan_in, out != nullptr)
-                            : pick_step_kernel<false>(fan_in, out != nullptr);
+    const void* k = interleaved != nullptr ? pick_interleaved_step_kernel(fan_in, out != nullptr)
+                    : blocked              ? pick_step_kernel<true>(fan_in, out != nullptr)
+                                           : pick_step_kernel<false>(fan_in, out != nullptr);
     return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in, blocks));
 }
 
@@ -1369,6 +1460,42 @@ extern "C" int adamw_shard_step_f32grad_blocked(float* state, const float* grad,
                                                 int64_t flat_index0, int64_t lo, void* stream) {
     return launch_step(state, nullptr, nullptr, nullptr, -1, grad, n, segs, n_segments, hp,
                        flat_bf16, flat_index0, lo, stream, true);
+}
+
+extern "C" int64_t grads_interleaved_elems(int32_t fan_in, int64_t n) {
+    return interleaved_elems(fan_in, n);
+}
+
+extern "C" int adamw_shard_step_interleaved(float* state, const uint16_t* grads, int32_t fan_in,
+                                            int64_t n, const fsdpshard_segment* segs,
+                                            int32_t n_segments, const fsdpshard_adamw* hp,
+                                            uint16_t* flat_bf16, int64_t flat_index0, int64_t lo,
+                                            void* stream) {
+    if (grads == nullptr || fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
+    return launch_step(state, nullptr, nullptr, nullptr, fan_in, nullptr, n, segs, n_segments, hp,
+                       flat_bf16, flat_index0, lo, stream, true, grads);
+}
+
+extern "C" int grads_to_interleaved(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                                    uint16_t* grads, void* stream) {
+    if (grads == nullptr || n < 0) return FSDPSHARD_ERR_INVALID_ARG;
+    const int rc = check_contribs(contribs, fan_in);
+    if (rc != FSDPSHARD_OK) return rc;
+    if (!aligned16(grads)) return FSDPSHARD_ERR_ALIGNMENT;
+    const int64_t elems = interleaved_elems(fan_in, n);
+    if (elems < 0) return FSDPSHARD_ERR_OVERFLOW;
+    for (int r = 0; r < fan_in && n > 0; ++r)
+        if (overlaps(grads, elems * 2, contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+    if (n == 0) return FSDPSHARD_OK;
+    InterleaveParams p;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
+    p.dst = grads;
+    p.n = n;
+    p.fan_in = fan_in;
+    unsigned blocks = 0;
+    const int grc = tile_grid(n, 1, &blocks);
+    if (grc != FSDPSHARD_OK) return grc;
+    return launch(reinterpret_cast<const void*>(&interleave_kernel), blocks, &p, stream);
 }
 
 namespace {

@@ -146,6 +146,15 @@ inline int64_t blocked_elems(int64_t n) {
     return 3 * ((n + kStateBlock - 1) / kStateBlock) * kStateBlock;
 }
 
+// Elements of a buffer holding fan_in contributions of an n-element slice interleaved per block
+// of kStateBlock elements (-1 when its size in bytes does not fit int64 or fan_in is out of range).
+inline int64_t interleaved_elems(int32_t fan_in, int64_t n) {
+    if (n < 0 || fan_in < 1 || fan_in > FSDPSHARD_MAX_FAN_IN) return -1;
+    const int64_t blocks = n / kStateBlock + (n % kStateBlock != 0 ? 1 : 0);
+    if (blocks > INT64_MAX / (2 * kStateBlock * fan_in)) return -1;
+    return blocks * kStateBlock * fan_in;
+}
+
 inline int check_contribs(const uint16_t* const* contribs, int32_t fan_in) {
     if (contribs == nullptr || fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
     if (fan_in > FSDPSHARD_MAX_FAN_IN) return FSDPSHARD_ERR_UNSUPPORTED;

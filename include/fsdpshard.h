@@ -140,6 +140,44 @@ int adamw_shard_step_f32grad_blocked(float* state, const float* grad, int64_t n,
                                      int64_t flat_index0, int64_t lo, void* stream);
 
 /*
+ * Interleaved gradient layout (an alternative to F separate contribution arrays).
+ *
+ * The F bf16 contributions of an n-element slice kept in one array of
+ * grads_interleaved_elems(F, n) elements: for block b = i / FSDPSHARD_STATE_BLOCK and
+ * o = i % FSDPSHARD_STATE_BLOCK, contribution r's element i is at
+ * grads[(b * F + r) * FSDPSHARD_STATE_BLOCK + o].  Positions past n in the last block are never
+ * read.  The values are the slice's F contributions of [FSDP], communication pattern of one unit
+ * (what the reduce-scatter sums); only their placement differs: a receive buffer the peers write
+ * into block by block.  With it the step streams one gradient array instead of F.
+ */
+int64_t grads_interleaved_elems(int32_t fan_in, int64_t n);  /* F * ceil(n / 512) * 512, or -1 if
+                                                               fan_in or n is out of range     */
+
+/*
+ * adamw_shard_step_interleaved -- adamw_shard_step_blocked with the contributions interleaved.
+ *   grads   device, grads_interleaved_elems(fan_in, n) bf16 bit patterns, 16-byte aligned, read
+ *           only; it must not overlap the state, the bf16 window or grad_sumsq
+ *   fan_in  1 .. FSDPSHARD_MAX_FAN_IN; contributions are added in rank order r = 0 .. F-1
+ * The results are bit-identical to adamw_shard_step_blocked on the same contributions; every
+ * other argument and error is that call's (OVERFLOW also when the gradient array's size in bytes
+ * does not fit int64).
+ */
+int adamw_shard_step_interleaved(float* state, const uint16_t* grads, int32_t fan_in, int64_t n,
+                                 const fsdpshard_segment* segs, int32_t n_segments,
+                                 const fsdpshard_adamw* hp, uint16_t* flat_bf16,
+                                 int64_t flat_index0, int64_t lo, void* stream);
+
+/*
+ * grads_to_interleaved -- copy F separate contributions (n elements each) into the interleaved
+ * array `grads` (grads_interleaved_elems(fan_in, n) elements; positions past n in the last block
+ * are left untouched).  All pointers device and 16-byte aligned; `grads` must not overlap a
+ * contribution.  Errors: INVALID_ARG, UNSUPPORTED (fan_in > FSDPSHARD_MAX_FAN_IN), ALIGNMENT,
+ * OVERFLOW, HIP.
+ */
+int grads_to_interleaved(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                         uint16_t* grads, void* stream);
+
+/*
  * state_to_blocked, state_from_blocked -- copy an n-element slice's state between the separate
  * arrays (n floats each) and the blocked array (state_blocked_elems(n) floats), e.g. to
  * checkpoint or reshard blocked state with reshard_plan / reshard_copy, which move the separate

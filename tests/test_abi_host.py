@@ -191,6 +191,52 @@ def test_step_validation_errors():
     assert _step(lib, a, b, c, g, 2, 100, None, 0, hp, g[0] + 64, 0, 0) == INVALID
 
 
+def test_interleaved_validation_errors():
+    """The interleaved gradient array: its size rule, and every argument check of the step and of
+    the conversion, which stop before anything is launched."""
+    lib = F.lib()
+    assert F.grads_interleaved_elems(8, 1000) == 8 * 1024
+    assert F.grads_interleaved_elems(3, 512) == 3 * 512
+    assert F.grads_interleaved_elems(1, 0) == 0
+    assert lib.grads_interleaved_elems(0, 10) == -1
+    assert lib.grads_interleaved_elems(65, 10) == -1
+    assert lib.grads_interleaved_elems(2, -1) == -1
+    assert lib.grads_interleaved_elems(64, 2 ** 62) == -1          # bytes beyond int64
+    hp = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    st, gi, out = _Fake.at(0), _Fake.at(1), _Fake.at(2)
+    il = lambda state, grads, fan_in, n, segs=None, nseg=0, h=hp, flat=out: \
+        lib.adamw_shard_step_interleaved(state, grads, fan_in, n, segs, nseg,
+                                         ctypes.byref(h) if h is not None else None, flat, 0, 0,
+                                         None)
+    assert il(st, gi, 8, 0) == OK
+    assert il(st, None, 8, 0) == INVALID
+    assert il(None, gi, 8, 0) == INVALID
+    assert il(st, gi, 0, 0) == INVALID
+    assert il(st, gi, 65, 0) == UNSUP
+    assert il(st, gi + 8, 8, 0) == ALIGN
+    assert il(st + 4, gi, 8, 0) == ALIGN
+    assert il(st, gi, 8, -1) == INVALID
+    assert il(st, gi, 8, 0, h=None) == INVALID
+    assert il(st, gi, 64, 2 ** 59) == OVERFLOW
+    n = 1000                                  # 8 * 1024 bf16 = 16 KiB of gradients
+    assert il(st, gi, 8, n, flat=gi + 16384 - 64) == INVALID       # bf16 window inside grads
+    assert il(gi + 16384 - 16, gi, 8, n) == INVALID                # state over the grads' end
+    assert il(st, gi, 8, n, segs=st + 64, nseg=1) == INVALID       # table inside the state
+    clip = F._AdamW(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1, 1.0, st + 8)
+    assert il(st, gi, 8, n, h=clip) == INVALID                     # sum inside the state
+    g = (ctypes.c_void_p * 2)(_Fake.at(3), _Fake.at(4))
+    conv = lib.grads_to_interleaved
+    assert conv(g, 2, 0, gi, None) == OK
+    assert conv(g, 2, 0, None, None) == INVALID
+    assert conv(g, 0, 0, gi, None) == INVALID
+    assert conv(g, 2, -1, gi, None) == INVALID
+    assert conv(g, 2, 0, gi + 2, None) == ALIGN
+    assert conv((ctypes.c_void_p * 2)(_Fake.at(3), None), 2, 0, gi, None) == INVALID
+    # the 2 * 512-element array (2 KiB) starting 1 KiB before a contribution runs into it
+    assert conv(g, 2, 100, _Fake.at(3, -1024), None) == INVALID
+    assert conv(g, 2, 100, _Fake.at(4, -1024), None) == INVALID
+
+
 def test_reduce_and_unflatten_validation_errors():
     lib = F.lib()
     g = (ctypes.c_void_p * 2)(_Fake.at(3), _Fake.at(4))
