@@ -101,6 +101,8 @@ def lib():
     h.adamw_shard_step_interleaved.argtypes = [c_vp, c_vp, c_i32, c_i64, c_vp, c_i32,
                                                ctypes.POINTER(_AdamW), c_vp, c_i64, c_i64, c_vp]
     h.grads_to_interleaved.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, c_vp, c_vp]
+    h.grad_sumsq_shard_interleaved.argtypes = [c_vp, c_i32, c_i64, c_vp, c_i32, ctypes.c_float,
+                                               c_vp, c_i64, c_vp, c_vp]
     h.state_to_blocked.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp]
     h.state_from_blocked.argtypes = [c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]
     h.reduce_shard_accumulate.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float,
@@ -137,6 +139,7 @@ def lib():
                  "fsdpshard_stream_mix_shaped", "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
                  "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
                  "adamw_shard_step_interleaved", "grads_to_interleaved",
+                 "grad_sumsq_shard_interleaved",
                  "state_to_blocked", "state_from_blocked"):
         getattr(h, name).restype = ctypes.c_int
     _lib_handle = h
@@ -466,6 +469,21 @@ def grad_sumsq_shard(sumsq, contribs=None, grad=None, n=None, scale=1.0, segs=No
         arr_p, fan_in, gp, n, _segs(segs, n_segments), int(n_segments), float(scale),
         _ptr(workspace, "workspace"), wbytes, _ptr(sumsq, "sumsq", {torch.float64}, 1),
         _stream(stream, sumsq)))
+
+
+def grad_sumsq_shard_interleaved(sumsq, grads, fan_in, n, scale=1.0, segs=None, n_segments=0,
+                                 workspace=None, stream=None):
+    """grad_sumsq_shard of fan_in contributions held in the interleaved array ``grads``."""
+    import torch
+    n, fan_in = int(n), int(fan_in)
+    need = grad_sumsq_workspace_bytes(n)
+    if workspace is None:
+        workspace = _call_workspace(need, sumsq.device, stream)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check("grad_sumsq_shard_interleaved", lib().grad_sumsq_shard_interleaved(
+        _ptr(grads, "grads", _bf16_dtypes(), grads_interleaved_elems(fan_in, n)), fan_in, n,
+        _segs(segs, n_segments), int(n_segments), float(scale), _ptr(workspace, "workspace"),
+        wbytes, _ptr(sumsq, "sumsq", {torch.float64}, 1), _stream(stream, sumsq)))
 
 
 NOALLOC_MAX_ELEMS = 65536 * 32768

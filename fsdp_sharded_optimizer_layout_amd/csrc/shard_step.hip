@@ -372,8 +372,8 @@ __device__ __forceinline__ void store_bf16_lines(uint16_t* out, int s, int q, in
 // interleaved buffer at p.contrib[0], whose block b holds every rank's elements
 // [512b, 512b + 512) one rank after another: rank r's element i at
 // ((i / 512) * fan_in + r) * 512 + i % 512.
-template <int F, bool GIL>
-__device__ __forceinline__ const uint16_t* grad_src(const StepParams& p, int r, int64_t e0) {
+template <int F, bool GIL, class Params>
+__device__ __forceinline__ const uint16_t* grad_src(const Params& p, int r, int64_t e0) {
     if constexpr (GIL) {
         const uint64_t u = static_cast<uint64_t>(e0);
         const int64_t fan_in = F > 0 ? F : p.fan_in;
@@ -718,8 +718,8 @@ __device__ __forceinline__ void square_group(const SumsqParams& p, SegCursor& cu
     add_squares(cur, p.n, gb, nvec, lane, gs, cnt, acc);
 }
 
-template <int F>
-__global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
+template <int F, bool GIL>
+__device__ __forceinline__ void sumsq_body(SumsqParams p) {
     constexpr int B = sumsq_batch<F>();
     static_assert(kSumsqGroups % B == 0, "a batch must divide a wave's groups");
     __shared__ double wave_part[kWavesPerBlock];
@@ -751,7 +751,8 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
                         for (int b = 0; b < B; ++b) {
                             const int64_t e0 = (base0 + (g0 + b) * kWave + lane) * kVec;
 #pragma unroll
-                            for (int r = 0; r < F; ++r) raw[b][r] = ld_u4_nt(p.contrib[r] + e0);
+                            for (int r = 0; r < F; ++r)
+                                raw[b][r] = ld_u4_nt(grad_src<F, GIL>(p, r, e0));
                         }
 #pragma unroll
                         for (int b = 0; b < B; ++b) {
@@ -788,15 +789,16 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
                     } else if constexpr (F > 0) {
                         uint4 raw[F];
 #pragma unroll
-                        for (int r = 0; r < F; ++r)
-                            raw[r] = full ? ld_u4_nt(p.contrib[r] + e0)
-                                          : ld_u4_partial(p.contrib[r] + e0, cnt);
+                        for (int r = 0; r < F; ++r) {
+                            const uint16_t* src = grad_src<F, GIL>(p, r, e0);
+                            raw[r] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
+                        }
 #pragma unroll
                         for (int r = 0; r < F; ++r) accumulate(g, raw[r]);
                     } else {
                         for (int r = 0; r < p.fan_in; ++r) {
-                            const uint4 q = full ? ld_u4_nt(p.contrib[r] + e0)
-                                                 : ld_u4_partial(p.contrib[r] + e0, cnt);
+                            const uint16_t* src = grad_src<F, GIL>(p, r, e0);
+                            const uint4 q = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
                             accumulate(g, q);
                         }
                     }
@@ -814,6 +816,17 @@ __global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
         for (int w = 1; w < kWavesPerBlock; ++w) b += wave_part[w];
         p.partials[tile] = b;
     }
+}
+
+template <int F>
+__global__ __launch_bounds__(kBlock) void sumsq_kernel(SumsqParams p) {
+    sumsq_body<F, false>(p);
+}
+
+// The F bf16 contributions interleaved per 512-element block in one array (grad_src).
+template <int F>
+__global__ __launch_bounds__(kBlock) void sumsq_interleaved_kernel(SumsqParams p) {
+    sumsq_body<F, true>(p);
 }
 
 // Finish: thread t adds partials t, t + 256, t + 512, ... in that order, then the fixed wave and
@@ -1613,12 +1626,16 @@ inline int sumsq_groups_per_cu(int32_t fan_in, int64_t work_groups) {
     return 0;
 }
 
+// fan_in 0 selects the fp32 gradient `grad`; with `interleaved`, the fan_in contributions are
+// read from that one interleaved array (contribs unused).
 int launch_sumsq(const uint16_t* const* contribs, int32_t fan_in, const float* grad, int64_t n,
                  const fsdpshard_segment* segs, int32_t n_segments, float scale, double* partials,
-                 int64_t parts, double* sumsq, void* stream) {
+                 int64_t parts, double* sumsq, void* stream,
+                 const uint16_t* interleaved = nullptr) {
     SumsqParams p;
     for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
-        p.contrib[r] = (fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
+        p.contrib[r] = (interleaved == nullptr && fan_in > 0 && r < fan_in) ? contribs[r] : nullptr;
+    if (interleaved != nullptr) p.contrib[0] = interleaved;
     p.grad32 = fan_in == 0 ? grad : nullptr;
     p.segs = segs;
     p.partials = partials;
@@ -1630,11 +1647,17 @@ int launch_sumsq(const uint16_t* const* contribs, int32_t fan_in, const float* g
     p.n_partials = static_cast<int32_t>(parts);
     p.scale = scale;
     if (parts > 0) {
-        const void* k = fan_in == 0   ? reinterpret_cast<const void*>(&sumsq_kernel<-1>)
-                        : fan_in == 1 ? reinterpret_cast<const void*>(&sumsq_kernel<1>)
-                        : fan_in == 4 ? reinterpret_cast<const void*>(&sumsq_kernel<4>)
-                        : fan_in == 8 ? reinterpret_cast<const void*>(&sumsq_kernel<8>)
-                                      : reinterpret_cast<const void*>(&sumsq_kernel<0>);
+        const void* k =
+            interleaved != nullptr
+                ? (fan_in == 1   ? reinterpret_cast<const void*>(&sumsq_interleaved_kernel<1>)
+                   : fan_in == 4 ? reinterpret_cast<const void*>(&sumsq_interleaved_kernel<4>)
+                   : fan_in == 8 ? reinterpret_cast<const void*>(&sumsq_interleaved_kernel<8>)
+                                 : reinterpret_cast<const void*>(&sumsq_interleaved_kernel<0>))
+            : fan_in == 0 ? reinterpret_cast<const void*>(&sumsq_kernel<-1>)
+            : fan_in == 1 ? reinterpret_cast<const void*>(&sumsq_kernel<1>)
+            : fan_in == 4 ? reinterpret_cast<const void*>(&sumsq_kernel<4>)
+            : fan_in == 8 ? reinterpret_cast<const void*>(&sumsq_kernel<8>)
+                          : reinterpret_cast<const void*>(&sumsq_kernel<0>);
         const int rc = launch(k, static_cast<unsigned>(parts), &p, stream,
                               sumsq_groups_per_cu(fan_in, parts));
         if (rc != FSDPSHARD_OK) return rc;
@@ -1661,6 +1684,30 @@ extern "C" int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in,
     if (rc != FSDPSHARD_OK) return rc;
     return launch_sumsq(contribs, fan_in, grad, n, segs, n_segments, scale,
                         static_cast<double*>(workspace), parts, sumsq, stream);
+}
+
+extern "C" int grad_sumsq_shard_interleaved(const uint16_t* grads, int32_t fan_in, int64_t n,
+                                            const fsdpshard_segment* segs, int32_t n_segments,
+                                            float scale, void* workspace, int64_t workspace_bytes,
+                                            double* sumsq, void* stream) {
+    if (grads == nullptr || fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
+    if (fan_in > FSDPSHARD_MAX_FAN_IN) return FSDPSHARD_ERR_UNSUPPORTED;
+    // The interleaved array is checked as one input of grads_interleaved_elems elements.
+    const uint16_t* one[1] = {grads};
+    int64_t parts = 0;
+    int rc = check_sumsq_args(one, 1, nullptr, n, segs, n_segments, sumsq, &parts);
+    if (rc != FSDPSHARD_OK) return rc;
+    const int64_t elems = interleaved_elems(fan_in, n);
+    if (elems < 0) return FSDPSHARD_ERR_OVERFLOW;
+    const int64_t need = parts * static_cast<int64_t>(sizeof(double));
+    if (parts > 0 && (workspace == nullptr || workspace_bytes < need))
+        return FSDPSHARD_ERR_CAPACITY;
+    if (parts > 0 && !aligned8(workspace)) return FSDPSHARD_ERR_ALIGNMENT;
+    rc = check_sumsq_overlaps(one, 1, nullptr, elems, segs, n_segments,
+                              parts > 0 ? workspace : nullptr, need, sumsq);
+    if (rc != FSDPSHARD_OK) return rc;
+    return launch_sumsq(nullptr, fan_in, nullptr, n, segs, n_segments, scale,
+                        static_cast<double*>(workspace), parts, sumsq, stream, grads);
 }
 
 // ------------------------------------------------------------------------------------------------

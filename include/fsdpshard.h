@@ -311,6 +311,21 @@ int grad_sumsq_shard(const uint16_t* const* contribs, int32_t fan_in, const floa
                      void* workspace, int64_t workspace_bytes, double* sumsq, void* stream);
 
 /*
+ * grad_sumsq_shard_interleaved -- grad_sumsq_shard of fan_in contributions held in the
+ * interleaved layout (see grads_interleaved_elems): the same sum, bit for bit, in the same
+ * order.
+ *   grads   device, grads_interleaved_elems(fan_in, n) bf16 bit patterns, 16-byte aligned
+ *   fan_in  1 .. FSDPSHARD_MAX_FAN_IN
+ * Every other argument and error is grad_sumsq_shard's (the interleaved array is the input that
+ * the workspace, sumsq and the segment table must not overlap; OVERFLOW also when its size in
+ * bytes does not fit int64).
+ */
+int grad_sumsq_shard_interleaved(const uint16_t* grads, int32_t fan_in, int64_t n,
+                                 const fsdpshard_segment* segs, int32_t n_segments, float scale,
+                                 void* workspace, int64_t workspace_bytes, double* sumsq,
+                                 void* stream);
+
+/*
  * grad_sumsq_shard_noalloc -- grad_sumsq_shard with no workspace argument.
  *
  * For callers that cannot allocate device memory: code under HIP graph capture, tight serving

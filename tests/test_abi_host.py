@@ -235,6 +235,20 @@ def test_interleaved_validation_errors():
     # the 2 * 512-element array (2 KiB) starting 1 KiB before a contribution runs into it
     assert conv(g, 2, 100, _Fake.at(3, -1024), None) == INVALID
     assert conv(g, 2, 100, _Fake.at(4, -1024), None) == INVALID
+    sq = lambda grads, fan_in, n, segs=None, nseg=0, ws=_Fake.at(7), wsb=1 << 20, res=_Fake.at(8): \
+        lib.grad_sumsq_shard_interleaved(grads, fan_in, n, segs, nseg, 1.0, ws, wsb, res, None)
+    # (n == 0 still launches the kernel that writes +0 into sumsq, so no call below succeeds)
+    assert sq(None, 8, 0) == INVALID
+    assert sq(gi, 0, 0) == INVALID
+    assert sq(gi, 65, 0) == UNSUP
+    assert sq(gi + 8, 8, 0) == ALIGN
+    assert sq(gi, 8, 0, res=None) == INVALID
+    assert sq(gi, 8, -1) == INVALID
+    assert sq(gi, 64, 2 ** 59) == OVERFLOW
+    assert sq(gi, 8, n, wsb=0) == CAPACITY
+    assert sq(gi, 8, n, ws=gi + 16384 - 8) == INVALID          # workspace over the grads' end
+    assert sq(gi, 8, n, res=gi + 8192) == INVALID              # sum inside the grads
+    assert sq(gi, 8, n, segs=_Fake.at(7), nseg=1) == INVALID     # table over the workspace
 
 
 def test_reduce_and_unflatten_validation_errors():

@@ -6,8 +6,12 @@
   1 ulp) and bit for bit against adamw_shard_step_blocked on the same contributions, over sizes
   with ragged tails, the compile-time fan-ins 1, 2, 4 and 8 and run-time fan-ins, segment tables
   with NaN padding gradients, output phases and clipping; the gradient array is never written;
+* grad_sumsq_shard_interleaved within relative 1e-12 of the oracle's exactly rounded sum and bit
+  for bit equal to grad_sumsq_shard on the separate contributions (whole tiles, ragged tails,
+  padding inside whole tiles, compile-time and run-time fan-ins); the clipped cases of the step
+  take their norm from it;
 * a ragged slice whose interleaved offsets pass 2^31 elements, and the 7B-shaped slice at full
-  size: interleaved steps equal blocked steps bit for bit.
+  size: interleaved steps and sums equal the separate-contribution ones bit for bit.
 """
 
 import numpy as np
@@ -25,6 +29,7 @@ from gpu_helpers import SENT16, Guarded, assert_bf16, assert_f32, bit_equal, say
 pytestmark = pytest.mark.gpu
 HP = dict(W.ADAMW)
 SENT = np.float32(np.uint32(0x7FB0B0B0).view(np.float32))
+SUMSQ_RTOL = 1e-12
 
 
 @pytest.mark.parametrize("n", [1, 7, 511, 512, 513, 4099, 65539, 1_000_003])
@@ -88,12 +93,20 @@ def test_interleaved_step_matches_oracle_and_blocked_step(case):
         dev = [to_dev16(cb) for cb in contribs]
         packed = BL.to_interleaved(contribs, fill=SENT16)
         gi = Guarded(packed)
+        kw_b = dict(kw)
         if clip:
-            F.grad_sumsq_shard(sumsq, contribs=dev, n=n, segs=sd, n_segments=nseg)
-            ohp["grad_scale"] = float(OC.clipped_scale(OC.grad_sumsq(contribs, real), clip))
+            sumsq_b = torch.zeros(1, dtype=torch.float64, device="cuda")
+            F.grad_sumsq_shard_interleaved(sumsq, gi.data(), F_in, n, segs=sd, n_segments=nseg)
+            F.grad_sumsq_shard(sumsq_b, contribs=dev, n=n, segs=sd, n_segments=nseg)
+            exact = OC.grad_sumsq(contribs, real)
+            torch.cuda.synchronize()
+            assert float(sumsq.item()) == float(sumsq_b.item())
+            assert abs(float(sumsq.item()) - exact) <= SUMSQ_RTOL * exact
+            ohp["grad_scale"] = float(OC.clipped_scale(exact, clip))
             kw.update(max_grad_norm=clip, grad_sumsq=sumsq)
+            kw_b.update(max_grad_norm=clip, grad_sumsq=sumsq_b)
         F.adamw_shard_step_interleaved(blk_i.data(), gi.data(), F_in, flat=flat_i.window(), **kw)
-        F.adamw_shard_step_blocked(blk_b.data(), dev, flat=flat_b.window(), **kw)
+        F.adamw_shard_step_blocked(blk_b.data(), dev, flat=flat_b.window(), **kw_b)
         om, omm, ov, oout = OS.shard_step(om, omm, ov, contribs, flags, ohp, t)
         torch.cuda.synchronize()
         gm, gmm, gv = BL.from_blocked(blk_i.data_host(), n)
@@ -107,6 +120,51 @@ def test_interleaved_step_matches_oracle_and_blocked_step(case):
         gi.assert_guards("interleaved gradients")
     blk_i.assert_guards("blocked state")
     flat_i.assert_guards("flat window")
+
+
+SUMSQ_CASES = [(1, 1), (7, 8), (513, 3), (32768, 4), (32769, 8), (1_000_003, 8), (2_500_001, 1),
+               (300_017, 5), (100_003, 16), (70_001, 2)]
+
+
+@pytest.mark.parametrize("n,F_in", SUMSQ_CASES)
+def test_interleaved_sumsq_matches_exact_and_separate(n, F_in):
+    say(f"interleaved sumsq n={n} F={F_in}")
+    contribs = [W.np_bf16_normal([64, F_in, r], n, 1e-2) for r in range(F_in)]
+    gi = Guarded(BL.to_interleaved(contribs, fill=SENT16))
+    got_t = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    sep_t = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    F.grad_sumsq_shard_interleaved(got_t, gi.data(), F_in, n, scale=0.5)
+    F.grad_sumsq_shard(sep_t, contribs=[to_dev16(c) for c in contribs], n=n, scale=0.5)
+    torch.cuda.synchronize()
+    got, sep = float(got_t.item()), float(sep_t.item())
+    want = OC.grad_sumsq(contribs, np.ones(n, bool), 0.5)
+    assert got == sep, (got, sep)
+    assert abs(got - want) <= SUMSQ_RTOL * want, (got, want)
+    gi.assert_guards("interleaved gradients")
+
+
+@pytest.mark.parametrize("F_in", [1, 3, 4, 8])
+def test_interleaved_sumsq_padding_inside_whole_tiles(F_in):
+    # 300 small tensors padded to 16, NaN in the padding, across many whole tiles.
+    sizes = [(i * 7919) % 3001 + 1 for i in range(300)]
+    L, segs, flags = _layout(sizes, 16, None, 2, 1)
+    n = L.n
+    real = (flags & OL.PADDING) == 0
+    say(f"interleaved sumsq padded tiles F={F_in} n={n}")
+    contribs = [W.np_bf16_normal([69, F_in, r], n, 1e-2) for r in range(F_in)]
+    for c in contribs:
+        c[~real] = 0x7FC0
+    sd = F.segments_to_device(segs)
+    got_t = torch.zeros(1, dtype=torch.float64, device="cuda")
+    sep_t = torch.zeros(1, dtype=torch.float64, device="cuda")
+    F.grad_sumsq_shard_interleaved(got_t, to_dev16(BL.to_interleaved(contribs)), F_in, n, segs=sd,
+                                   n_segments=L.n_segments)
+    F.grad_sumsq_shard(sep_t, contribs=[to_dev16(c) for c in contribs], n=n, segs=sd,
+                       n_segments=L.n_segments)
+    torch.cuda.synchronize()
+    want = OC.grad_sumsq(contribs, real)
+    assert float(got_t.item()) == float(sep_t.item())
+    assert abs(float(got_t.item()) - want) <= SUMSQ_RTOL * want
 
 
 def _bf16_like(n, gen, std):
@@ -127,16 +185,21 @@ def _interleaved_equals_blocked(n, fan_in, segs_dev, n_segments, hp, state0_seed
     gi = torch.empty(F.grads_interleaved_elems(fan_in, n), dtype=torch.int16, device="cuda")
     flat_i = torch.empty(n, dtype=torch.int16, device="cuda")
     flat_b = torch.empty(n, dtype=torch.int16, device="cuda")
+    sq_i = torch.zeros(1, dtype=torch.float64, device="cuda")
+    sq_b = torch.zeros(1, dtype=torch.float64, device="cuda")
     for t in range(1, steps + 1):
         for g in grads:
             g.copy_(_bf16_like(n, gen, 1e-3))
         F.grads_to_interleaved(grads, gi, n=n)
+        F.grad_sumsq_shard_interleaved(sq_i, gi, fan_in, n, segs=segs_dev, n_segments=n_segments)
+        F.grad_sumsq_shard(sq_b, contribs=grads, n=n, segs=segs_dev, n_segments=n_segments)
         kw = dict(step=t, n=n, segs=segs_dev, n_segments=n_segments, flat_index0=0, lo=0, **hp)
         F.adamw_shard_step_interleaved(st_i, gi, fan_in, flat=flat_i, **kw)
         F.adamw_shard_step_blocked(st_b, grads, flat=flat_b, **kw)
         torch.cuda.synchronize()
         assert torch.equal(st_i.view(torch.int32), st_b.view(torch.int32)), f"state step {t}"
         assert torch.equal(flat_i, flat_b), f"bf16 step {t}"
+        assert float(sq_i.item()) == float(sq_b.item()), f"sum of squares step {t}"
         say(f"  step {t} ok")
     del st_i, st_b, grads, gi, flat_i, flat_b
     torch.cuda.empty_cache()
