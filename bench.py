@@ -17,7 +17,8 @@ for the roofline figure.
 The default run times the 7B-shaped slice (the headline `value`), then the memory-system
 references under "ceiling", then, under "workloads", the 70B-shaped, one-layer and 2,000-tensor
 slices, the separate-array entry point on the 7B-shaped slice and the 7B-shaped slice with its
-contributions interleaved in one array, then the CPU oracle.
+contributions interleaved in one array (each of these in a fresh process of its own), then the
+CPU oracle.
 
 Prints one JSON line (the last line of stdout).
 """
@@ -27,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -625,6 +627,31 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=2 
     return out
 
 
+def run_child(args, spec):
+    """One measurement (`--child spec`) in a fresh Python process on the same GPU; its record."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--child", spec, "--workload", args.workload,
+           "--steps", str(args.steps), "--warmup", str(args.warmup), "--evict-mb",
+           str(args.evict_mb)]
+    if args.no_copy_reference:
+        cmd.append("--no-copy-reference")
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    if r.returncode != 0:
+        raise RuntimeError(f"measurement {spec} failed with status {r.returncode}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def child_measurement(args, w, F, W, torch, dev, stream):
+    """The measurement `args.child` names, in this (fresh) process."""
+    if args.child == "ceiling":
+        L, _ = F.shard_layout(w.sizes, w.world_size, w.rank, w.pad_multiple, w.wd_mask)
+        return ceiling_references(F, torch, dev, stream, L.n_real * (2 * w.fan_in + 12),
+                                  L.n_real * 14)
+    kind, name, layout = args.child.split(":")
+    if kind != "workload" or layout not in LAYOUT_DESCRIPTION:
+        raise ValueError(f"unknown measurement {args.child}")
+    return measure_workload(F, W, torch, name, layout, args, dev, stream)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -670,6 +697,9 @@ def main():
                     help="time only the selected workload")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+    # One measurement of the default run in a process of its own: "ceiling", or
+    # "workload:NAME:LAYOUT".  Prints its JSON record as the last line of stdout.
+    ap.add_argument("--child", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.summarize_counters:
         if args.path == "reshard":
@@ -708,6 +738,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.child:
+        print(json.dumps(child_measurement(args, w, F, W, torch, dev, stream)), flush=True)
+        return
     blocked = args.state == "blocked" and args.path != "split"
     if args.grads == "interleaved" and (not blocked or args.path != "fused"):
         print("--grads interleaved needs the fused path and the blocked state", file=sys.stderr)
@@ -740,18 +773,19 @@ def main():
         for k, x in (mix_ref or {}).items():
             if isinstance(x, dict):
                 log(f"  traffic replica {k}: {x['GBps']} GB/s")
-    read_bytes = L.n_real * (2 * Fi + 12)
-    write_bytes = L.n_real * 14
     del S, stages, evict
     torch.cuda.empty_cache()
 
-    # The plain-stream references run before the other workloads: measured after those
-    # workloads' allocations (the interleaved slice alone takes 41 GB), the 2 : 1 stream landed on
-    # other physical memory and read 4 % lower, the other references unchanged.
+    # The memory-system references and every other workload run in a fresh process each: the
+    # bandwidth of a set of buffers depends on where in memory they land, and that depends on
+    # what the process allocated and freed before (measured on one box: the 2 : 1 reference
+    # read 4 % lower after the other workloads' allocations, and the separate-array step 7 %
+    # lower after the references').  A fresh process sees what a run of that workload alone
+    # sees.
     ceiling = None
     if not args.no_copy_reference:
         log("memory-system references:")
-        ceiling = ceiling_references(F, torch, dev, stream, read_bytes, write_bytes)
+        ceiling = run_child(args, "ceiling")
 
     extra = None
     if args.path == "fused" and not args.no_extra_workloads:
@@ -759,7 +793,7 @@ def main():
         for name, lay in EXTRA_WORKLOADS:
             if name == w.name and lay == layout:
                 continue
-            x = measure_workload(F, W, torch, name, lay, args, dev, stream)
+            x = run_child(args, f"workload:{name}:{lay}")
             log(f"workload {name} ({x['state_layout']}): {x['kernel_avg_ms']:.4f} ms, "
                 f"{x['GBps']} GB/s, frac {x['frac']}")
             extra.append(x)
