@@ -3,7 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path PATH]
                     [--state blocked|separate] [--grads separate|interleaved]
-                    [--no-extra-workloads] [--no-copy-reference] [--no-cpu-baseline]
+                    [--no-extra-workloads] [--no-ceiling] [--no-copy-reference]
+                    [--no-cpu-baseline]
 
 A step is one pass of the whole hot path over the rank's slice: the host layout call
 (shard_layout: flatten, floor-rule slice, segment table) and the fused GPU step
@@ -583,8 +584,7 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=2 
     read streams (the step's gradient streams at fan-in 8) alone, into one write stream and with
     one of them written in place; plus the time bound the pure rates imply for the step's
     bytes."""
-    # One allocation cut into nine streams, so that the calibration copy below can move
-    # CALIB_COPY_BYTES between two halves of it.
+    # One allocation cut into nine streams.
     n4 = nbytes // 4
     whole = torch.ones(9 * n4, dtype=torch.float32, device=dev)
     bufs = [whole[i * n4:(i + 1) * n4] for i in range(9)]
@@ -608,12 +608,6 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=2 
         out[name] = best
         log(f"  {name}: {best['GBps']} GB/s (vectors per thread, threads, per CU, XCD run: "
             f"{best['shape']})")
-    c4 = CALIB_COPY_BYTES // 4
-    assert 2 * c4 <= whole.numel()
-    src, dst = whole[:c4], whole[c4:2 * c4]
-    ms = time_launches(torch, lambda: F.stream_copy(src, dst, stream=stream), stream, reps=10)
-    out["copy_plain"] = {"GBps": round(2 * CALIB_COPY_BYTES / (ms / 1e3) / 1e9, 1),
-                         "kernel": "fsdpshard_stream_copy (the counters' calibration kernel)"}
     # If a channel could only read at the pure-read rate and write at the pure-write rate, one
     # after the other, the step's bytes would need at least this long.
     t = read_bytes / (out["read"]["GBps"] * 1e9) + write_bytes / (out["write"]["GBps"] * 1e9)
@@ -622,7 +616,7 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=2 
         "read_bytes": read_bytes, "write_bytes": write_bytes,
         "meaning": "the step's read and write bytes at the pure-read and pure-write rates, one "
                    "after the other"}
-    del bufs, A, B, C, sink, src, dst, whole
+    del bufs, A, B, C, sink, whole
     torch.cuda.empty_cache()
     return out
 
@@ -695,6 +689,9 @@ def main():
                     help="skip the traffic replicas and the memory-system references")
     ap.add_argument("--no-extra-workloads", action="store_true",
                     help="time only the selected workload")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the memory-system references (the plain copy that calibrates the "
+                         "hardware counters still runs)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     # One measurement of the default run in a process of its own: "ceiling", or
@@ -784,8 +781,15 @@ def main():
     # sees.
     ceiling = None
     if not args.no_copy_reference:
-        log("memory-system references:")
-        ceiling = run_child(args, "ceiling")
+        # The counters' calibration copy runs in this process, beside the measured kernel.
+        calib = copy_reference(F, torch, dev, stream)
+        torch.cuda.empty_cache()
+        ceiling = {}
+        if not args.no_ceiling:
+            log("memory-system references:")
+            ceiling = run_child(args, "ceiling")
+        ceiling["copy_plain"] = dict(calib, kernel="fsdpshard_stream_copy (the counters' "
+                                                   "calibration kernel)")
 
     extra = None
     if args.path == "fused" and not args.no_extra_workloads:
