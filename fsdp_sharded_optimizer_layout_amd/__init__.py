@@ -103,6 +103,9 @@ def lib():
     h.grads_to_interleaved.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, c_vp, c_vp]
     h.grad_sumsq_shard_interleaved.argtypes = [c_vp, c_i32, c_i64, c_vp, c_i32, ctypes.c_float,
                                                c_vp, c_i64, c_vp, c_vp]
+    h.reduce_shard_interleaved.argtypes = [c_vp, c_i32, c_i64, ctypes.c_float, c_vp, c_i32, c_vp]
+    h.reduce_shard_sumsq_interleaved.argtypes = [c_vp, c_i32, c_i64, ctypes.c_float, c_vp, c_i32,
+                                                 c_vp, c_i32, c_vp, c_i64, c_vp, c_vp]
     h.state_to_blocked.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_vp]
     h.state_from_blocked.argtypes = [c_vp, c_i64, c_vp, c_vp, c_vp, c_vp]
     h.reduce_shard_accumulate.argtypes = [ctypes.POINTER(c_vp), c_i32, c_i64, ctypes.c_float,
@@ -139,7 +142,8 @@ def lib():
                  "fsdpshard_stream_mix_shaped", "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
                  "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
                  "adamw_shard_step_interleaved", "grads_to_interleaved",
-                 "grad_sumsq_shard_interleaved",
+                 "grad_sumsq_shard_interleaved", "reduce_shard_interleaved",
+                 "reduce_shard_sumsq_interleaved",
                  "state_to_blocked", "state_from_blocked"):
         getattr(h, name).restype = ctypes.c_int
     _lib_handle = h
@@ -440,6 +444,19 @@ def reduce_shard_accumulate(contribs, acc, scale=1.0, n=None, stream=None):
         _ptr(acc, "acc", {torch.float32}, n), _stream(stream, acc)))
 
 
+def reduce_shard_interleaved(grads, fan_in, out, accumulate=False, scale=1.0, n=None,
+                             stream=None):
+    """reduce_shard (or, with ``accumulate``, reduce_shard_accumulate into ``out``) of fan_in
+    contributions held in the interleaved array ``grads``."""
+    import torch
+    n = out.numel() if n is None else int(n)
+    fan_in = int(fan_in)
+    _check("reduce_shard_interleaved", lib().reduce_shard_interleaved(
+        _ptr(grads, "grads", _bf16_dtypes(), grads_interleaved_elems(fan_in, n)), fan_in, n,
+        float(scale), _ptr(out, "out", {torch.float32}, n), 1 if accumulate else 0,
+        _stream(stream, out)))
+
+
 def grad_sumsq_workspace_bytes(n):
     return int(lib().grad_sumsq_workspace_bytes(int(n)))
 
@@ -525,6 +542,23 @@ def reduce_shard_sumsq(contribs, out, sumsq, accumulate=False, scale=1.0, n=None
     _check("reduce_shard_sumsq", lib().reduce_shard_sumsq(
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), n, float(scale),
         _ptr(out, "out", {torch.float32}, n), 1 if accumulate else 0,
+        _segs(segs, n_segments), int(n_segments), _ptr(workspace, "workspace"), wbytes,
+        _ptr(sumsq, "sumsq", {torch.float64}, 1), _stream(stream, out)))
+
+
+def reduce_shard_sumsq_interleaved(grads, fan_in, out, sumsq, accumulate=False, scale=1.0, n=None,
+                                   segs=None, n_segments=0, workspace=None, stream=None):
+    """reduce_shard_sumsq of fan_in contributions held in the interleaved array ``grads``."""
+    import torch
+    n = out.numel() if n is None else int(n)
+    fan_in = int(fan_in)
+    need = grad_sumsq_workspace_bytes(n)
+    if workspace is None:
+        workspace = _call_workspace(need, sumsq.device, stream)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check("reduce_shard_sumsq_interleaved", lib().reduce_shard_sumsq_interleaved(
+        _ptr(grads, "grads", _bf16_dtypes(), grads_interleaved_elems(fan_in, n)), fan_in, n,
+        float(scale), _ptr(out, "out", {torch.float32}, n), 1 if accumulate else 0,
         _segs(segs, n_segments), int(n_segments), _ptr(workspace, "workspace"), wbytes,
         _ptr(sumsq, "sumsq", {torch.float64}, 1), _stream(stream, out)))
 

@@ -889,8 +889,8 @@ struct ReduceSqParams {
     float scale;
 };
 
-template <int F, bool ACC>
-__global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) {
+template <int F, bool ACC, bool GIL>
+__device__ __forceinline__ void reduce_sumsq_body(ReduceSqParams p) {
     __shared__ double wave_part[kWavesPerBlock];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
@@ -910,7 +910,7 @@ __global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) 
                 auto issue = [&](int slot, int g0) {
                     const int64_t e0 = (base0 + g0 * kWave + lane) * kVec;
 #pragma unroll
-                    for (int r = 0; r < F; ++r) raw[slot][r] = ld_u4_nt(p.contrib[r] + e0);
+                    for (int r = 0; r < F; ++r) raw[slot][r] = ld_u4_nt(grad_src<F, GIL>(p, r, e0));
                     if constexpr (ACC) load8(p.out + e0, true, kVec, acc[slot]);
                 };
                 auto finish = [&](int slot, int g0) {
@@ -950,7 +950,7 @@ __global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) 
                     float acc[kVec];
                     if constexpr (ACC) load8(p.out + e0, true, kVec, acc);
 #pragma unroll
-                    for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
+                    for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(grad_src<F, GIL>(p, r, e0));
                     float g[kVec];
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) g[e] = 0.0f;
@@ -982,8 +982,8 @@ __global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) 
                     float acc[kVec];
                     if constexpr (ACC) load8(p.out + e0, full, cnt, acc);
                     for (int r = 0; r < p.fan_in; ++r) {
-                        const uint4 q = full ? ld_u4_nt(p.contrib[r] + e0)
-                                             : ld_u4_partial(p.contrib[r] + e0, cnt);
+                        const uint16_t* src = grad_src<0, GIL>(p, r, e0);
+                        const uint4 q = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
                         accumulate(g, q);
                     }
 #pragma unroll
@@ -1008,6 +1008,17 @@ __global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) 
     }
 }
 
+template <int F, bool ACC>
+__global__ __launch_bounds__(kBlock) void reduce_sumsq_kernel(ReduceSqParams p) {
+    reduce_sumsq_body<F, ACC, false>(p);
+}
+
+// The F contributions interleaved per 512-element block in one array (grad_src).
+template <int F, bool ACC>
+__global__ __launch_bounds__(kBlock) void reduce_sumsq_interleaved_kernel(ReduceSqParams p) {
+    reduce_sumsq_body<F, ACC, true>(p);
+}
+
 // ------------------------------------------------------------------------------------------------
 // Standalone reduce and unflatten: one 512-element group per wave.
 
@@ -1024,8 +1035,8 @@ constexpr int reduce_groups() { return F >= 8 && !ACC ? 2 : 1; }
 // micro-batches; one rounding for the sum, one for the scale, one for the addition).
 // F >= 1 is a compile-time fan-in, F == 0 the run-time one; each wave owns reduce_groups<F, ACC>()
 // consecutive groups, and a complete tile issues all its loads before the first add.
-template <int F, bool ACC>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
+template <int F, bool ACC, bool GIL>
+__device__ __forceinline__ void reduce_body(ReduceParams p) {
     constexpr int U = reduce_groups<F, ACC>();
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
@@ -1041,7 +1052,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
                 const int64_t e0 = (base0 + u * kWave + lane) * kVec;
                 if constexpr (ACC) load8(p.out + e0, true, kVec, acc[u]);
 #pragma unroll
-                for (int r = 0; r < F; ++r) raw[u][r] = ld_u4_nt(p.contrib[r] + e0);
+                for (int r = 0; r < F; ++r) raw[u][r] = ld_u4_nt(grad_src<F, GIL>(p, r, e0));
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -1087,7 +1098,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (r0 + q < p.fan_in) {
-                    const uint16_t* src = p.contrib[r0 + q] + e0;
+                    const uint16_t* src = grad_src<0, GIL>(p, r0 + q, e0);
                     q4[q] = full ? ld_u4_nt(src) : ld_u4_partial(src, cnt);
                 }
             }
@@ -1102,6 +1113,17 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
         }
         store8(p.out + e0, full, cnt, g);
     }
+}
+
+template <int F, bool ACC>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
+    reduce_body<F, ACC, false>(p);
+}
+
+// The F contributions interleaved per 512-element block in one array (grad_src).
+template <int F, bool ACC>
+__global__ __launch_bounds__(kBlock) void reduce_interleaved_kernel(ReduceParams p) {
+    reduce_body<F, ACC, true>(p);
 }
 
 __global__ __launch_bounds__(kBlock) void unflatten_kernel(UnflattenParams p) {
@@ -1384,29 +1406,66 @@ int launch_step(float* master, float* m, float* v, const uint16_t* const* contri
     return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in, blocks));
 }
 
+// The gradient source of the reductions: F separate arrays, or (`interleaved` non-null) the F
+// contributions in that one interleaved array.  Checks it as the step does; `elems` receives the
+// interleaved array's length.
+int check_grad_source(const uint16_t* const* contribs, const uint16_t* interleaved,
+                      int32_t fan_in, int64_t n, int64_t* elems) {
+    *elems = 0;
+    if (interleaved == nullptr) return check_contribs(contribs, fan_in);
+    if (fan_in < 1) return FSDPSHARD_ERR_INVALID_ARG;
+    if (fan_in > FSDPSHARD_MAX_FAN_IN) return FSDPSHARD_ERR_UNSUPPORTED;
+    if (!aligned16(interleaved)) return FSDPSHARD_ERR_ALIGNMENT;
+    *elems = interleaved_elems(fan_in, n);
+    return *elems < 0 ? FSDPSHARD_ERR_OVERFLOW : FSDPSHARD_OK;
+}
+
+// Whether a written buffer overlaps the gradient source (n elements per separate array).
+bool overlaps_grad_source(const void* w, int64_t wbytes, const uint16_t* const* contribs,
+                          const uint16_t* interleaved, int32_t fan_in, int64_t n,
+                          int64_t il_elems) {
+    if (interleaved != nullptr) return overlaps(w, wbytes, interleaved, il_elems * 2);
+    for (int r = 0; r < fan_in; ++r)
+        if (overlaps(w, wbytes, contribs[r], n * 2)) return true;
+    return false;
+}
+
+template <int F>
+const void* reduce_kernel_for(bool accumulate, bool interleaved) {
+    if (interleaved)
+        return accumulate ? reinterpret_cast<const void*>(&reduce_interleaved_kernel<F, true>)
+                          : reinterpret_cast<const void*>(&reduce_interleaved_kernel<F, false>);
+    return accumulate ? reinterpret_cast<const void*>(&reduce_kernel<F, true>)
+                      : reinterpret_cast<const void*>(&reduce_kernel<F, false>);
+}
+
 int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, float scale,
-                  float* out, bool accumulate, void* stream) {
+                  float* out, bool accumulate, void* stream,
+                  const uint16_t* interleaved = nullptr) {
     if (out == nullptr || n < 0) return FSDPSHARD_ERR_INVALID_ARG;
-    int rc = check_contribs(contribs, fan_in);
+    int64_t il_elems = 0;
+    int rc = check_grad_source(contribs, interleaved, fan_in, n, &il_elems);
     if (rc != FSDPSHARD_OK) return rc;
     if (!aligned16(out)) return FSDPSHARD_ERR_ALIGNMENT;
     if (n > INT64_MAX / 4) return FSDPSHARD_ERR_OVERFLOW;
-    for (int r = 0; r < fan_in && n > 0; ++r)
-        if (overlaps(out, n * 4, contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+    if (n > 0 && overlaps_grad_source(out, n * 4, contribs, interleaved, fan_in, n, il_elems))
+        return FSDPSHARD_ERR_INVALID_ARG;
     if (n == 0) return FSDPSHARD_OK;
     ReduceParams p;
-    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
+        p.contrib[r] = (interleaved == nullptr && r < fan_in) ? contribs[r] : nullptr;
+    if (interleaved != nullptr) p.contrib[0] = interleaved;
     p.out = out;
     p.n = n;
     p.fan_in = fan_in;
     p.scale = scale;
+    const bool il = interleaved != nullptr;
     const void* k = nullptr;
     int groups = 1;
     switch (fan_in) {
 #define FSDPSHARD_REDUCE_CASE(FI)                                                               \
     case FI:                                                                                    \
-        k = accumulate ? reinterpret_cast<const void*>(&reduce_kernel<FI, true>)               \
-                       : reinterpret_cast<const void*>(&reduce_kernel<FI, false>);             \
+        k = reduce_kernel_for<FI>(accumulate, il);                                              \
         groups = accumulate ? reduce_groups<FI, true>() : reduce_groups<FI, false>();          \
         break;
         FSDPSHARD_REDUCE_CASE(1)
@@ -1415,8 +1474,7 @@ int launch_reduce(const uint16_t* const* contribs, int32_t fan_in, int64_t n, fl
         FSDPSHARD_REDUCE_CASE(8)
 #undef FSDPSHARD_REDUCE_CASE
         default:
-            k = accumulate ? reinterpret_cast<const void*>(&reduce_kernel<0, true>)
-                           : reinterpret_cast<const void*>(&reduce_kernel<0, false>);
+            k = reduce_kernel_for<0>(accumulate, il);
             groups = accumulate ? reduce_groups<0, true>() : reduce_groups<0, false>();
     }
     unsigned blocks = 0;
@@ -1561,6 +1619,13 @@ extern "C" int reduce_shard(const uint16_t* const* contribs, int32_t fan_in, int
 extern "C" int reduce_shard_accumulate(const uint16_t* const* contribs, int32_t fan_in,
                                        int64_t n, float scale, float* acc, void* stream) {
     return launch_reduce(contribs, fan_in, n, scale, acc, true, stream);
+}
+
+extern "C" int reduce_shard_interleaved(const uint16_t* grads, int32_t fan_in, int64_t n,
+                                       float scale, float* out, int32_t accumulate,
+                                       void* stream) {
+    if (grads == nullptr || (accumulate != 0 && accumulate != 1)) return FSDPSHARD_ERR_INVALID_ARG;
+    return launch_reduce(nullptr, fan_in, n, scale, out, accumulate != 0, stream, grads);
 }
 
 extern "C" int64_t grad_sumsq_workspace_bytes(int64_t n) {
@@ -1777,15 +1842,28 @@ extern "C" int grad_sumsq_shard_noalloc(const uint16_t* const* contribs, int32_t
                         stream);
 }
 
-extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
-                                 float scale, float* out, int32_t accumulate,
-                                 const fsdpshard_segment* segs, int32_t n_segments,
-                                 void* workspace, int64_t workspace_bytes, double* sumsq,
-                                 void* stream) {
+namespace {
+
+template <int F>
+const void* reduce_sq_kernel_for(bool acc, bool interleaved) {
+    if (interleaved)
+        return acc ? reinterpret_cast<const void*>(&reduce_sumsq_interleaved_kernel<F, true>)
+                   : reinterpret_cast<const void*>(&reduce_sumsq_interleaved_kernel<F, false>);
+    return acc ? reinterpret_cast<const void*>(&reduce_sumsq_kernel<F, true>)
+               : reinterpret_cast<const void*>(&reduce_sumsq_kernel<F, false>);
+}
+
+// reduce_shard_sumsq from F separate arrays, or from the interleaved array when `interleaved`
+// is non-null (contribs unused).
+int launch_reduce_sumsq(const uint16_t* const* contribs, const uint16_t* interleaved,
+                        int32_t fan_in, int64_t n, float scale, float* out, int32_t accumulate,
+                        const fsdpshard_segment* segs, int32_t n_segments, void* workspace,
+                        int64_t workspace_bytes, double* sumsq, void* stream) {
     if (out == nullptr || n < 0 || sumsq == nullptr || n_segments < 0 ||
         (n_segments > 0 && segs == nullptr) || (accumulate != 0 && accumulate != 1))
         return FSDPSHARD_ERR_INVALID_ARG;
-    int rc = check_contribs(contribs, fan_in);
+    int64_t il_elems = 0;
+    int rc = check_grad_source(contribs, interleaved, fan_in, n, &il_elems);
     if (rc != FSDPSHARD_OK) return rc;
     if (!aligned16(out)) return FSDPSHARD_ERR_ALIGNMENT;
     if (!aligned8(sumsq)) return FSDPSHARD_ERR_ALIGNMENT;
@@ -1803,12 +1881,14 @@ extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_i
     for (int i = 0; i < 3; ++i) {
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(wr[i], wb[i], wr[j], wb[j])) return FSDPSHARD_ERR_INVALID_ARG;
-        for (int r = 0; r < fan_in && n > 0; ++r)
-            if (overlaps(wr[i], wb[i], contribs[r], n * 2)) return FSDPSHARD_ERR_INVALID_ARG;
+        if (n > 0 && overlaps_grad_source(wr[i], wb[i], contribs, interleaved, fan_in, n, il_elems))
+            return FSDPSHARD_ERR_INVALID_ARG;
         if (overlaps(wr[i], wb[i], segs, sb)) return FSDPSHARD_ERR_INVALID_ARG;
     }
     ReduceSqParams p;
-    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r) p.contrib[r] = r < fan_in ? contribs[r] : nullptr;
+    for (int r = 0; r < FSDPSHARD_MAX_FAN_IN; ++r)
+        p.contrib[r] = (interleaved == nullptr && r < fan_in) ? contribs[r] : nullptr;
+    if (interleaved != nullptr) p.contrib[0] = interleaved;
     p.out = out;
     p.segs = segs;
     p.partials = static_cast<double*>(workspace);
@@ -1818,13 +1898,13 @@ extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_i
     p.scale = scale;
     if (parts > 0) {
         const bool acc = accumulate != 0;
+        const bool il = interleaved != nullptr;
         const void* k = nullptr;
         bool pipelined = false;
         switch (fan_in) {
 #define FSDPSHARD_REDUCE_SQ_CASE(FI)                                                            \
     case FI:                                                                                    \
-        k = acc ? reinterpret_cast<const void*>(&reduce_sumsq_kernel<FI, true>)                \
-                : reinterpret_cast<const void*>(&reduce_sumsq_kernel<FI, false>);              \
+        k = reduce_sq_kernel_for<FI>(acc, il);                                                  \
         pipelined = acc ? reduce_sq_pipelined<FI, true>() : reduce_sq_pipelined<FI, false>();   \
         break;
             FSDPSHARD_REDUCE_SQ_CASE(1)
@@ -1833,8 +1913,7 @@ extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_i
             FSDPSHARD_REDUCE_SQ_CASE(8)
 #undef FSDPSHARD_REDUCE_SQ_CASE
             default:
-                k = acc ? reinterpret_cast<const void*>(&reduce_sumsq_kernel<0, true>)
-                        : reinterpret_cast<const void*>(&reduce_sumsq_kernel<0, false>);
+                k = reduce_sq_kernel_for<0>(acc, il);
         }
         rc = launch(k, static_cast<unsigned>(parts), &p, stream,
                     pipelined                ? kReduceSqPipelinedGroupsPerCU
@@ -1856,6 +1935,27 @@ extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_i
     f.scale = 1.0f;
     // One work-group adds the partials (or writes +0 for an empty slice).
     return launch(reinterpret_cast<const void*>(&sumsq_finish_kernel), 1, &f, stream);
+}
+
+}  // namespace
+
+extern "C" int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_in, int64_t n,
+                                 float scale, float* out, int32_t accumulate,
+                                 const fsdpshard_segment* segs, int32_t n_segments,
+                                 void* workspace, int64_t workspace_bytes, double* sumsq,
+                                 void* stream) {
+    return launch_reduce_sumsq(contribs, nullptr, fan_in, n, scale, out, accumulate, segs,
+                               n_segments, workspace, workspace_bytes, sumsq, stream);
+}
+
+extern "C" int reduce_shard_sumsq_interleaved(const uint16_t* grads, int32_t fan_in, int64_t n,
+                                             float scale, float* out, int32_t accumulate,
+                                             const fsdpshard_segment* segs, int32_t n_segments,
+                                             void* workspace, int64_t workspace_bytes,
+                                             double* sumsq, void* stream) {
+    if (grads == nullptr) return FSDPSHARD_ERR_INVALID_ARG;
+    return launch_reduce_sumsq(nullptr, grads, fan_in, n, scale, out, accumulate, segs,
+                               n_segments, workspace, workspace_bytes, sumsq, stream);
 }
 
 extern "C" int unflatten_bf16(const float* master, int64_t n, const fsdpshard_segment* segs,

@@ -281,6 +281,19 @@ int reduce_shard_accumulate(const uint16_t* const* contribs, int32_t fan_in, int
                             float scale, float* acc, void* stream);
 
 /*
+ * reduce_shard_interleaved -- reduce_shard (accumulate = 0) or reduce_shard_accumulate
+ * (accumulate = 1, `out` is the accumulator) of fan_in contributions held in the interleaved
+ * layout (see grads_interleaved_elems); the results are bit-identical to those calls on the same
+ * contributions.
+ *   grads  device, grads_interleaved_elems(fan_in, n) bf16 bit patterns, 16-byte aligned; it
+ *          must not overlap `out`
+ * Errors: those of reduce_shard; INVALID_ARG also for accumulate other than 0 or 1; OVERFLOW
+ * also when the gradient array's size in bytes does not fit int64.
+ */
+int reduce_shard_interleaved(const uint16_t* grads, int32_t fan_in, int64_t n, float scale,
+                             float* out, int32_t accumulate, void* stream);
+
+/*
  * grad_sumsq_workspace_bytes -- device workspace grad_sumsq_shard needs for an n-element slice
  * (8 bytes per 32,768 elements, rounded up); -1 for n < 0.
  */
@@ -385,6 +398,16 @@ int reduce_shard_sumsq(const uint16_t* const* contribs, int32_t fan_in, int64_t 
                        float* out, int32_t accumulate, const fsdpshard_segment* segs,
                        int32_t n_segments, void* workspace, int64_t workspace_bytes, double* sumsq,
                        void* stream);
+
+/*
+ * reduce_shard_sumsq_interleaved -- reduce_shard_sumsq of fan_in contributions held in the
+ * interleaved layout: bit-identical results.  `grads` as for reduce_shard_interleaved; every
+ * other argument and error as for reduce_shard_sumsq.
+ */
+int reduce_shard_sumsq_interleaved(const uint16_t* grads, int32_t fan_in, int64_t n, float scale,
+                                   float* out, int32_t accumulate, const fsdpshard_segment* segs,
+                                   int32_t n_segments, void* workspace, int64_t workspace_bytes,
+                                   double* sumsq, void* stream);
 
 /*
  * One piece of a reshard plan: `length` elements that land at `dst_offset` of the destination

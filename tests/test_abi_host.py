@@ -249,6 +249,29 @@ def test_interleaved_validation_errors():
     assert sq(gi, 8, n, ws=gi + 16384 - 8) == INVALID          # workspace over the grads' end
     assert sq(gi, 8, n, res=gi + 8192) == INVALID              # sum inside the grads
     assert sq(gi, 8, n, segs=_Fake.at(7), nseg=1) == INVALID     # table over the workspace
+    red = lambda grads, fan_in, n, out=_Fake.at(9), acc=0: \
+        lib.reduce_shard_interleaved(grads, fan_in, n, 1.0, out, acc, None)
+    assert red(gi, 8, 0) == OK
+    assert red(None, 8, 0) == INVALID
+    assert red(gi, 8, 0, out=None) == INVALID
+    assert red(gi, 0, 0) == INVALID
+    assert red(gi, 65, 0) == UNSUP
+    assert red(gi + 8, 8, 0) == ALIGN
+    assert red(gi, 8, 0, out=_Fake.at(9, 8)) == ALIGN
+    assert red(gi, 8, 0, acc=2) == INVALID
+    assert red(gi, 64, 2 ** 59) == OVERFLOW
+    assert red(gi, 8, n, out=gi + 16384 - 16) == INVALID            # out over the grads' end
+    rsq = lambda grads, fan_in, n, out=_Fake.at(9), ws=_Fake.at(7), wsb=1 << 20, res=_Fake.at(8): \
+        lib.reduce_shard_sumsq_interleaved(grads, fan_in, n, 1.0, out, 0, None, 0, ws, wsb, res,
+                                           None)
+    assert rsq(None, 8, 0) == INVALID
+    assert rsq(gi, 65, 0) == UNSUP
+    assert rsq(gi + 8, 8, 0) == ALIGN
+    assert rsq(gi, 64, 2 ** 59) == OVERFLOW
+    assert rsq(gi, 8, n, wsb=0) == CAPACITY
+    assert rsq(gi, 8, n, out=gi + 16384 - 16) == INVALID            # out over the grads' end
+    assert rsq(gi, 8, n, ws=gi + 8) == INVALID                      # workspace inside the grads
+    assert rsq(gi, 8, n, res=gi + 64) == INVALID                    # sum inside the grads
 
 
 def test_reduce_and_unflatten_validation_errors():

@@ -10,6 +10,9 @@
   for bit equal to grad_sumsq_shard on the separate contributions (whole tiles, ragged tails,
   padding inside whole tiles, compile-time and run-time fan-ins); the clipped cases of the step
   take their norm from it;
+* reduce_shard_interleaved and reduce_shard_sumsq_interleaved (plain and accumulating) bit for
+  bit equal to the oracle's reduction and to the separate-array calls, the fused sum within
+  relative 1e-12 of the oracle's exact sum and equal to the separate-array one;
 * a ragged slice whose interleaved offsets pass 2^31 elements, and the 7B-shaped slice at full
   size: interleaved steps and sums equal the separate-contribution ones bit for bit.
 """
@@ -167,6 +170,73 @@ def test_interleaved_sumsq_padding_inside_whole_tiles(F_in):
     assert abs(float(got_t.item()) - want) <= SUMSQ_RTOL * want
 
 
+RED_CASES = [(1, 1, False), (7, 3, True), (4099, 8, False), (32769, 8, True), (65539, 2, True),
+             (300_017, 5, False), (1_000_003, 4, True), (300_017, 8, True), (98_304, 4, False),
+             (70_001, 16, True)]
+
+
+@pytest.mark.parametrize("n,F_in,acc", RED_CASES)
+def test_interleaved_reductions_match_oracle_and_separate(n, F_in, acc):
+    say(f"interleaved reduce n={n} F={F_in} accumulate={acc}")
+    contribs = [W.np_bf16_normal([72, F_in, r], n, 1e-2) for r in range(F_in)]
+    dev = [to_dev16(c) for c in contribs]
+    gi = Guarded(BL.to_interleaved(contribs, fill=SENT16))
+    acc0 = W.np_f32_normal([73, n], n, 1e-3) if acc else np.full(n, np.nan, np.float32)
+    want = OS.accumulate_fp32(acc0, contribs, 0.5) if acc else OS.reduce_contributions(contribs, 0.5)
+    # the plain and the accumulating reduction
+    out_i, out_s = Guarded(acc0), Guarded(acc0)
+    F.reduce_shard_interleaved(gi.data(), F_in, out_i.data(), accumulate=acc, scale=0.5)
+    if acc:
+        F.reduce_shard_accumulate(dev, out_s.data(), scale=0.5)
+    else:
+        F.reduce_shard(dev, out_s.data(), scale=0.5)
+    torch.cuda.synchronize()
+    assert bit_equal(out_i.data_host(), want)
+    assert bit_equal(out_i.data_host(), out_s.data_host())
+    out_i.assert_guards("out")
+    # fused with the sum of squares
+    sq_out_i, sq_out_s = Guarded(acc0), Guarded(acc0)
+    res_i = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    res_s = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    F.reduce_shard_sumsq_interleaved(gi.data(), F_in, sq_out_i.data(), res_i, accumulate=acc,
+                                     scale=0.5)
+    F.reduce_shard_sumsq(dev, sq_out_s.data(), res_s, accumulate=acc, scale=0.5)
+    torch.cuda.synchronize()
+    assert bit_equal(sq_out_i.data_host(), want)
+    sq_out_i.assert_guards("out")
+    got, sep = float(res_i.item()), float(res_s.item())
+    osum = OC.sumsq_exact(want)
+    assert got == sep, (got, sep)
+    assert abs(got - osum) <= SUMSQ_RTOL * osum, (got, osum)
+    assert np.array_equal(gi.data_host(), BL.to_interleaved(contribs, fill=SENT16))
+    gi.assert_guards("interleaved gradients")
+
+
+@pytest.mark.parametrize("F_in,acc", [(8, False), (8, True), (4, True), (1, False), (3, True)])
+def test_interleaved_reduce_sumsq_padding_inside_whole_tiles(F_in, acc):
+    sizes = [(i * 7919) % 3001 + 1 for i in range(300)]
+    L, segs, flags = _layout(sizes, 16, None, 2, 1)
+    n = L.n
+    real = (flags & OL.PADDING) == 0
+    say(f"interleaved reduce+sumsq padded tiles F={F_in} accumulate={acc} n={n}")
+    contribs = [W.np_bf16_normal([76, F_in, r], n, 1e-2) for r in range(F_in)]
+    for c in contribs:
+        c[~real] = 0x7FC0
+    acc0 = W.np_f32_normal([77, n], n, 1e-3) if acc else np.zeros(n, np.float32)
+    out = Guarded(acc0)
+    res = torch.zeros(1, dtype=torch.float64, device="cuda")
+    F.reduce_shard_sumsq_interleaved(to_dev16(BL.to_interleaved(contribs)), F_in, out.data(), res,
+                                     accumulate=acc, scale=0.25, segs=F.segments_to_device(segs),
+                                     n_segments=L.n_segments)
+    torch.cuda.synchronize()
+    want = (OS.accumulate_fp32(acc0, contribs, 0.25) if acc
+            else OS.reduce_contributions(contribs, 0.25))
+    assert bit_equal(out.data_host()[real], want[real])
+    osum = OC.sumsq_exact(want, real)
+    got = float(res.item())
+    assert abs(got - osum) <= SUMSQ_RTOL * osum, (got, osum)
+
+
 def _bf16_like(n, gen, std):
     return (torch.randn(n, generator=gen, device="cuda") * std).to(torch.bfloat16).view(torch.int16)
 
@@ -200,6 +270,15 @@ def _interleaved_equals_blocked(n, fan_in, segs_dev, n_segments, hp, state0_seed
         assert torch.equal(st_i.view(torch.int32), st_b.view(torch.int32)), f"state step {t}"
         assert torch.equal(flat_i, flat_b), f"bf16 step {t}"
         assert float(sq_i.item()) == float(sq_b.item()), f"sum of squares step {t}"
+    red_i = torch.empty(n, dtype=torch.float32, device="cuda")
+    red_b = torch.empty(n, dtype=torch.float32, device="cuda")
+    F.reduce_shard_interleaved(gi, fan_in, red_i, n=n)
+    F.reduce_shard(grads, red_b, n=n)
+    F.reduce_shard_interleaved(gi, fan_in, red_i, accumulate=True, scale=0.5, n=n)
+    F.reduce_shard_accumulate(grads, red_b, scale=0.5, n=n)
+    torch.cuda.synchronize()
+    assert torch.equal(red_i.view(torch.int32), red_b.view(torch.int32)), "reduction"
+    del red_i, red_b
         say(f"  step {t} ok")
     del st_i, st_b, grads, gi, flat_i, flat_b
     torch.cuda.empty_cache()
@@ -207,8 +286,9 @@ def _interleaved_equals_blocked(n, fan_in, segs_dev, n_segments, hp, state0_seed
 
 def test_interleaved_offsets_beyond_2_31():
     """Fan-in 8 on a ragged slice of 2^28 + 123 elements: the interleaved array holds
-    8 * (2^28 + 512) elements, so its offsets pass 2^31; the conversion and two steps equal the
-    blocked step on the separate contributions bit for bit over the whole slice."""
+    8 * (2^28 + 512) elements, so its offsets pass 2^31; the conversion, two steps, their sums
+    of squares and a plain and an accumulating reduction equal the separate-contribution calls
+    bit for bit over the whole slice."""
     n = (1 << 28) + 123
     say(f"interleaved offsets beyond 2^31: n={n}")
     assert F.grads_interleaved_elems(8, n) > (1 << 31)
