@@ -270,6 +270,8 @@ def _interleaved_equals_blocked(n, fan_in, segs_dev, n_segments, hp, state0_seed
         assert torch.equal(st_i.view(torch.int32), st_b.view(torch.int32)), f"state step {t}"
         assert torch.equal(flat_i, flat_b), f"bf16 step {t}"
         assert float(sq_i.item()) == float(sq_b.item()), f"sum of squares step {t}"
+        say(f"  step {t} ok")
+    del st_i, st_b, flat_i, flat_b
     red_i = torch.empty(n, dtype=torch.float32, device="cuda")
     red_b = torch.empty(n, dtype=torch.float32, device="cuda")
     F.reduce_shard_interleaved(gi, fan_in, red_i, n=n)
@@ -278,9 +280,7 @@ def _interleaved_equals_blocked(n, fan_in, segs_dev, n_segments, hp, state0_seed
     F.reduce_shard_accumulate(grads, red_b, scale=0.5, n=n)
     torch.cuda.synchronize()
     assert torch.equal(red_i.view(torch.int32), red_b.view(torch.int32)), "reduction"
-    del red_i, red_b
-        say(f"  step {t} ok")
-    del st_i, st_b, grads, gi, flat_i, flat_b
+    del red_i, red_b, grads, gi
     torch.cuda.empty_cache()
 
 
