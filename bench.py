@@ -364,8 +364,10 @@ def build_stages(F, torch, S, path, stream, args):
     common = S.common(stream)
     stages = []
     suffix = {"blocked": "_blocked", "separate": "", "interleaved": "_interleaved"}[S.layout]
-    if S.layout == "interleaved" and path != "fused":
-        raise ValueError("the interleaved contributions feed the fused step only (--path fused)")
+    f32_suffix = "" if S.layout == "separate" else "_blocked"
+    il = S.gi is not None
+    if il and path == "split":
+        raise ValueError("the split path reads separate contributions")
     if path == "fused":
         stages.append(("adamw_shard_step" + suffix, lambda t: S.step_bf16(F, t, **common),
                        L.n_real * bpp))
@@ -382,33 +384,44 @@ def build_stages(F, torch, S, path, stream, args):
         segkw = dict(segs=S.segs_dev, n_segments=L.n_segments, workspace=ws, stream=stream)
         clip = dict(max_grad_norm=args.max_grad_norm, grad_sumsq=sumsq)
         f32_bytes = L.n_real * algorithmic_bytes_per_param_f32grad()
+        # The contributions' calls: from F arrays, or from the interleaved array.
+        if il:
+            sumsq_bf16 = lambda: F.grad_sumsq_shard_interleaved(sumsq, S.gi, Fi, n, **segkw)
+            red = lambda acc, a: F.reduce_shard_interleaved(S.gi, Fi, acc, accumulate=a,
+                                                            stream=stream)
+            red_sq = lambda acc, a: F.reduce_shard_sumsq_interleaved(S.gi, Fi, acc, sumsq,
+                                                                     accumulate=a, **segkw)
+        else:
+            sumsq_bf16 = lambda: F.grad_sumsq_shard(sumsq, contribs=S.grads, n=n, **segkw)
+            red = lambda acc, a: (F.reduce_shard_accumulate(S.grads, acc, stream=stream) if a
+                                  else F.reduce_shard(S.grads, acc, stream=stream))
+            red_sq = lambda acc, a: F.reduce_shard_sumsq(S.grads, acc, sumsq, accumulate=a,
+                                                         **segkw)
+        isfx = "_interleaved" if il else ""
         if path == "clipped":
-            stages.append(("grad_sumsq_shard", lambda t: F.grad_sumsq_shard(
-                sumsq, contribs=S.grads, n=n, **segkw), n * 2 * Fi))
+            stages.append(("grad_sumsq_shard" + isfx, lambda t: sumsq_bf16(), n * 2 * Fi))
             stages.append(("adamw_shard_step" + suffix + " (clipped)", lambda t: S.step_bf16(
                 F, t, **clip, **common), L.n_real * bpp))
         elif path == "clipped32":
             acc = torch.empty(n, dtype=torch.float32, device=dev)
-            stages.append(("reduce_shard_sumsq", lambda t: F.reduce_shard_sumsq(
-                S.grads, acc, sumsq, **segkw), n * (2 * Fi + 4)))
-            stages.append(("adamw_shard_step_f32grad" + suffix + " (clipped)", lambda t: S.step_f32(
-                F, acc, t, **clip, **common), f32_bytes))
+            stages.append(("reduce_shard_sumsq" + isfx, lambda t: red_sq(acc, False),
+                           n * (2 * Fi + 4)))
+            stages.append(("adamw_shard_step_f32grad" + f32_suffix + " (clipped)",
+                           lambda t: S.step_f32(F, acc, t, **clip, **common), f32_bytes))
         else:   # accumulate
             acc = torch.empty(n, dtype=torch.float32, device=dev)
-            stages.append(("reduce_shard", lambda t: F.reduce_shard(S.grads, acc, stream=stream),
-                           n * (2 * Fi + 4)))
+            stages.append(("reduce_shard" + isfx, lambda t: red(acc, False), n * (2 * Fi + 4)))
             for mb in range(1, args.micro_batches - 1):
-                stages.append((f"reduce_shard_accumulate[{mb}]", lambda t: F.reduce_shard_accumulate(
-                    S.grads, acc, stream=stream), n * (2 * Fi + 8)))
+                name = "reduce_shard_interleaved (accumulate)" if il else "reduce_shard_accumulate"
+                stages.append((f"{name}[{mb}]", lambda t: red(acc, True), n * (2 * Fi + 8)))
             if args.micro_batches > 1:
-                stages.append((f"reduce_shard_sumsq (accumulate)[{args.micro_batches - 1}]",
-                               lambda t: F.reduce_shard_sumsq(S.grads, acc, sumsq, accumulate=True,
-                                                              **segkw), n * (2 * Fi + 8)))
+                stages.append((f"reduce_shard_sumsq{isfx} (accumulate)[{args.micro_batches - 1}]",
+                               lambda t: red_sq(acc, True), n * (2 * Fi + 8)))
             else:
                 stages.append(("grad_sumsq_shard (fp32)", lambda t: F.grad_sumsq_shard(
                     sumsq, grad=acc, n=n, **segkw), n * 4))
-            stages.append(("adamw_shard_step_f32grad" + suffix + " (clipped)", lambda t: S.step_f32(
-                F, acc, t, **clip, **common), f32_bytes))
+            stages.append(("adamw_shard_step_f32grad" + f32_suffix + " (clipped)",
+                           lambda t: S.step_f32(F, acc, t, **clip, **common), f32_bytes))
     return stages
 
 
@@ -675,7 +688,7 @@ def main():
                          "separate arrays)")
     ap.add_argument("--grads", choices=["separate", "interleaved"], default="separate",
                     help="gradient contributions: F separate arrays (default), or interleaved per "
-                         "512-element block in one array (fused path, blocked state only)")
+                         "512-element block in one array (blocked state only)")
     ap.add_argument("--max-grad-norm", type=float, default=1.0)
     ap.add_argument("--evict-mb", type=int, default=-1,
                     help="MiB written between timed steps to flush the 256 MB last-level cache "
@@ -739,8 +752,9 @@ def main():
         print(json.dumps(child_measurement(args, w, F, W, torch, dev, stream)), flush=True)
         return
     blocked = args.state == "blocked" and args.path != "split"
-    if args.grads == "interleaved" and (not blocked or args.path != "fused"):
-        print("--grads interleaved needs the fused path and the blocked state", file=sys.stderr)
+    if args.grads == "interleaved" and not blocked:
+        print("--grads interleaved needs the blocked state (and not the split path)",
+              file=sys.stderr)
         sys.exit(2)
     layout = ("interleaved" if args.grads == "interleaved" else "blocked") if blocked else "separate"
     S = Slice(F, W, torch, w.name, layout, dev)
