@@ -20,7 +20,8 @@
  *     found before anything is enqueued; a launch the HIP runtime refuses (FSDPSHARD_ERR_HIP)
  *     may leave a multi-kernel call's earlier kernels enqueued.  Nothing is thrown and nothing
  *     aborts.
- *   - n == 0 is a successful no-op.
+ *   - n == 0 is a successful no-op, except that the calls with a sum of squares still write +0
+ *     into their result (one small kernel).
  */
 #ifndef FSDPSHARD_H
 #define FSDPSHARD_H
