@@ -635,15 +635,21 @@ def ceiling_references(F, torch, dev, stream, read_bytes, write_bytes, nbytes=2 
 
 
 def run_child(args, spec):
-    """One measurement (`--child spec`) in a fresh Python process on the same GPU; its record."""
+    """One measurement (`--child spec`) in a fresh Python process on the same GPU; its record, or
+    {"error": ...} if the child failed (the headline line is printed either way)."""
     cmd = [sys.executable, os.path.abspath(__file__), "--child", spec, "--workload", args.workload,
            "--steps", str(args.steps), "--warmup", str(args.warmup), "--evict-mb",
            str(args.evict_mb)]
     if args.no_copy_reference:
         cmd.append("--no-copy-reference")
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    try:
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    except subprocess.TimeoutExpired:
+        log(f"measurement {spec} timed out")
+        return {"error": "timed out"}
     if r.returncode != 0:
-        raise RuntimeError(f"measurement {spec} failed with status {r.returncode}")
+        log(f"measurement {spec} failed with status {r.returncode}")
+        return {"error": f"exit status {r.returncode}"}
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
@@ -812,8 +818,11 @@ def main():
             if name == w.name and lay == layout:
                 continue
             x = run_child(args, f"workload:{name}:{lay}")
-            log(f"workload {name} ({x['state_layout']}): {x['kernel_avg_ms']:.4f} ms, "
-                f"{x['GBps']} GB/s, frac {x['frac']}")
+            if "error" in x:
+                x = dict(x, workload=name, layout=lay)
+            else:
+                log(f"workload {name} ({x['state_layout']}): {x['kernel_avg_ms']:.4f} ms, "
+                    f"{x['GBps']} GB/s, frac {x['frac']}")
             extra.append(x)
 
     cpu = cpu_single = None

@@ -62,3 +62,22 @@ def test_cpu_baseline_legs_report_the_contract_fields():
     assert par["kind"] == "oracle" and par["cores"] == 2 and par["value"] > 0
     assert set(par["host"]) == {"os_cpu_count", "affinity", "cgroup_quota", "usable"}
     assert "2 processes" in par["sample"]
+
+
+def test_failed_child_measurement_is_recorded_not_fatal():
+    # A measurement that runs in a child process and fails (an unknown layout; without a GPU the
+    # child stops even earlier, also with status 1) comes back as an error record, so the bench
+    # still prints its line with the headline.
+    import argparse
+    args = argparse.Namespace(workload="p1000003_n8_rank3", steps=1, warmup=0, evict_mb=-1,
+                              no_copy_reference=True)
+    rec = bench.run_child(args, "workload:p1000003_n8_rank3:no_such_layout")
+    assert rec == {"error": "exit status 1"}
+
+
+def test_layout_keys():
+    assert bench.traffic_key("w") == "w"
+    assert bench.traffic_key("w", "separate") == "w:separate"
+    assert bench.traffic_key("w", "interleaved") == "w:interleaved"
+    assert set(bench.LAYOUT_DESCRIPTION) == {"blocked", "separate", "interleaved"}
+    assert all(lay in bench.LAYOUT_DESCRIPTION for _, lay in bench.EXTRA_WORKLOADS)
