@@ -520,16 +520,20 @@ def mix_references(F, torch, S, stream, evict, shapes=False):
     bpp = algorithmic_bytes_per_param(S.w.fan_in)
     out16 = (S.flat[S.phase:S.phase + n8] if S.phase == 0
              else torch.empty(n8, dtype=torch.int16, device=S.dev))
-    if S.blocked:
+    if S.gi is not None:
+        mix = lambda: F.stream_mix_interleaved(S.gi, S.w.fan_in, S.state, out16, n8,
+                                               stream=stream)
+    elif S.blocked:
         mix = lambda: F.stream_mix_blocked(S.grads, S.state, out16, n8, stream=stream)
     else:
         mix = lambda: F.stream_mix(S.grads, S.master, S.m, S.v, out16, n=n8, stream=stream)
     ms = time_launches(torch, mix, stream, evict=evict)
+    suffix = {"blocked": "_blocked", "separate": "", "interleaved": "_interleaved"}[S.layout]
     ref = {"step_order": {"GBps": round(n8 * bpp / (ms / 1e3) / 1e9, 1), "ms": round(ms, 4),
-                          "kernel": "fsdpshard_stream_mix" + ("_blocked" if S.blocked else "")},
+                          "kernel": "fsdpshard_stream_mix" + suffix},
            "flushed": evict is not None}
     best = dict(ref["step_order"], shape="the step's")
-    if shapes and S.blocked and S.w.fan_in in (1, 4, 8):
+    if shapes and S.layout == "blocked" and S.w.fan_in in (1, 4, 8):
         for G, per_cu, run, phased in MIX_SHAPES:
             ms = time_launches(torch, lambda: F.stream_mix_shaped(
                 S.grads, S.state, out16, n8, G, per_cu, run, phased, stream=stream), stream,
@@ -545,8 +549,7 @@ def mix_references(F, torch, S, stream, evict, shapes=False):
 
 def measure_workload(F, W, torch, name, layout, args, dev, stream, mix=True):
     """The fused step of one workload: its stage timing, roofline figures and (like for like,
-    flushed when the step is) the traffic replica (not for the interleaved contributions, which
-    no replica reads)."""
+    flushed when the step is) the traffic replica."""
     S = Slice(F, W, torch, name, layout, dev)
     stages = build_stages(F, torch, S, "fused", stream, args)
     evict_mb, evict = make_evict(torch, dev, stages[0][2], args.evict_mb)
@@ -565,7 +568,7 @@ def measure_workload(F, W, torch, name, layout, args, dev, stream, mix=True):
            "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
            "traffic": counter_traffic(traffic_key(name, layout)),
            "timing": r["timing"]}
-    if mix and layout != "interleaved" and not args.no_copy_reference:
+    if mix and not args.no_copy_reference:
         out["mix_reference"] = mix_references(F, torch, S, stream, evict)
     del S, evict
     torch.cuda.empty_cache()
@@ -785,7 +788,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic}
 
     mix_ref = None
-    if not args.no_copy_reference and args.path == "fused" and layout != "interleaved":
+    if not args.no_copy_reference and args.path == "fused":
         mix_ref = mix_references(F, torch, S, stream, evict, shapes=True)
         for k, x in (mix_ref or {}).items():
             if isinstance(x, dict):

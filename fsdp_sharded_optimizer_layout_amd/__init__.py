@@ -132,6 +132,7 @@ def lib():
                                                c_vp]
     h.fsdpshard_stream_rw.argtypes = [ctypes.POINTER(c_vp), c_i32, ctypes.POINTER(c_vp), c_i32,
                                       c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
+    h.fsdpshard_stream_mix_interleaved.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i64, c_vp]
     h.fsdpshard_stream_mix_shaped.argtypes = [ctypes.POINTER(c_vp), c_i32, c_vp, c_vp, c_i64,
                                               c_i32, c_i32, c_i32, c_i32, c_vp]
     for name in ("shard_layout", "reduce_shard", "adamw_shard_step", "unflatten_bf16",
@@ -139,7 +140,8 @@ def lib():
                  "reshard_plan", "reshard_copy",
                  "fsdpshard_abi_version", "fsdpshard_stream_copy", "fsdpshard_stream_rw",
                  "fsdpshard_stream_mix", "fsdpshard_stream_mix_blocked",
-                 "fsdpshard_stream_mix_shaped", "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
+                 "fsdpshard_stream_mix_shaped", "fsdpshard_stream_mix_interleaved",
+                 "reduce_shard_sumsq", "grad_sumsq_shard_noalloc",
                  "adamw_shard_step_blocked", "adamw_shard_step_f32grad_blocked",
                  "adamw_shard_step_interleaved", "grads_to_interleaved",
                  "grad_sumsq_shard_interleaved", "reduce_shard_interleaved",
@@ -623,6 +625,18 @@ def stream_mix_blocked(contribs, state, out, n, stream=None):
     _check("fsdpshard_stream_mix_blocked", lib().fsdpshard_stream_mix_blocked(
         ctypes.cast(arr, ctypes.POINTER(c_vp)), len(contribs), _ptr(state, "state"),
         _ptr(out, "out"), n, _stream(stream, state)))
+
+
+def stream_mix_interleaved(grads, fan_in, state, out, n, stream=None):
+    """Measurement aid: stream_mix_blocked fed by the fan_in contributions interleaved in one
+    array ``grads``."""
+    n, fan_in = int(n), int(fan_in)
+    _need_bytes(grads, "grads", 2 * grads_interleaved_elems(fan_in, n))
+    _need_bytes(state, "state", 4 * state_blocked_elems(n))
+    _need_bytes(out, "out", 2 * n)
+    _check("fsdpshard_stream_mix_interleaved", lib().fsdpshard_stream_mix_interleaved(
+        _ptr(grads, "grads"), fan_in, _ptr(state, "state"), _ptr(out, "out"), n,
+        _stream(stream, state)))
 
 
 def stream_mix_shaped(contribs, state, out, n, groups_per_wave, per_cu, xcd_run, phased,

@@ -10,7 +10,9 @@
 //                          threads per work-group, work-groups per CU, XCD run length).
 //   * stream_mix_kernel    the fused step's exact loads and stores (same vector width, cache
 //                          hints, tile map, load issue order and work-groups per CU) with
-//                          trivial integer arithmetic in place of the reduction and the update.
+//                          trivial integer arithmetic in place of the reduction and the update;
+//                          stream_mix_interleaved_kernel the same for the step fed by
+//                          contributions interleaved in one array.
 //   * stream_mix_shaped_kernel
 //                          the same bytes as the blocked-state step in other shapes: G groups
 //                          per wave, any work-groups per CU and XCD run, and optionally in phases
@@ -134,11 +136,24 @@ struct MixParams {
     int32_t fan_in;
 };
 
-// One 512-element group per wave, exactly as the step: F non-temporal bf16 loads, three fp32
-// read-modify-write streams (separate, or the blocked array in s[0]), one bf16 store per
-// 8-element vector.
-template <int F, bool BLK>
-__global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
+// One 512-element group per wave, exactly as the step: F non-temporal bf16 loads (from F arrays,
+// or with GIL from one array interleaved per 512-element block: contribution r's element i at
+// ((i / 512) * F + r) * 512 + i % 512), three fp32 read-modify-write streams (separate, or the
+// blocked array in s[0]), one bf16 store per 8-element vector.
+template <int F, bool BLK, bool GIL>
+__device__ __forceinline__ const uint16_t* mix_src(const MixParams& p, int r, int64_t e0) {
+    if constexpr (GIL) {
+        const uint64_t u = static_cast<uint64_t>(e0);
+        const int64_t fan_in = F > 0 ? F : p.fan_in;
+        return p.contrib[0] + (static_cast<int64_t>(u / kStateBlock) * fan_in + r) * kStateBlock +
+               static_cast<int64_t>(u % kStateBlock);
+    } else {
+        return p.contrib[r] + e0;
+    }
+}
+
+template <int F, bool BLK, bool GIL>
+__device__ __forceinline__ void stream_mix_body(MixParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int64_t vec = tile_base<kStepXcdRun>(wave, 1) + lane;
@@ -160,7 +175,7 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (F > 0) {
 #pragma unroll
-        for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(p.contrib[r] + e0);
+        for (int r = 0; r < F; ++r) raw[r] = ld_u4_nt(mix_src<F, BLK, GIL>(p, r, e0));
     }
     if constexpr (!kStateFirst) {
         __builtin_amdgcn_sched_barrier(0);
@@ -171,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
         for (int r = 0; r < F; ++r) x ^= raw[r].x ^ raw[r].y ^ raw[r].z ^ raw[r].w;
     } else {
         for (int r = 0; r < fan_in; ++r) {
-            const uint4 q = ld_u4_nt(p.contrib[r] + e0);
+            const uint4 q = ld_u4_nt(mix_src<F, BLK, GIL>(p, r, e0));
             x ^= q.x ^ q.y ^ q.z ^ q.w;
         }
     }
@@ -182,6 +197,17 @@ __global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
     }
     st_u4_nt(p.out + e0, make_uint4(__float_as_uint(st[0][1]), __float_as_uint(st[1][1]),
                                     __float_as_uint(st[2][1]), x));
+}
+
+template <int F, bool BLK>
+__global__ __launch_bounds__(kBlock) void stream_mix_kernel(MixParams p) {
+    stream_mix_body<F, BLK, false>(p);
+}
+
+// The replica of the step fed by interleaved contributions (blocked state).
+template <int F>
+__global__ __launch_bounds__(kBlock) void stream_mix_interleaved_kernel(MixParams p) {
+    stream_mix_body<F, true, true>(p);
 }
 
 // Blocked-state replica of any shape: wave w owns G consecutive groups and issues every load of
@@ -387,6 +413,35 @@ extern "C" int fsdpshard_stream_mix(const uint16_t* const* contribs, int32_t fan
 extern "C" int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in,
                                             float* state, uint16_t* out, int64_t n, void* stream) {
     return stream_mix_impl(contribs, fan_in, state, nullptr, nullptr, out, n, true, stream);
+}
+
+extern "C" int fsdpshard_stream_mix_interleaved(const uint16_t* grads, int32_t fan_in,
+                                                float* state, uint16_t* out, int64_t n,
+                                                void* stream) {
+    if (grads == nullptr || state == nullptr || out == nullptr || n < 0 || n % kVec != 0 ||
+        fan_in < 1)
+        return FSDPSHARD_ERR_INVALID_ARG;
+    if (fan_in > FSDPSHARD_MAX_FAN_IN) return FSDPSHARD_ERR_UNSUPPORTED;
+    if (!aligned16(grads) || !aligned16(state) || !aligned16(out)) return FSDPSHARD_ERR_ALIGNMENT;
+    if (n > INT64_MAX / 16) return FSDPSHARD_ERR_OVERFLOW;
+    const int64_t ge = interleaved_elems(fan_in, n);
+    if (ge < 0) return FSDPSHARD_ERR_OVERFLOW;
+    const int64_t sb = blocked_elems(n) * 4;
+    if (n > 0 && (overlaps(state, sb, out, n * 2) || overlaps(state, sb, grads, ge * 2) ||
+                  overlaps(out, n * 2, grads, ge * 2)))
+        return FSDPSHARD_ERR_INVALID_ARG;
+    if (n == 0) return FSDPSHARD_OK;
+    MixParams p;
+    const uint16_t* one[1] = {grads};
+    fill_mix(p, one, 1, state, nullptr, nullptr, out, n);
+    p.fan_in = fan_in;
+    unsigned blocks = 0;
+    const int rc = tile_grid(n, 1, &blocks);
+    if (rc != FSDPSHARD_OK) return rc;
+    const void* k = fan_in == 1   ? reinterpret_cast<const void*>(&stream_mix_interleaved_kernel<1>)
+                    : fan_in == 8 ? reinterpret_cast<const void*>(&stream_mix_interleaved_kernel<8>)
+                                  : reinterpret_cast<const void*>(&stream_mix_interleaved_kernel<0>);
+    return launch(k, blocks, &p, stream, step_groups_per_cu(fan_in, blocks));   // as the step
 }
 
 extern "C" int fsdpshard_stream_mix_shaped(const uint16_t* const* contribs, int32_t fan_in,

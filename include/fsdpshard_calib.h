@@ -89,6 +89,15 @@ int fsdpshard_stream_mix_blocked(const uint16_t* const* contribs, int32_t fan_in
                                  uint16_t* out, int64_t n, void* stream);
 
 /*
+ * fsdpshard_stream_mix_interleaved -- the same replay for adamw_shard_step_interleaved: the
+ * fan_in contributions are read from `grads`, grads_interleaved_elems(fan_in, n) bf16 elements
+ * in the interleaved layout (16-byte aligned); `state`, `out`, n as fsdpshard_stream_mix_blocked.
+ * Returns 0 or an fsdpshard_status (INVALID_ARG, ALIGNMENT, UNSUPPORTED, OVERFLOW, HIP).
+ */
+int fsdpshard_stream_mix_interleaved(const uint16_t* grads, int32_t fan_in, float* state,
+                                     uint16_t* out, int64_t n, void* stream);
+
+/*
  * fsdpshard_stream_mix_shaped -- the bytes of fsdpshard_stream_mix_blocked in another launch
  * shape: each wavefront owns `groups_per_wave` consecutive 512-element groups and issues every
  * load of them (state, then contributions) before any store.  With phased == 1 the work-group

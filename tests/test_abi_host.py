@@ -361,6 +361,16 @@ def test_calibration_call_validation():
     st, out = _Fake.at(20), _Fake.at(21)
     assert ph(8, out, 0) == OK
     assert ph(8, out, 0, phased=0) == OK
+    gi = _Fake.at(30)
+    mi = lambda g, fi, s_, o, n: lib.fsdpshard_stream_mix_interleaved(g, fi, s_, o, n, None)
+    assert mi(gi, 8, st, out, 0) == OK
+    assert mi(None, 8, st, out, 0) == INVALID
+    assert mi(gi, 0, st, out, 0) == INVALID
+    assert mi(gi, 65, st, out, 0) == UNSUP
+    assert mi(gi, 8, st, out, 12) == INVALID                        # whole vectors only
+    assert mi(gi + 8, 8, st, out, 0) == ALIGN
+    assert mi(gi, 8, st, gi + 64, 1024) == INVALID                  # out inside the grads
+    assert mi(gi, 8, gi + 1024, out, 1024) == INVALID               # state over the grads
     assert ph(2, out, 0) == UNSUP                                   # fan-in 1, 4, 8 only
     assert ph(8, out, 0, g=3) == UNSUP                              # 1, 2 or 4 groups per wave
     assert ph(8, out, 12) == INVALID                                # whole vectors only

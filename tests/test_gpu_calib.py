@@ -106,8 +106,10 @@ def _mix_expected(contribs, state, n, shaped):
 
 @pytest.mark.parametrize("fan_in", [1, 8])
 @pytest.mark.parametrize("groups,per_cu,run,phased", [(0, 0, 0, 0), (1, 2, 32, 1), (2, 1, 2, 1),
-                                                      (4, 1, 1, 1), (1, 1, 16, 0), (2, 2, 4, 0)])
+                                                      (4, 1, 1, 1), (1, 1, 16, 0), (2, 2, 4, 0),
+                                                      (-1, 0, 0, 0)])
 def test_mix_replicas_move_the_steps_bytes(fan_in, groups, per_cu, run, phased):
+    # groups -1: the replica of the step fed by interleaved contributions.
     n = 8 * (64 * 4 * 4 * 21 + 97)               # 21 whole tiles of 16 groups plus a ragged tail
     rng = np.random.default_rng(fan_in + groups)
     contribs = [rng.integers(0, 2 ** 16, n, dtype=np.uint16) for _ in range(fan_in)]
@@ -121,6 +123,9 @@ def test_mix_replicas_move_the_steps_bytes(fan_in, groups, per_cu, run, phased):
         f"n={n}")
     if groups == 0:
         F.stream_mix_blocked(cd, st, out, n)
+    elif groups == -1:
+        gi = torch.from_numpy(BL.to_interleaved(contribs).view(np.int16)).cuda()
+        F.stream_mix_interleaved(gi, fan_in, st, out, n)
     else:
         F.stream_mix_shaped(cd, st, out, n, groups, per_cu, run, phased)
     torch.cuda.synchronize()
