@@ -2,8 +2,9 @@
 
     python tests/c_abi/build.py
 
-host_check needs only the C library; gpu_step also links the HIP runtime.  Binaries go to
-tests/c_abi/bin/ and find libfsdpshard.so through an rpath relative to their own location.
+host_check and host_edges need only the C library; gpu_step also links the HIP runtime.
+Binaries go to tests/c_abi/bin/ and find libfsdpshard.so through an rpath relative to their own
+location.
 """
 
 import os
@@ -27,6 +28,7 @@ HIP_LINK = [f"-L{os.path.join(ROCM, 'lib')}", "-lamdhip64", f"-Wl,-rpath,{os.pat
 def commands():
     return [
         COMMON + [os.path.join(HERE, "host_check.c"), "-o", os.path.join(BIN, "host_check")] + LINK,
+        COMMON + [os.path.join(HERE, "host_edges.c"), "-o", os.path.join(BIN, "host_edges")] + LINK,
         COMMON + HIP + [os.path.join(HERE, "gpu_step.c"), "-o", os.path.join(BIN, "gpu_step")]
         + LINK + HIP_LINK,
     ]

@@ -1,92 +1,50 @@
-"""The host entry points called from plain C (tests/c_abi/host_check.c, built with gcc against
-include/fsdpshard.h and libfsdpshard.so), checked against the oracle.
+"""The host entry points called from plain C (tests/c_abi/host_check.c and host_edges.c, built
+with gcc against include/fsdpshard.h and libfsdpshard.so).
 
-The layout and segment table must equal the oracle's; the reshard plan is applied to the oracle's
-source shards with NumPy and must rebuild the oracle's destination shard.  This shows that the
-header is valid C and that the C ABI works without Python in the call path.
+host_check's layout, segment table and reshard plan are checked against the oracle on random
+cases; host_edges runs the edge cases (short caller arrays, int64 extremes, empty inputs, argument
+errors) and checks them itself.  This shows that the header is valid C and that the C ABI works
+without Python in the call path.
 """
 
 import os
-import random
 import subprocess
 
-import numpy as np
 import pytest
 
-from oracle import layout as OL
-from oracle import reshard as OR
+import host_check_cases
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-BIN = os.path.join(HERE, "c_abi", "bin", "host_check")
+BIN = os.path.join(HERE, "c_abi", "bin")
 LIB = os.path.join(os.path.dirname(HERE), "fsdp_sharded_optimizer_layout_amd", "libfsdpshard.so")
+PROGRAMS = ("host_check", "host_edges")
 
 
 @pytest.fixture(scope="module")
-def host_check():
+def bin_dir():
     if not os.path.exists(LIB):
         pytest.fail("libfsdpshard.so is not built")
     import importlib.util
     spec = importlib.util.spec_from_file_location("c_abi_build", os.path.join(HERE, "c_abi", "build.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    if not os.path.exists(BIN) or os.path.getmtime(BIN) < os.path.getmtime(LIB):
+    stale = [p for p in PROGRAMS if not os.path.exists(os.path.join(BIN, p))
+             or os.path.getmtime(os.path.join(BIN, p)) < os.path.getmtime(LIB)
+             or os.path.getmtime(os.path.join(BIN, p)) < os.path.getmtime(
+                 os.path.join(HERE, "c_abi", p + ".c"))]
+    if stale:
         mod.build()
     return BIN
 
 
-def _run(binary, sizes, wd, pad, N, k, pad2, N2, k2):
-    text = f"{len(sizes)} {pad} {N} {k} {pad2} {N2} {k2}\n"
-    text += " ".join(map(str, sizes)) + "\n" + " ".join(str(int(x)) for x in wd) + "\n"
-    out = subprocess.run([binary], input=text, capture_output=True, text=True, timeout=60)
+def test_c_program_matches_oracle(bin_dir):
+    host_check_cases.check_random_cases(os.path.join(bin_dir, "host_check"))
+
+
+def test_c_edge_cases(bin_dir):
+    out = subprocess.run([os.path.join(bin_dir, "host_edges")], capture_output=True, text=True,
+                         timeout=120)
     assert out.returncode == 0, out.stderr
-    lines = [ln.split() for ln in out.stdout.splitlines()]
-    rec = {"segs": [], "pieces": []}
-    for ln in lines:
-        if ln[0] == "abi":
-            rec["abi"] = int(ln[1])
-        elif ln[0] == "layout":
-            rec["layout"] = list(map(int, ln[1:]))
-        elif ln[0] == "seg":
-            rec["segs"].append(tuple(map(int, ln[1:])))
-        elif ln[0] == "plan":
-            rec["count"] = int(ln[1])
-        elif ln[0] == "piece":
-            rec["pieces"].append(tuple(map(int, ln[1:])))
-        elif ln[0] == "badrank":
-            rec["badrank"] = (int(ln[1]), " ".join(ln[2:]))
-    return rec
-
-
-def test_c_program_matches_oracle(host_check):
-    rng = random.Random(5)
-    for trial in range(60):
-        T = rng.randint(1, 12)
-        sizes = [rng.choice([0, 1, 3, 8, 17, 100, 1001, 4096]) for _ in range(T)]
-        wd = [rng.random() < 0.5 for _ in range(T)]
-        pad, pad2 = rng.choice([1, 2, 8, 16]), rng.choice([1, 4, 16])
-        N, N2 = rng.randint(1, 9), rng.randint(1, 9)
-        k, k2 = rng.randrange(N), rng.randrange(N2)
-        rec = _run(host_check, sizes, wd, pad, N, k, pad2, N2, k2)
-        assert rec["abi"] == 1
-
-        lo, hi, segs = OL.segments(sizes, pad, [int(x) for x in wd], N, k)
-        offs, P = OL.flatten_offsets(sizes, pad)
-        real = sum(s["length"] for s in segs if not s["flags"] & OL.PADDING)
-        tensors = len({s["tensor_id"] for s in segs})
-        assert rec["layout"] == [P, lo, hi, hi - lo, real, len(segs), tensors], (trial, sizes)
-        assert rec["segs"] == [(s["shard_begin"], s["length"], s["tensor_offset"], s["tensor_id"],
-                                s["flags"]) for s in segs]
-
-        # Apply the plan to the oracle's shards: it must rebuild the oracle's destination shard.
-        flat = np.zeros(P, dtype=np.int64)
-        for i, (o, s) in enumerate(zip(offs, sizes)):
-            flat[o:o + s] = 1 + 1000 * i + np.arange(s)
-        src = OR.shard(flat, sizes, pad, N)
-        want = OR.reshard(src, sizes, pad, pad2, N2)[k2]
-        got = np.full(want.size, -1, dtype=np.int64)
-        assert rec["count"] == len(rec["pieces"])
-        for r, so, do, ln in rec["pieces"]:
-            assert (got[do:do + ln] == -1).all()                        # pieces are disjoint
-            got[do:do + ln] = 0 if r < 0 else src[r][so:so + ln]
-        assert np.array_equal(got, want), (trial, sizes, pad, N, pad2, N2, k2)
-        assert rec["badrank"] == (1, "invalid argument")
+    assert out.stdout.split("\n")[:-1] == [
+        "ok layout_capacity", "ok plan_capacity", "ok int64_extremes", "ok empty",
+        "ok many_tensors", "ok invalid", "ok status_strings"]
