@@ -547,6 +547,28 @@ def mix_references(F, torch, S, stream, evict, shapes=False):
     return ref
 
 
+def f32_step_reference(F, torch, S, stream, evict):
+    """The fp32-gradient step's bytes with trivial arithmetic (blocked state): the interleaved
+    replica at fan-in 2 reads 4 bytes of gradient per element, 2 KiB contiguous per 512-element
+    block, as the step reads its fp32 shard; with 24 bytes of state and the 2-byte bf16 copy it
+    moves the step's 30 bytes per element, in the step's grid, tile map and work-groups per CU."""
+    n8 = S.L.n - S.L.n % 8
+    if n8 == 0 or not S.blocked:
+        return None
+    g2 = torch.zeros(F.grads_interleaved_elems(2, n8), dtype=torch.int16, device=S.dev)
+    out16 = (S.flat[S.phase:S.phase + n8] if S.phase == 0
+             else torch.empty(n8, dtype=torch.int16, device=S.dev))
+    ms = time_launches(torch, lambda: F.stream_mix_interleaved(g2, 2, S.state, out16, n8,
+                                                               stream=stream),
+                       stream, evict=evict)
+    bpe = algorithmic_bytes_per_param_f32grad()
+    del g2, out16
+    return {"f32grad_step_bytes": {"GBps": round(n8 * bpe / (ms / 1e3) / 1e9, 1),
+                                   "ms": round(ms, 4),
+                                   "kernel": "fsdpshard_stream_mix_interleaved (fan-in 2)"},
+            "flushed": evict is not None}
+
+
 def measure_workload(F, W, torch, name, layout, args, dev, stream, mix=True):
     """The fused step of one workload: its stage timing, roofline figures and (like for like,
     flushed when the step is) the traffic replica."""
@@ -793,6 +815,11 @@ def main():
         for k, x in (mix_ref or {}).items():
             if isinstance(x, dict):
                 log(f"  traffic replica {k}: {x['GBps']} GB/s")
+    elif not args.no_copy_reference and args.path in ("clipped32", "accumulate"):
+        # These paths end with the fp32-gradient step: replay its bytes on the same buffers.
+        mix_ref = f32_step_reference(F, torch, S, stream, evict)
+        if mix_ref:
+            log(f"  fp32-gradient step replica: {mix_ref['f32grad_step_bytes']['GBps']} GB/s")
     del S, stages, evict
     torch.cuda.empty_cache()
 

@@ -32,3 +32,17 @@ def test_bench_prints_the_contract_line():
     for k in ("read", "write", "copy", "read2_write1"):
         assert rec["ceiling"][k]["GBps"] > 0
     assert rec["mix_reference"]["flushed"] is True        # a small slice runs with the flush
+
+
+def test_fp32_gradient_paths_carry_their_replica():
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "llama_layer_n8_rank0",
+           "--path", "accumulate", "--steps", "2", "--warmup", "1", "--no-cpu-baseline",
+           "--no-ceiling"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-3000:]
+    rec = json.loads(r.stdout.strip().splitlines()[-1])
+    calls = [st["call"] for st in rec["config"]["stages"]]
+    assert calls[-1].startswith("adamw_shard_step_f32grad_blocked")
+    ref = rec["mix_reference"]
+    assert ref["flushed"] == ("flush" in rec["config"]["timing"])   # flushed as the stages are
+    assert ref["f32grad_step_bytes"]["GBps"] > 0 and ref["f32grad_step_bytes"]["ms"] > 0
