@@ -292,6 +292,186 @@ static void case_status_strings(void) {
     printf("ok status_strings\n");
 }
 
+
+/* ---- randomized cases: exact bounds and invariants checked with 128-bit arithmetic ---- */
+
+static uint64_t rng_s = 0x9E3779B97F4A7C15ull;
+static uint64_t rnd(void) {  /* xorshift64* */
+    rng_s ^= rng_s >> 12;
+    rng_s ^= rng_s << 25;
+    rng_s ^= rng_s >> 27;
+    return rng_s * 0x2545F4914F6CDD1Dull;
+}
+
+static int64_t pick_size(void) {
+    switch (rnd() % 8) {
+        case 0: return 0;
+        case 1: case 2: case 3: return (int64_t)(rnd() % 100);
+        case 4: return (int64_t)(rnd() % 100000);
+        case 5: return (int64_t)(rnd() % (1ull << 40));
+        case 6: return I64MAX - (int64_t)(rnd() % 1000);
+        default: return I64MAX / (int64_t)(2 + rnd() % 20);
+    }
+}
+
+static int64_t pick_pad(void) {
+    static const int64_t small[6] = {1, 2, 8, 16, 512, 1 << 20};
+    if (rnd() % 8 == 0) return I64MAX / (int64_t)(1 + rnd() % 4);
+    return small[rnd() % 6];
+}
+
+static int32_t pick_world(int big) {
+    switch (rnd() % (big ? 4 : 2)) {
+        case 0: return (int32_t)(1 + rnd() % 9);
+        case 1: return (int32_t)(1 + rnd() % 64);
+        case 2: return I32MAX - (int32_t)(rnd() % 10);
+        default: return (int32_t)(1 + rnd() % (uint64_t)I32MAX);
+    }
+}
+
+/* Flat offsets under one padding multiple in 128 bits; returns 0 when P exceeds INT64_MAX. */
+static int offsets128(const int64_t* sizes, int T, int64_t pad, __int128* off) {
+    __int128 pos = 0;
+    for (int i = 0; i < T; ++i) {
+        off[i] = pos;
+        pos += ((__int128)sizes[i] + pad - 1) / pad * pad;
+    }
+    off[T] = pos;
+    return pos <= (__int128)I64MAX;
+}
+
+/* The tensor whose padded extent holds flat position u (empty extents hold nothing). */
+static int tensor_at(const __int128* off, int T, __int128 u) {
+    for (int i = 0; i < T; ++i)
+        if (off[i] <= u && u < off[i + 1]) return i;
+    return -1;
+}
+
+static void case_fuzz_layout(void) {
+    enum { MAXT = 20 };
+    int64_t sizes[MAXT];
+    uint8_t wd[MAXT];
+    __int128 off[MAXT + 1];
+    fsdpshard_segment segs[2 * MAXT + 2];
+    for (int trial = 0; trial < 40000; ++trial) {
+        const int T = (int)(rnd() % (MAXT + 1));
+        for (int i = 0; i < T; ++i) {
+            sizes[i] = pick_size();
+            wd[i] = (uint8_t)(rnd() & 1);
+        }
+        const int64_t pad = pick_pad();
+        const int32_t N = pick_world(1);
+        const int32_t k = (int32_t)(rnd() % (uint64_t)N);
+        const int fits = offsets128(sizes, T, pad, off);
+        fsdpshard_layout L;
+        int rc = shard_layout(sizes, T, pad, wd, N, k, &L, segs, 2 * MAXT + 2);
+        if (!fits) {
+            CHECK(rc == FSDPSHARD_ERR_OVERFLOW, "trial %d: rc %d, expected overflow", trial, rc);
+            continue;
+        }
+        CHECK(rc == FSDPSHARD_OK, "trial %d: rc %d", trial, rc);
+        const int64_t P = (int64_t)off[T];
+        CHECK(L.P == P && L.lo == floor_kp(k, P, N) && L.hi == floor_kp((int64_t)k + 1, P, N) &&
+                  L.n == L.hi - L.lo,
+              "trial %d: bounds", trial);
+        CHECK(L.n_segments <= 2 * T, "trial %d: %d segments for %d tensors", trial,
+              L.n_segments, T);
+        CHECK(segs_tile(segs, L.n_segments, L.n), "trial %d: segments do not tile", trial);
+        int64_t real = 0;
+        int32_t tensors = 0, last = -1;
+        for (int32_t j = 0; j < L.n_segments; ++j) {
+            const fsdpshard_segment* g = &segs[j];
+            const int id = g->tensor_id;
+            CHECK(id >= 0 && id < T && id >= last, "trial %d: tensor id %d", trial, id);
+            if (id != last) ++tensors;
+            last = id;
+            CHECK((__int128)L.lo + g->shard_begin == off[id] + g->tensor_offset,
+                  "trial %d: segment %d position", trial, j);
+            CHECK(off[id] + g->tensor_offset + g->length <= off[id + 1],
+                  "trial %d: segment %d leaves its tensor", trial, j);
+            const int pad_run = (g->flags & FSDPSHARD_SEG_PADDING) != 0;
+            if (pad_run) {
+                CHECK(g->tensor_offset >= sizes[id], "trial %d: padding over real data", trial);
+            } else {
+                CHECK(g->tensor_offset + g->length <= sizes[id], "trial %d: real run past the end",
+                      trial);
+                real += g->length;
+            }
+            CHECK(((g->flags & FSDPSHARD_SEG_WEIGHT_DECAY) != 0) == (wd[id] != 0),
+                  "trial %d: weight-decay flag", trial);
+        }
+        CHECK(real == L.n_real && tensors == L.n_tensors, "trial %d: counts", trial);
+    }
+    printf("ok fuzz_layout\n");
+}
+
+static void case_fuzz_plan(void) {
+    enum { MAXT = 12, CAP = 4096 };
+    int64_t sizes[MAXT];
+    __int128 oa[MAXT + 1], ob[MAXT + 1];
+    static fsdpshard_piece pieces[CAP];
+    for (int trial = 0; trial < 10000; ++trial) {
+        const int T = (int)(rnd() % (MAXT + 1));
+        for (int i = 0; i < T; ++i) sizes[i] = pick_size();
+        const int64_t pa = pick_pad(), pb = pick_pad();
+        const int32_t N = pick_world(0), N2 = pick_world(0);
+        const int32_t k2 = (int32_t)(rnd() % (uint64_t)N2);
+        const int fits = offsets128(sizes, T, pa, oa) & offsets128(sizes, T, pb, ob);
+        int32_t count = -1;
+        int rc = reshard_plan(sizes, T, pa, N, pb, N2, k2, pieces, CAP, &count);
+        if (!fits) {
+            CHECK(rc == FSDPSHARD_ERR_OVERFLOW, "trial %d: rc %d, expected overflow", trial, rc);
+            continue;
+        }
+        CHECK(rc == FSDPSHARD_OK && count >= 0 && count <= CAP, "trial %d: rc %d count %d",
+              trial, rc, count);
+        const int64_t Pa = (int64_t)oa[T], Pb = (int64_t)ob[T];
+        const int64_t lo2 = floor_kp(k2, Pb, N2), hi2 = floor_kp((int64_t)k2 + 1, Pb, N2);
+        int64_t pos = 0;
+        for (int32_t j = 0; j < count; ++j) {
+            const fsdpshard_piece* q = &pieces[j];
+            CHECK(q->dst_offset == pos && q->length > 0 && q->reserved == 0,
+                  "trial %d: piece %d placement", trial, j);
+            pos += q->length;
+            /* Walk the piece tensor by tensor (merged neighbours may span several). */
+            __int128 d = (__int128)lo2 + q->dst_offset;
+            __int128 left = q->length;
+            if (q->src_rank < 0) {
+                CHECK(q->src_offset == 0, "trial %d: zero piece %d source offset", trial, j);
+                while (left > 0) {      /* every element is destination padding */
+                    const int i = tensor_at(ob, T, d);
+                    CHECK(i >= 0 && d >= ob[i] + sizes[i], "trial %d: zero piece %d over data",
+                          trial, j);
+                    const __int128 c = left < ob[i + 1] - d ? left : ob[i + 1] - d;
+                    d += c;
+                    left -= c;
+                }
+                continue;
+            }
+            const int32_t r = q->src_rank;
+            CHECK(r < N, "trial %d: source rank %d of %d", trial, r, N);
+            const int64_t rlo = floor_kp(r, Pa, N), rhi = floor_kp((int64_t)r + 1, Pa, N);
+            CHECK(q->src_offset >= 0 && q->src_offset + q->length <= rhi - rlo,
+                  "trial %d: piece %d outside source shard", trial, j);
+            __int128 u = (__int128)rlo + q->src_offset;
+            while (left > 0) {          /* same tensor, same offset, real data on both sides */
+                const int i = tensor_at(oa, T, u);
+                CHECK(i >= 0 && tensor_at(ob, T, d) == i && u - oa[i] == d - ob[i] &&
+                          u - oa[i] < sizes[i],
+                      "trial %d: piece %d maps an element wrongly", trial, j);
+                const __int128 avail = oa[i] + sizes[i] - u;
+                const __int128 c = left < avail ? left : avail;
+                u += c;
+                d += c;
+                left -= c;
+            }
+        }
+        CHECK(pos == hi2 - lo2, "trial %d: pieces cover %lld of %lld", trial, (long long)pos,
+              (long long)(hi2 - lo2));
+    }
+    printf("ok fuzz_plan\n");
+}
+
 int main(void) {
     case_layout_capacity();
     case_plan_capacity();
@@ -300,6 +480,8 @@ int main(void) {
     case_many_tensors();
     case_invalid();
     case_status_strings();
+    case_fuzz_layout();
+    case_fuzz_plan();
     if (failures) {
         fprintf(stderr, "%d case(s) failed\n", failures);
         return 1;

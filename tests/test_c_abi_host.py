@@ -47,4 +47,4 @@ def test_c_edge_cases(bin_dir):
     assert out.returncode == 0, out.stderr
     assert out.stdout.split("\n")[:-1] == [
         "ok layout_capacity", "ok plan_capacity", "ok int64_extremes", "ok empty",
-        "ok many_tensors", "ok invalid", "ok status_strings"]
+        "ok many_tensors", "ok invalid", "ok status_strings", "ok fuzz_layout", "ok fuzz_plan"]

@@ -55,4 +55,4 @@ def test_sanitized_edge_cases(sanitized):
     assert r.stderr == "", r.stderr
     assert r.stdout.split("\n")[:-1] == [
         "ok layout_capacity", "ok plan_capacity", "ok int64_extremes", "ok empty",
-        "ok many_tensors", "ok invalid", "ok status_strings"]
+        "ok many_tensors", "ok invalid", "ok status_strings", "ok fuzz_layout", "ok fuzz_plan"]
