@@ -161,8 +161,8 @@ struct SegCursor {
     // in range), then narrows [a, b) to one eighth; the first segment begins at 0 <= pos.  The
     // probes are wave-uniform scalar loads, so the levels overlap the group's data loads.  Against
     // a binary search (one dependent probe per level) the step on a 237-segment slice ran
-    // 1.0-1.5 % faster (measured on MI355X, two boxes, 8 alternating rounds, cache flushed), and
-    // the 7B- and 70B-shaped slices were unchanged.
+    // 1.0-1.5 % faster (measured on MI355X, three boxes, 8 alternating rounds, cache flushed),
+    // and the 7B- and 70B-shaped slices were unchanged.
     __device__ void init(const fsdpshard_segment* s, int32_t ns, int64_t pos) {
         segs = s;
         n_segs = ns;
@@ -174,16 +174,21 @@ struct SegCursor {
         }
         int32_t a = 0, b = ns;
         while (b - a > 1) {
-            const int32_t step = (b - a + 7) >> 3;
+            const int32_t step = (b - a - 1) / 8 + 1;             // ceil((b - a) / 8), no overflow
+            int32_t probe[7];
             int64_t begin[7];
 #pragma unroll
-            for (int j = 0; j < 7; ++j) begin[j] = segs[min(a + (j + 1) * step, b - 1)].shard_begin;
+            for (int j = 0; j < 7; ++j) {
+                const int64_t m = static_cast<int64_t>(a) + static_cast<int64_t>(j + 1) * step;
+                probe[j] = static_cast<int32_t>(m < b - 1 ? m : b - 1);
+                begin[j] = segs[probe[j]].shard_begin;
+            }
             __builtin_amdgcn_sched_barrier(0);   // all seven loads before the first compare
             int32_t na = a;
 #pragma unroll
             for (int j = 0; j < 7; ++j)
-                if (begin[j] <= pos) na = max(na, min(a + (j + 1) * step, b - 1));
-            b = min(na + step, b);
+                if (begin[j] <= pos) na = max(na, probe[j]);
+            b = step < b - na ? na + step : b;
             a = na;
         }
         load(a);
